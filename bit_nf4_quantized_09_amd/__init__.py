@@ -1,0 +1,282 @@
+"""QLoRA NF4 linear layer for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libqlora_nf4.so`` (declared in
+``include/qlora_nf4.h``).  This module only marshals arguments: it checks
+dtypes and shapes, allocates outputs and workspaces with torch, and passes raw
+device pointers plus the current HIP stream.  Every step of the computation
+runs in the library's HIP kernels; there is no CPU or PyTorch fallback, and a
+missing library raises ``NF4Error``.
+
+Names follow the stubs on the zerotofrontier.app PEFT page ("NF4, derived from
+normal quantiles": nf4_quantize / nf4_dequantize; "Double quantization":
+double_quantize / double_dequantize) and the layer formula of "Putting it
+together" (prism.theerrors.in QLoRA explainer).
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "NF4Error", "NF4Weight", "lib_path", "load_library", "nf4_quantize", "nf4_double_quantize",
+    "nf4_double_dequantize", "nf4_dequantize", "quantize_weight", "qlora_linear_fwd",
+    "qlora_linear_bwd", "nf4_storage_bytes", "nf4_codebook", "nf4_workspace_bytes",
+    "NF4_OP_DOUBLE_QUANTIZE", "NF4_OP_LINEAR_FWD", "NF4_OP_LINEAR_BWD",
+]
+
+NF4_OK, NF4_ERR_ARG, NF4_ERR_UNSUPPORTED, NF4_ERR_WORKSPACE, NF4_ERR_HIP = range(5)
+NF4_F32, NF4_BF16 = 0, 1
+NF4_OP_DOUBLE_QUANTIZE, NF4_OP_LINEAR_FWD, NF4_OP_LINEAR_BWD = 1, 2, 3
+_STATUS = {1: "NF4_ERR_ARG", 2: "NF4_ERR_UNSUPPORTED", 3: "NF4_ERR_WORKSPACE", 4: "NF4_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "_lib", "libqlora_nf4.so")
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, status), message))
+        self.status = status
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("q", ctypes.c_void_p), ("c2", ctypes.c_void_p),
+                ("mean", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+def load_library():
+    """Load libqlora_nf4.so (raises NF4Error if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise NF4Error(NF4_ERR_HIP, "HIP library not built (%s); run __graft_entry__.build()" % path)
+    L = ctypes.CDLL(path)
+    L.nf4_quantize.restype = ctypes.c_int
+    L.nf4_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i32, _vp, _vp, _vp]
+    L.nf4_double_quantize.restype = ctypes.c_int
+    L.nf4_double_quantize.argtypes = [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.nf4_double_dequantize.restype = ctypes.c_int
+    L.nf4_double_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i32, _vp, _vp]
+    L.nf4_dequantize.restype = ctypes.c_int
+    L.nf4_dequantize.argtypes = [ctypes.POINTER(_Weight), _vp, ctypes.c_int, _vp]
+    L.qlora_linear_fwd.restype = ctypes.c_int
+    L.qlora_linear_fwd.argtypes = [ctypes.POINTER(_Weight), _vp, _i64, _vp, _vp, _i32, ctypes.c_float,
+                                   _vp, _vp, _vp, _sz, _vp]
+    L.qlora_linear_bwd.restype = ctypes.c_int
+    L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_Weight), _vp, _vp, _i64, _vp, _vp, _i32,
+                                   ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.nf4_workspace_bytes.restype = _sz
+    L.nf4_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64, _i32]
+    L.nf4_storage_bytes.restype = None
+    L.nf4_storage_bytes.argtypes = [_i64, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                    ctypes.POINTER(_sz)]
+    L.nf4_codebook.restype = None
+    L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.nf4_last_error.restype = ctypes.c_char_p
+    L.nf4_last_error.argtypes = []
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != NF4_OK:
+        raise NF4Error(status, load_library().nf4_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off: off + nbytes]
+
+
+@dataclass
+class NF4Weight:
+    """A frozen weight as double-quantized NF4: codes, q, c2, mean on the GPU."""
+    codes: torch.Tensor   # uint8 [ceil(n/2)]
+    q: torch.Tensor       # uint8 [ceil(n/64)]
+    c2: torch.Tensor      # float32 [ceil(n1/256)]
+    mean: torch.Tensor    # float32 [1]
+    shape: Tuple[int, int]
+
+    def descriptor(self) -> _Weight:
+        rows, cols = self.shape
+        return _Weight(self.codes.data_ptr(), self.q.data_ptr(), self.c2.data_ptr(),
+                       self.mean.data_ptr(), rows, cols)
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.codes, self.q, self.c2, self.mean))
+
+
+def nf4_codebook():
+    """The 16 NF4 levels (host copy)."""
+    out = (ctypes.c_float * 16)()
+    load_library().nf4_codebook(out)
+    return list(out)
+
+
+def nf4_storage_bytes(n: int, blocksize: int = 64, blocksize2: int = 256):
+    """(codes, q, c2) bytes of a double-quantized NF4 tensor of n values."""
+    a, b, c = _sz(), _sz(), _sz()
+    load_library().nf4_storage_bytes(n, blocksize, blocksize2, ctypes.byref(a), ctypes.byref(b),
+                                     ctypes.byref(c))
+    return a.value, b.value, c.value
+
+
+def nf4_workspace_bytes(op: int, M: int, N: int, K: int, r: int) -> int:
+    return int(load_library().nf4_workspace_bytes(op, M, N, K, r))
+
+
+def nf4_quantize(w: torch.Tensor, blocksize: int = 64):
+    """Blockwise-absmax NF4 codes of a fp32/bf16 tensor: (codes uint8, absmax fp32)."""
+    L = load_library()
+    _dev(w, "w")
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be float32 or bfloat16")
+    n = w.numel()
+    codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty((n + 63) // 64, dtype=torch.float32, device=w.device)
+    _check(L.nf4_quantize(_ptr(w), NF4_BF16 if w.dtype == torch.bfloat16 else NF4_F32, n, blocksize,
+                          _ptr(codes), _ptr(absmax), _stream(w.device)))
+    return codes, absmax
+
+
+def nf4_double_quantize(absmax: torch.Tensor, blocksize2: int = 256):
+    """Double quantization of the first-level constants: (q uint8, c2 fp32, mean fp32[1])."""
+    L = load_library()
+    _dev(absmax, "absmax", torch.float32)
+    n1 = absmax.numel()
+    q = torch.empty(n1, dtype=torch.uint8, device=absmax.device)
+    c2 = torch.empty((n1 + 255) // 256, dtype=torch.float32, device=absmax.device)
+    mean = torch.empty(1, dtype=torch.float32, device=absmax.device)
+    wsb = L.nf4_workspace_bytes(NF4_OP_DOUBLE_QUANTIZE, 0, n1, 0, 0)
+    ws = _workspace(wsb, absmax.device)
+    _check(L.nf4_double_quantize(_ptr(absmax), n1, blocksize2, _ptr(q), _ptr(c2), _ptr(mean),
+                                 _ptr(ws), wsb, _stream(absmax.device)))
+    return q, c2, mean
+
+
+def nf4_double_dequantize(q: torch.Tensor, c2: torch.Tensor, mean: torch.Tensor,
+                          blocksize2: int = 256) -> torch.Tensor:
+    """c1' = fma(E4M3(q), fp32(c2/448), mean) per constant."""
+    L = load_library()
+    _dev(q, "q", torch.uint8)
+    _dev(c2, "c2", torch.float32)
+    _dev(mean, "mean", torch.float32)
+    out = torch.empty(q.numel(), dtype=torch.float32, device=q.device)
+    _check(L.nf4_double_dequantize(_ptr(q), _ptr(c2), _ptr(mean), q.numel(), blocksize2, _ptr(out),
+                                   _stream(q.device)))
+    return out
+
+
+def quantize_weight(w: torch.Tensor) -> NF4Weight:
+    """Quantize a 2-D (out x in) fp32/bf16 weight to the double-quantized NF4 tuple."""
+    if w.dim() != 2:
+        raise ValueError("weight must be 2-D (out x in)")
+    codes, absmax = nf4_quantize(w)
+    q, c2, mean = nf4_double_quantize(absmax)
+    return NF4Weight(codes, q, c2, mean, (int(w.shape[0]), int(w.shape[1])))
+
+
+def nf4_dequantize(W: NF4Weight, dtype=torch.float32) -> torch.Tensor:
+    """Dequantized weight (rows x cols) as float32 or bfloat16."""
+    L = load_library()
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dtype must be float32 or bfloat16")
+    out = torch.empty(W.shape, dtype=dtype, device=W.device)
+    d = W.descriptor()
+    _check(L.nf4_dequantize(ctypes.byref(d), _ptr(out), NF4_BF16 if dtype == torch.bfloat16 else NF4_F32,
+                            _stream(W.device)))
+    return out
+
+
+def qlora_linear_fwd(W: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, alpha: float,
+                     save_t: bool = True):
+    """Y = X dequant(W)^T + (alpha/r) (X A^T) B^T.  Returns (Y bf16 [M, N], T bf16 [M, r] or None)."""
+    L = load_library()
+    N, K = W.shape
+    _dev(X, "X", torch.bfloat16)
+    _dev(A, "A", torch.bfloat16)
+    _dev(B, "B", torch.bfloat16)
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [M, %d]" % K)
+    r = A.shape[0]
+    if tuple(A.shape) != (r, K) or tuple(B.shape) != (N, r):
+        raise ValueError("A must be [r, K] and B [N, r]")
+    M = X.shape[0]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    T = torch.empty((M, r), dtype=torch.bfloat16, device=X.device) if save_t else None
+    wsb = L.nf4_workspace_bytes(NF4_OP_LINEAR_FWD, M, N, K, r)
+    ws = _workspace(wsb, X.device)
+    d = W.descriptor()
+    _check(L.qlora_linear_fwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(Y),
+                              _ptr(T), _ptr(ws), wsb, _stream(X.device)))
+    return Y, T
+
+
+def qlora_linear_bwd(W: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
+                     B: torch.Tensor, alpha: float, T: Optional[torch.Tensor] = None,
+                     need_dx: bool = True):
+    """Backward of qlora_linear_fwd: (dX bf16 [M, K] or None, dA fp32 [r, K], dB fp32 [N, r])."""
+    L = load_library()
+    N, K = W.shape
+    _dev(X, "X", torch.bfloat16)
+    _dev(dY, "dY", torch.bfloat16)
+    _dev(A, "A", torch.bfloat16)
+    _dev(B, "B", torch.bfloat16)
+    M = X.shape[0]
+    r = A.shape[0]
+    if tuple(dY.shape) != (M, N) or tuple(X.shape) != (M, K):
+        raise ValueError("X must be [M, K] and dY [M, N]")
+    if tuple(A.shape) != (r, K) or tuple(B.shape) != (N, r):
+        raise ValueError("A must be [r, K] and B [N, r]")
+    if T is not None:
+        _dev(T, "T", torch.bfloat16)
+        if tuple(T.shape) != (M, r):
+            raise ValueError("T must be [M, r]")
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device) if need_dx else None
+    dA = torch.empty((r, K), dtype=torch.float32, device=X.device)
+    dB = torch.empty((N, r), dtype=torch.float32, device=X.device)
+    wsb = L.nf4_workspace_bytes(NF4_OP_LINEAR_BWD, M, N, K, r)
+    ws = _workspace(wsb, X.device)
+    d = W.descriptor()
+    _check(L.qlora_linear_bwd(ctypes.byref(d), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, float(alpha),
+                              _ptr(T), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(X.device)))
+    return dX, dA, dB

@@ -1,0 +1,296 @@
+// api.hip -- the extern "C" entry points declared in include/qlora_nf4.h.
+//
+// Host side only: argument validation (before any HIP call), the NF4 table,
+// workspace carving and kernel dispatch.  Every product step runs in the
+// gfx950 kernels of codec.hip, lora.hip and fused.hip.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/qlora_nf4.h"
+#include "launch.h"
+
+using nf4::Nf4Table;
+using nf4::WeightView;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nf4_status fail(nf4_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+nf4_status hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return NF4_OK;
+    return fail(NF4_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ---------------------------------------------------------------------------
+// NF4 levels ("NF4, derived from normal quantiles", zerotofrontier.app
+// "sft/peft"): probabilities from p_max = ((1-1/30)+(1-1/32))/2 down towards
+// 1/2, 8 evenly spaced quantiles on the positive side and 7 on the negative
+// side, an exact zero, normalised by the largest magnitude.  The inverse
+// normal CDF is solved by bisection on erfcl in long double.
+// ---------------------------------------------------------------------------
+long double norm_cdf(long double x) { return 0.5L * erfcl(-x / sqrtl(2.0L)); }
+
+long double norm_quantile(long double p) {
+    long double lo = -40.0L, hi = 40.0L;
+    for (int it = 0; it < 256; ++it) {
+        const long double mid = 0.5L * (lo + hi);
+        if (mid == lo || mid == hi) break;
+        if (norm_cdf(mid) < p) lo = mid;
+        else hi = mid;
+    }
+    return 0.5L * (lo + hi);
+}
+
+Nf4Table build_table() {
+    const long double pmax = ((1.0L - 1.0L / 30.0L) + (1.0L - 1.0L / 32.0L)) / 2.0L;
+    const long double top = norm_quantile(pmax);
+    long double v[16];
+    for (int i = 0; i < 7; ++i) v[i] = -norm_quantile(pmax - (long double)i * (pmax - 0.5L) / 7.0L);
+    v[7] = 0.0L;
+    for (int i = 0; i < 8; ++i) v[8 + i] = norm_quantile(pmax - (long double)(7 - i) * (pmax - 0.5L) / 8.0L);
+    Nf4Table t;
+    for (int i = 0; i < 16; ++i) t.lv[i] = (float)(v[i] / top);
+    t.lv[7] = 0.0f;
+    for (int j = 0; j < 15; ++j) {
+        // largest fp32 not above the (exact) midpoint: x > th[j] <=> x > midpoint
+        const double mid = ((double)t.lv[j] + (double)t.lv[j + 1]) / 2.0;
+        float th = (float)mid;
+        if ((double)th > mid) th = nextafterf(th, -INFINITY);
+        t.th[j] = th;
+    }
+    return t;
+}
+
+const Nf4Table& table() {
+    static Nf4Table t;
+    static std::once_flag once;
+    std::call_once(once, [] { t = build_table(); });
+    return t;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+nf4_status check_weight(const nf4_weight* W, WeightView& v, bool linear) {
+    if (!W) return fail(NF4_ERR_ARG, "weight descriptor is NULL");
+    if (W->rows < 0 || W->cols < 0) return fail(NF4_ERR_ARG, "negative weight shape");
+    const int64_t n = W->rows * W->cols;
+    if (n > 0 && (!W->codes || !W->q || !W->c2 || !W->mean))
+        return fail(NF4_ERR_ARG, "weight has a NULL codes/q/c2/mean pointer");
+    if (!W->mean) return fail(NF4_ERR_ARG, "weight mean pointer is NULL");
+    if (linear) {
+        if (W->cols % 64 != 0) return fail(NF4_ERR_UNSUPPORTED, "K (cols) must be a multiple of 64");
+        if (W->rows % 8 != 0) return fail(NF4_ERR_UNSUPPORTED, "N (rows) must be a multiple of 8");
+        if (W->rows == 0 || W->cols == 0) return fail(NF4_ERR_ARG, "empty weight");
+    }
+    if (!aligned(W->codes, 16)) return fail(NF4_ERR_ARG, "codes must be 16-byte aligned");
+    if (!aligned(W->c2, 4) || !aligned(W->mean, 4)) return fail(NF4_ERR_ARG, "misaligned c2/mean");
+    v.codes = W->codes;
+    v.q = W->q;
+    v.c2 = W->c2;
+    v.mean = W->mean;
+    v.rows = W->rows;
+    v.cols = W->cols;
+    return NF4_OK;
+}
+
+nf4_status check_lora(const void* A, const void* B, int32_t r, float alpha) {
+    if (r < 1 || r > 128) return fail(NF4_ERR_UNSUPPORTED, "rank r must be in [1, 128]");
+    if (r % 8 != 0) return fail(NF4_ERR_UNSUPPORTED, "rank r must be a multiple of 8");
+    if (!A || !B) return fail(NF4_ERR_ARG, "adapter A or B is NULL");
+    if (!aligned(A, 16) || !aligned(B, 16)) return fail(NF4_ERR_ARG, "A and B must be 16-byte aligned");
+    if (!isfinite(alpha)) return fail(NF4_ERR_ARG, "alpha must be finite");
+    return NF4_OK;
+}
+
+size_t rank_buffer_bytes(int64_t M, int32_t r) { return align256((size_t)M * (size_t)r * 2); }
+
+}  // namespace
+
+extern "C" {
+
+const char* nf4_last_error(void) { return g_last_error.c_str(); }
+
+void nf4_codebook(float out[16]) {
+    if (!out) return;
+    memcpy(out, table().lv, sizeof(float) * 16);
+}
+
+void nf4_storage_bytes(int64_t n, int32_t blocksize, int32_t blocksize2, size_t* codes_bytes,
+                       size_t* q_bytes, size_t* c2_bytes) {
+    if (n < 0 || blocksize <= 0 || blocksize2 <= 0) n = 0;
+    if (blocksize <= 0) blocksize = 64;
+    if (blocksize2 <= 0) blocksize2 = 256;
+    const int64_t n1 = (n + blocksize - 1) / blocksize;
+    const int64_t n2 = (n1 + blocksize2 - 1) / blocksize2;
+    if (codes_bytes) *codes_bytes = (size_t)((n + 1) / 2);
+    if (q_bytes) *q_bytes = (size_t)n1;
+    if (c2_bytes) *c2_bytes = (size_t)n2 * 4;
+}
+
+size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r) {
+    (void)K;
+    if (M < 0 || N < 0 || r < 0) return 0;
+    switch (op) {
+        case NF4_OP_DOUBLE_QUANTIZE: return nf4::double_quantize_ws_bytes(N);
+        case NF4_OP_LINEAR_FWD: return 2 * rank_buffer_bytes(M, r);
+        case NF4_OP_LINEAR_BWD: return 2 * rank_buffer_bytes(M, r);
+        default: return 0;
+    }
+}
+
+nf4_status nf4_quantize(const void* w, nf4_dtype dtype, int64_t n, int32_t blocksize, uint8_t* codes,
+                        float* absmax, void* stream) {
+    if (blocksize != 64) return fail(NF4_ERR_UNSUPPORTED, "blocksize must be 64");
+    if (dtype != NF4_F32 && dtype != NF4_BF16) return fail(NF4_ERR_ARG, "dtype must be NF4_F32 or NF4_BF16");
+    if (n < 0) return fail(NF4_ERR_ARG, "n must be >= 0");
+    if (n == 0) return NF4_OK;
+    if (!w || !codes || !absmax) return fail(NF4_ERR_ARG, "NULL w/codes/absmax");
+    if (!aligned(w, 16)) return fail(NF4_ERR_ARG, "w must be 16-byte aligned");
+    if (!aligned(codes, 4) || !aligned(absmax, 4)) return fail(NF4_ERR_ARG, "codes/absmax must be 4-byte aligned");
+    return hip_status(nf4::launch_quantize(w, dtype == NF4_BF16, n, codes, absmax, table(),
+                                           (hipStream_t)stream),
+                      "nf4_quantize");
+}
+
+nf4_status nf4_double_quantize(const float* absmax, int64_t n1, int32_t blocksize2, uint8_t* q,
+                               float* c2, float* mean, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (blocksize2 != 256) return fail(NF4_ERR_UNSUPPORTED, "blocksize2 must be 256");
+    if (n1 < 0) return fail(NF4_ERR_ARG, "n1 must be >= 0");
+    if (!mean) return fail(NF4_ERR_ARG, "mean is NULL");
+    if (n1 > 0 && (!absmax || !q || !c2)) return fail(NF4_ERR_ARG, "NULL absmax/q/c2");
+    if (!aligned(absmax, 16)) return fail(NF4_ERR_ARG, "absmax must be 16-byte aligned");
+    if (!aligned(q, 4) || !aligned(c2, 4) || !aligned(mean, 4)) return fail(NF4_ERR_ARG, "misaligned q/c2/mean");
+    const size_t need = nf4::double_quantize_ws_bytes(n1);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_DOUBLE_QUANTIZE)");
+    if (need > 0 && !aligned(workspace, 8)) return fail(NF4_ERR_ARG, "workspace must be 8-byte aligned");
+    return hip_status(nf4::launch_double_quantize(absmax, n1, q, c2, mean, (double*)workspace,
+                                                  (hipStream_t)stream),
+                      "nf4_double_quantize");
+}
+
+nf4_status nf4_double_dequantize(const uint8_t* q, const float* c2, const float* mean, int64_t n1,
+                                 int32_t blocksize2, float* c1_out, void* stream) {
+    if (blocksize2 != 256) return fail(NF4_ERR_UNSUPPORTED, "blocksize2 must be 256");
+    if (n1 < 0) return fail(NF4_ERR_ARG, "n1 must be >= 0");
+    if (n1 == 0) return NF4_OK;
+    if (!q || !c2 || !mean || !c1_out) return fail(NF4_ERR_ARG, "NULL q/c2/mean/c1_out");
+    if (!aligned(c2, 4) || !aligned(mean, 4) || !aligned(c1_out, 4)) return fail(NF4_ERR_ARG, "misaligned fp32 pointer");
+    return hip_status(nf4::launch_double_dequantize(q, c2, mean, n1, c1_out, (hipStream_t)stream),
+                      "nf4_double_dequantize");
+}
+
+nf4_status nf4_dequantize(const nf4_weight* W, void* out, nf4_dtype out_dtype, void* stream) {
+    WeightView v;
+    nf4_status st = check_weight(W, v, false);
+    if (st != NF4_OK) return st;
+    if (out_dtype != NF4_F32 && out_dtype != NF4_BF16) return fail(NF4_ERR_ARG, "out_dtype must be NF4_F32 or NF4_BF16");
+    if (v.rows * v.cols == 0) return NF4_OK;
+    if (!out) return fail(NF4_ERR_ARG, "out is NULL");
+    if (!aligned(out, 16)) return fail(NF4_ERR_ARG, "out must be 16-byte aligned");
+    return hip_status(nf4::launch_dequantize(v, out, out_dtype == NF4_BF16, table(), (hipStream_t)stream),
+                      "nf4_dequantize");
+}
+
+nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const void* A,
+                            const void* B, int32_t r, float alpha, void* Y, void* T_out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    WeightView v;
+    nf4_status st = check_weight(W, v, true);
+    if (st != NF4_OK) return st;
+    st = check_lora(A, B, r, alpha);
+    if (st != NF4_OK) return st;
+    if (M < 0) return fail(NF4_ERR_ARG, "M must be >= 0");
+    if (M == 0) return NF4_OK;
+    if (!X || !Y) return fail(NF4_ERR_ARG, "X or Y is NULL");
+    if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(T_out, 16))
+        return fail(NF4_ERR_ARG, "X, Y and T_out must be 16-byte aligned");
+    // workspace: [s*T bf16 M x r][T bf16 M x r when T_out is NULL]
+    const size_t rb = rank_buffer_bytes(M, r);
+    const size_t need = T_out ? rb : 2 * rb;
+    if (!workspace || workspace_bytes < need)
+        return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LINEAR_FWD)");
+    if (!aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
+    uint16_t* Ts = (uint16_t*)workspace;
+    uint16_t* Tb = T_out ? (uint16_t*)T_out : (uint16_t*)((char*)workspace + rb);
+    const float s = alpha / (float)r;
+    hipStream_t hs = (hipStream_t)stream;
+    const uint16_t* x = (const uint16_t*)X;
+    hipError_t e;
+    if (M <= 16) {
+        e = nf4::launch_lora_t_small(x, (const uint16_t*)A, M, v.cols, r, Tb, Ts, s, hs);
+        if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
+        e = nf4::launch_fused_gemv(v, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, table(), hs);
+        return hip_status(e, "qlora_linear_fwd (gemv)");
+    }
+    e = nf4::launch_lora_gemm(x, false, (const uint16_t*)A, false, M, r, v.cols, 1.0f, Tb, false, Ts,
+                              s, hs);
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
+    e = nf4::launch_fused_fwd(v, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, table(), hs);
+    return hip_status(e, "qlora_linear_fwd (gemm)");
+}
+
+nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, int64_t M,
+                            const void* A, const void* B, int32_t r, float alpha, const void* T,
+                            void* dX, float* dA, float* dB, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    WeightView v;
+    nf4_status st = check_weight(W, v, true);
+    if (st != NF4_OK) return st;
+    st = check_lora(A, B, r, alpha);
+    if (st != NF4_OK) return st;
+    if (M < 0) return fail(NF4_ERR_ARG, "M must be >= 0");
+    if (!dA || !dB) return fail(NF4_ERR_ARG, "dA or dB is NULL");
+    if (!aligned(dA, 4) || !aligned(dB, 4)) return fail(NF4_ERR_ARG, "dA/dB must be 4-byte aligned");
+    if (M > 0 && (!X || !dY)) return fail(NF4_ERR_ARG, "X or dY is NULL");
+    if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(T, 16) || !aligned(dX, 16))
+        return fail(NF4_ERR_ARG, "X, dY, T and dX must be 16-byte aligned");
+    const size_t rb = rank_buffer_bytes(M, r);
+    const size_t need = T ? rb : 2 * rb;
+    if (M > 0 && (!workspace || workspace_bytes < need))
+        return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LINEAR_BWD)");
+    if (M > 0 && !aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
+    const float s = alpha / (float)r;
+    hipStream_t hs = (hipStream_t)stream;
+    const uint16_t* x = (const uint16_t*)X;
+    const uint16_t* g = (const uint16_t*)dY;
+    const uint16_t* al = (const uint16_t*)A;
+    const uint16_t* bl = (const uint16_t*)B;
+    uint16_t* Us = (uint16_t*)workspace;       // s * dY B
+    const uint16_t* Tb = (const uint16_t*)T;
+    hipError_t e;
+    if (M > 0) {
+        // Us = s dY B   (B stored N x r: contraction-strided)
+        e = nf4::launch_lora_gemm(g, false, bl, true, M, r, v.rows, s, Us, false, nullptr, 0.0f, hs);
+        if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (U)");
+        if (!Tb) {
+            uint16_t* Tw = (uint16_t*)((char*)workspace + rb);
+            e = nf4::launch_lora_gemm(x, false, al, false, M, r, v.cols, 1.0f, Tw, false, nullptr,
+                                      0.0f, hs);
+            if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (T)");
+            Tb = Tw;
+        }
+        if (dX) {
+            e = nf4::launch_fused_bwd_dx(v, g, M, Us, al, r, (uint16_t*)dX, table(), hs);
+            if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dX)");
+        }
+    }
+    // dA = (s U)^T X  (r x K), dB = s dY^T T  (N x r); contraction over the M tokens
+    e = nf4::launch_lora_gemm(Us, true, x, true, r, v.cols, M, 1.0f, dA, true, nullptr, 0.0f, hs);
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dA)");
+    e = nf4::launch_lora_gemm(g, true, Tb, true, v.rows, r, M, s, dB, true, nullptr, 0.0f, hs);
+    return hip_status(e, "qlora_linear_bwd (dB)");
+}
+
+}  // extern "C"

@@ -1,0 +1,299 @@
+// codec.hip -- NF4 quantize, double quantization, constant decode and dequantize.
+//
+// zerotofrontier.app "sft/peft": "Block-wise quantization in one page" (absmax
+// blocks of 64, nearest level), "NF4, derived from normal quantiles" (the
+// levels), "Double quantization" (mean-subtracted 8-bit constants in blocks of
+// 256 with fp32 second-level constants), "The real way" (two codes per byte).
+// All of these kernels are HBM-bound streams.
+#include "launch.h"
+
+namespace nf4 {
+
+// ---------------------------------------------------------------------------
+// Quantize.  One lane owns 16 bytes of input: 4 fp32 or 8 bf16 values.  The
+// lanes of one 64-value block (16 or 8 of them) reduce the absmax with xor
+// shuffles, then each lane encodes its values and writes its 2 or 4 code bytes.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ w, int64_t n,
+                                                  uint8_t* __restrict__ codes,
+                                                  float* __restrict__ absmax, Nf4Table tab) {
+    constexpr int EPL = 16 / sizeof(T);
+    constexpr int LPB = 64 / EPL;
+    const int64_t nblk = (n + 63) / 64;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t b = g / LPB;
+    if (b >= nblk) return;               // whole 64-value groups leave together
+    const int sub = (int)(g % LPB);
+    const int64_t base = b * 64 + (int64_t)sub * EPL;
+    const bool full = (b * 64 + 64 <= n);
+
+    float v[EPL];
+    if (full) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(w + base);
+        if constexpr (sizeof(T) == 4) {
+            v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
+            v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
+        } else {
+            const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(r4[j]); v[2 * j + 1] = bf16_hi(r4[j]); }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int64_t idx = base + e;
+            float x = 0.0f;
+            if (idx < n) {
+                if constexpr (sizeof(T) == 4) x = __uint_as_float(w[idx]);
+                else x = bf16_to_f32(w[idx]);
+            }
+            v[e] = x;
+        }
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) m = fmaxf(m, fabsf(v[e]));
+#pragma unroll
+    for (int o = LPB / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, LPB));
+    if (sub == 0) absmax[b] = m;
+
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        uint32_t code = (m == 0.0f) ? 7u : nf4_encode(__fdiv_rn(v[e], m), tab);
+        if (!full && base + e >= n) code = 0u;
+        packed |= code << (4 * e);
+    }
+    uint8_t* dst = codes + base / 2;
+    if (full) {
+        if constexpr (EPL == 4) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+        else *reinterpret_cast<uint32_t*>(dst) = packed;
+    } else {
+        const int64_t nbytes = (n + 1) / 2;
+#pragma unroll
+        for (int j = 0; j < EPL / 2; ++j)
+            if (base / 2 + j < nbytes) dst[j] = (uint8_t)(packed >> (8 * j));
+    }
+}
+
+hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, uint8_t* codes, float* absmax,
+                           const Nf4Table& tab, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const int64_t nblk = (n + 63) / 64;
+    const int lpb = w_bf16 ? 8 : 16;
+    const int64_t lanes = nblk * lpb;
+    const unsigned grid = (unsigned)((lanes + 255) / 256);
+    if (w_bf16)
+        hipLaunchKernelGGL(k_quantize<uint16_t>, dim3(grid), dim3(256), 0, s,
+                           (const uint16_t*)w, n, codes, absmax, tab);
+    else
+        hipLaunchKernelGGL(k_quantize<uint32_t>, dim3(grid), dim3(256), 0, s,
+                           (const uint32_t*)w, n, codes, absmax, tab);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Mean of the first-level constants.  S is the float64 sum over an aligned
+// pairwise tree: neighbours 2i and 2i+1 are added at every level.  A workgroup
+// reduces an aligned chunk of 2048 values (8 per lane in registers, then xor
+// butterflies, then the 4 waves), which is exactly the tree restricted to that
+// chunk; zero padding past the end leaves every sum unchanged because the
+// constants are >= +0.  Chunks of chunks repeat the same step.
+// ---------------------------------------------------------------------------
+constexpr int SUM_CHUNK = 2048;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_pairwise_chunks(const T* __restrict__ x, int64_t n,
+                                                         double* __restrict__ out, int64_t mean_n1,
+                                                         float* __restrict__ mean) {
+    const int64_t c0 = (int64_t)blockIdx.x * SUM_CHUNK + threadIdx.x * 8;
+    double v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (c0 + e < n) ? (double)x[c0 + e] : 0.0;
+    double s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
+    __shared__ double sw[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) sw[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double r = (sw[0] + sw[1]) + (sw[2] + sw[3]);
+        if (mean_n1 >= 0) *mean = (mean_n1 > 0) ? (float)(r / (double)mean_n1) : 0.0f;
+        else out[blockIdx.x] = r;
+    }
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t double_quantize_ws_bytes(int64_t n1) {
+    size_t total = 0;
+    int64_t len = ceil_div(n1, SUM_CHUNK);
+    while (len > 1) {
+        total += (size_t)len;
+        len = ceil_div(len, SUM_CHUNK);
+    }
+    return total * sizeof(double);
+}
+
+// ---------------------------------------------------------------------------
+// Double-quantize encode: one wave per block of 256 constants, 4 per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_dq_encode(const float* __restrict__ c1, int64_t n1,
+                                                  const float* __restrict__ mean_p,
+                                                  uint8_t* __restrict__ q, float* __restrict__ c2) {
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const float mean = *mean_p;
+    const int64_t base = b * 256 + lane * 4;
+    const bool full = (b * 256 + 256 <= n1);
+    float d[4];
+    if (full) {
+        const float4 c = *reinterpret_cast<const float4*>(c1 + base);
+        d[0] = c.x - mean; d[1] = c.y - mean; d[2] = c.z - mean; d[3] = c.w - mean;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = (base + e < n1) ? c1[base + e] - mean : 0.0f;
+    }
+    float m = fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3])));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) c2[b] = m;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t code = (m == 0.0f) ? 0u : e4m3_from_unit(__fdiv_rn(d[e], m));
+        packed |= code << (8 * e);
+    }
+    if (full) {
+        *reinterpret_cast<uint32_t*>(q + base) = packed;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (base + e < n1) q[base + e] = (uint8_t)(packed >> (8 * e));
+    }
+}
+
+hipError_t launch_double_quantize(const float* c1, int64_t n1, uint8_t* q, float* c2, float* mean,
+                                  double* ws, hipStream_t s) {
+    // mean: repeated chunk reductions until one chunk is left; that last pass writes the mean
+    int64_t len = ceil_div(n1, SUM_CHUNK);
+    if (len <= 1) {
+        hipLaunchKernelGGL(k_pairwise_chunks<float>, dim3(1), dim3(256), 0, s, c1, n1,
+                           (double*)nullptr, n1, mean);
+    } else {
+        hipLaunchKernelGGL(k_pairwise_chunks<float>, dim3((unsigned)len), dim3(256), 0, s, c1, n1,
+                           ws, (int64_t)-1, (float*)nullptr);
+        double* cur = ws;
+        while (true) {
+            const int64_t next = ceil_div(len, SUM_CHUNK);
+            if (next <= 1) {
+                hipLaunchKernelGGL(k_pairwise_chunks<double>, dim3(1), dim3(256), 0, s, cur, len,
+                                   (double*)nullptr, n1, mean);
+                break;
+            }
+            double* nxt = cur + len;
+            hipLaunchKernelGGL(k_pairwise_chunks<double>, dim3((unsigned)next), dim3(256), 0, s,
+                               cur, len, nxt, (int64_t)-1, (float*)nullptr);
+            cur = nxt;
+            len = next;
+        }
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n1 == 0) return e;
+    hipLaunchKernelGGL(k_dq_encode, dim3((unsigned)ceil_div(n1, 256)), dim3(64), 0, s, c1, n1,
+                       mean, q, c2);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Two-level constant decode, one constant per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_double_dequantize(const uint8_t* __restrict__ q,
+                                                           const float* __restrict__ c2,
+                                                           const float* __restrict__ mean_p,
+                                                           int64_t n1, float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n1) return;
+    out[i] = decode_c1(q[i], c2_step(c2[i >> 8]), *mean_p);
+}
+
+hipError_t launch_double_dequantize(const uint8_t* q, const float* c2, const float* mean, int64_t n1,
+                                    float* out, hipStream_t s) {
+    if (n1 == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_double_dequantize, dim3((unsigned)ceil_div(n1, 256)), dim3(256), 0, s, q,
+                       c2, mean, n1, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: one lane per 8 values (one 32-bit word of codes).
+// ---------------------------------------------------------------------------
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
+                                                    const uint8_t* __restrict__ q,
+                                                    const float* __restrict__ c2,
+                                                    const float* __restrict__ mean_p, int64_t n,
+                                                    void* __restrict__ out, Nf4Table tab) {
+    __shared__ float s_lv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if (threadIdx.x == j) s_lv[j] = tab.lv[j];
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i0 = t * 8;
+    if (i0 >= n) return;
+    const int64_t b = i0 >> 6;
+    const float c1p = decode_c1(q[b], c2_step(c2[b >> 8]), *mean_p);
+    const bool full = (i0 + 8 <= n);
+    uint32_t word;
+    if (full) {
+        word = *reinterpret_cast<const uint32_t*>(codes + i0 / 2);
+    } else {
+        word = 0;
+        const int64_t nbytes = (n + 1) / 2;
+        for (int j = 0; j < 4; ++j)
+            if (i0 / 2 + j < nbytes) word |= (uint32_t)codes[i0 / 2 + j] << (8 * j);
+    }
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = s_lv[(word >> (4 * e)) & 0xFu] * c1p;
+    if (OUT_BF16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(out) + i0;
+        if (full) {
+            uint4 pk;
+            pk.x = pack_bf16x2(v[0], v[1]); pk.y = pack_bf16x2(v[2], v[3]);
+            pk.z = pack_bf16x2(v[4], v[5]); pk.w = pack_bf16x2(v[6], v[7]);
+            *reinterpret_cast<uint4*>(o) = pk;
+        } else {
+            for (int e = 0; e < 8; ++e)
+                if (i0 + e < n) o[e] = f32_to_bf16(v[e]);
+        }
+    } else {
+        float* o = reinterpret_cast<float*>(out) + i0;
+        if (full) {
+            *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+            for (int e = 0; e < 8; ++e)
+                if (i0 + e < n) o[e] = v[e];
+        }
+    }
+}
+
+hipError_t launch_dequantize(const WeightView& W, void* out, bool out_bf16, const Nf4Table& tab,
+                             hipStream_t s) {
+    const int64_t n = W.rows * W.cols;
+    if (n == 0) return hipSuccess;
+    const unsigned grid = (unsigned)ceil_div(ceil_div(n, 8), 256);
+    if (out_bf16)
+        hipLaunchKernelGGL(k_dequantize<true>, dim3(grid), dim3(256), 0, s, W.codes, W.q, W.c2,
+                           W.mean, n, out, tab);
+    else
+        hipLaunchKernelGGL(k_dequantize<false>, dim3(grid), dim3(256), 0, s, W.codes, W.q, W.c2,
+                           W.mean, n, out, tab);
+    return hipGetLastError();
+}
+
+}  // namespace nf4

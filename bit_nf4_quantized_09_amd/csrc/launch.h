@@ -1,0 +1,60 @@
+// launch.h -- host-side launchers for the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "nf4_common.h"
+
+namespace nf4 {
+
+// Device view of a double-quantized NF4 weight (N x K, row-major).
+struct WeightView {
+    const uint8_t* codes;
+    const uint8_t* q;
+    const float* c2;
+    const float* mean;
+    int64_t rows;   // N
+    int64_t cols;   // K
+};
+
+// ---- codec ----------------------------------------------------------------
+hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, uint8_t* codes, float* absmax,
+                           const Nf4Table& tab, hipStream_t s);
+size_t double_quantize_ws_bytes(int64_t n1);
+hipError_t launch_double_quantize(const float* c1, int64_t n1, uint8_t* q, float* c2, float* mean,
+                                  double* ws, hipStream_t s);
+hipError_t launch_double_dequantize(const uint8_t* q, const float* c2, const float* mean, int64_t n1,
+                                    float* out, hipStream_t s);
+hipError_t launch_dequantize(const WeightView& W, void* out, bool out_bf16, const Nf4Table& tab,
+                             hipStream_t s);
+
+// ---- LoRA side products (bf16 operands, fp32 accumulation) ----------------
+// C[i][j] = scale * sum_p Aop[i][p] * Bop[p][j], output bf16 or fp32, ldc = Nc;
+// if C2 != NULL it also receives bf16(scale2 * sum) (same layout).
+// a_trans == false: Aop is row-major [Mc x P] (lda = P);  true: stored [P x Mc] (lda = Mc).
+// b_trans == false: Bop^T is row-major [Nc x P] (ldb = P); true: Bop stored [P x Nc] (ldb = Nc).
+hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, bool b_trans,
+                            int64_t Mc, int64_t Nc, int64_t P, float scale, void* C, bool c_f32,
+                            uint16_t* C2, float scale2, hipStream_t s);
+// T = X A^T for few tokens (M <= 16): X [M x K], A [r x K] -> T bf16 [M x r] and
+// Ts = bf16(s * X A^T).
+hipError_t launch_lora_t_small(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int r,
+                               uint16_t* T, uint16_t* Ts, float s, hipStream_t st);
+
+// ---- fused dequant products -------------------------------------------------
+// Y = X W'^T + Ts B^T, Ts = s T   (MFMA GEMM, dequantization fused into the W operand load)
+hipError_t launch_fused_fwd(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Ts,
+                            const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
+                            hipStream_t st);
+// Same product for M <= 16 tokens (HBM-bound dequant-GEMV).
+hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Ts,
+                             const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
+                             hipStream_t st);
+// dX = dY W' + Us A, Us = s U   (contraction over N, W' used transposed)
+hipError_t launch_fused_bwd_dx(const WeightView& W, const uint16_t* dY, int64_t M, const uint16_t* Us,
+                               const uint16_t* Al, int r, uint16_t* dX, const Nf4Table& tab,
+                               hipStream_t st);
+
+}  // namespace nf4

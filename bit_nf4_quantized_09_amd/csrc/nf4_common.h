@@ -1,0 +1,159 @@
+// nf4_common.h -- device helpers shared by the gfx950 kernels of the library.
+//
+// Number formats (zerotofrontier.app "sft/peft" page):
+//   NF4   -- 16-level codebook, "NF4, derived from normal quantiles"; the levels
+//            and the 15 encode thresholds are computed on the host and passed by
+//            value (Nf4Table), so they live in SGPRs / constant registers.
+//   E4M3  -- the 8-bit float of "Double quantization", read as OCP FP8 E4M3
+//            (bias 7, largest finite 448); stored codes are 448 * (c1-mean)/c2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nf4 {
+
+// 16 levels (ascending) and the 15 fp32 thresholds t_j: x > t_j exactly when
+// x lies above the float64 midpoint between levels j and j+1.
+struct Nf4Table {
+    float lv[16];
+    float th[15];
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 a = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, a);
+}
+
+// ---------------------------------------------------------------------------
+// OCP FP8 E4M3
+// ---------------------------------------------------------------------------
+// Exact value of a code (no NaN codes are ever produced).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 0xFu;
+    const uint32_t m = b & 7u;
+    // normal: (8+m) * 2^(e-10) -> fp32 exponent e-7+127, mantissa m<<20
+    float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    float sub = (float)m * 0x1p-9f;
+    float mag = (e == 0u) ? sub : normal;
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// Nearest E4M3 code of v = s * 448 (exact in float64), ties to even code; the
+// sign bit follows s.  |s| <= 1.
+__device__ __forceinline__ uint32_t e4m3_from_unit(float s) {
+    const uint32_t sign = (__float_as_uint(s) >> 24) & 0x80u;
+    const double a = fabs((double)s * 448.0);
+    if (a < 0x1p-6) {                                   // subnormal grid, step 2^-9
+        const double m = rint(a * 512.0);               // 0..8; 8 is the smallest normal
+        return sign | (uint32_t)m;
+    }
+    int e = ilogb(a);                                    // -6 .. 8
+    double m = rint(ldexp(a, 3 - e));                    // 8 .. 16
+    uint32_t mi = (uint32_t)m;
+    if (mi == 16u) { mi = 8u; e += 1; }
+    return sign | ((uint32_t)(e + 7) << 3) | (mi - 8u);
+}
+
+// Two-level constant decode: c1' = fma(E4M3(q), step, mean), step = fp32(c2/448).
+__device__ __forceinline__ float decode_c1(uint32_t q, float step, float mean) {
+    return __fmaf_rn(e4m3_to_f32(q), step, mean);
+}
+
+__device__ __forceinline__ float c2_step(float c2) { return __fdiv_rn(c2, 448.0f); }
+
+// ---------------------------------------------------------------------------
+// NF4 encode: number of thresholds below x, by a 4-step branch-free search.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t nf4_encode(float x, const Nf4Table& t) {
+    uint32_t i = (x > t.th[7]) ? 8u : 0u;
+    const float t3 = i ? t.th[11] : t.th[3];
+    i += (x > t3) ? 4u : 0u;
+    const float t1 = (i & 8u) ? ((i & 4u) ? t.th[13] : t.th[9]) : ((i & 4u) ? t.th[5] : t.th[1]);
+    i += (x > t1) ? 2u : 0u;
+    float t0;
+    if (i & 8u) {
+        t0 = (i & 4u) ? ((i & 2u) ? t.th[14] : t.th[12]) : ((i & 2u) ? t.th[10] : t.th[8]);
+    } else {
+        t0 = (i & 4u) ? ((i & 2u) ? t.th[6] : t.th[4]) : ((i & 2u) ? t.th[2] : t.th[0]);
+    }
+    i += (x > t0) ? 1u : 0u;
+    return i;
+}
+
+// ---------------------------------------------------------------------------
+// NF4 decode of 8 packed codes through a per-lane scaled table.
+//
+// A lane that owns one (row, 64-block) builds the 16 scaled values
+// bf16(fp32(level_j * c1')) once, split into a low-byte table and a high-byte
+// table (4 registers each).  v_perm_b32 then looks up four 8-entry byte
+// tables at a time; bit 3 of each code picks the half.
+// ---------------------------------------------------------------------------
+struct ScaledTable {
+    uint32_t lo[4];   // low bytes of entries 0..15, four per register
+    uint32_t hi[4];   // high bytes
+};
+
+__device__ __forceinline__ ScaledTable make_scaled_table(const Nf4Table& t, float c1p) {
+    uint32_t p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = pack_bf16x2(t.lv[2 * j] * c1p, t.lv[2 * j + 1] * c1p);
+    ScaledTable s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // bytes of p[2j] = [e0.lo e0.hi e1.lo e1.hi], p[2j+1] = [e2.lo ...]
+        s.lo[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x06040200u);
+        s.hi[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x07050301u);
+    }
+    return s;
+}
+
+// Byte lane k of `sel` holds a code 0..15; returns the table bytes for them.
+__device__ __forceinline__ void lookup4(const ScaledTable& s, uint32_t sel, uint32_t& lo, uint32_t& hi) {
+    const uint32_t s7 = sel & 0x07070707u;
+    const uint32_t m = ((sel >> 3) & 0x01010101u) * 0xFFu;   // 0xFF where code >= 8
+    const uint32_t la = __builtin_amdgcn_perm(s.lo[1], s.lo[0], s7);
+    const uint32_t lb = __builtin_amdgcn_perm(s.lo[3], s.lo[2], s7);
+    const uint32_t ha = __builtin_amdgcn_perm(s.hi[1], s.hi[0], s7);
+    const uint32_t hb = __builtin_amdgcn_perm(s.hi[3], s.hi[2], s7);
+    lo = (lb & m) | (la & ~m);
+    hi = (hb & m) | (ha & ~m);
+}
+
+// 8 codes (nibble i = element i) -> 8 bf16 in element order (4 registers).
+__device__ __forceinline__ void decode8(const ScaledTable& s, uint32_t w, uint32_t out[4]) {
+    const uint32_t ev = w & 0x0F0F0F0Fu;           // elements 0,2,4,6
+    const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;    // elements 1,3,5,7
+    uint32_t elo, ehi, olo, ohi;
+    lookup4(s, ev, elo, ehi);
+    lookup4(s, od, olo, ohi);
+    // bf16 pairs (e0,e2),(e4,e6) and (o1,o3),(o5,o7)
+    const uint32_t e01 = __builtin_amdgcn_perm(ehi, elo, 0x05010400u);
+    const uint32_t e23 = __builtin_amdgcn_perm(ehi, elo, 0x07030602u);
+    const uint32_t o01 = __builtin_amdgcn_perm(ohi, olo, 0x05010400u);
+    const uint32_t o23 = __builtin_amdgcn_perm(ohi, olo, 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);   // elements 0,1
+    out[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);   // 2,3
+    out[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);   // 4,5
+    out[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);   // 6,7
+}
+
+}  // namespace nf4

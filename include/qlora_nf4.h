@@ -1,0 +1,159 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) QLoRA NF4 linear-layer library.
+ *
+ * The frozen weight of a linear layer is stored as blockwise-absmax NF4 with
+ * double-quantized constants, and the layer runs
+ *     Y = X dequant(W)^T + (alpha/r) (X A^T) B^T
+ * forward, with dX, dA and dB backward (no gradient for W).
+ *
+ * Passages that define the operations (page title, section):
+ *   [BQ]  zerotofrontier.app "sft/peft", "Block-wise quantization in one page"
+ *   [NF]  same page, "NF4, derived from normal quantiles"
+ *   [DQ]  same page, "Double quantization" (stubs double_quantize / double_dequantize)
+ *   [E2E] same page, "Paged optimizers, and QLoRA end to end" (r, alpha, gradient flow)
+ *   [RW]  same page, "The real way" (two codes per byte, dequant fused into the matmul)
+ *   [PT]  prism.theerrors.in QLoRA explainer, "Putting it together" (layer formula)
+ *
+ * Conventions shared by every entry point:
+ *   - Memory: every pointer argument is device memory unless stated; the
+ *     caller owns all buffers.  The library never allocates or frees device
+ *     memory and keeps no pointer after a call returns.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *     only enqueue work; inputs must stay alive until the stream has run it.
+ *     No call synchronizes the host.
+ *   - Layouts: row-major, dense.  W is N x K (out x in); blocks of 64 run
+ *     along the flattened row-major weight.  bf16 data is IEEE bfloat16.
+ *   - Errors: arguments are checked on the host before any HIP call; on
+ *     error nothing is enqueued and a status is returned, with a message
+ *     from nf4_last_error().  Faults inside kernels surface at the next
+ *     synchronizing HIP call, as for any HIP work.
+ *   - Alignment: device pointers to arrays of 16-byte vectors (w, codes,
+ *     X, A, B, dY, Y, T, dX, out) must be 16-byte aligned.
+ *   - Concurrency: calls are reentrant; concurrent calls on different
+ *     streams must not share output buffers or workspaces.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nf4_status {
+    NF4_OK = 0,
+    NF4_ERR_ARG = 1,          /* null pointer, negative or inconsistent size, misalignment */
+    NF4_ERR_UNSUPPORTED = 2,  /* valid for the method, outside what this library implements */
+    NF4_ERR_WORKSPACE = 3,    /* workspace missing or smaller than nf4_workspace_bytes() */
+    NF4_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} nf4_status;
+
+typedef enum nf4_dtype { NF4_F32 = 0, NF4_BF16 = 1 } nf4_dtype;
+
+/* A double-quantized NF4 weight: the storage tuple of [DQ] + [RW].
+ * n = rows * cols values; n1 = ceil(n/64) first-level constants. */
+typedef struct nf4_weight {
+    const uint8_t* codes;  /* ceil(n/2) bytes; element 2i in the low nibble of byte i */
+    const uint8_t* q;      /* n1 bytes: OCP FP8 E4M3 codes of 448*(c1 - mean)/c2 */
+    const float* c2;       /* ceil(n1/256) fp32 second-level constants */
+    const float* mean;     /* 1 fp32: mean of the first-level constants */
+    int64_t rows;          /* N (out features) */
+    int64_t cols;          /* K (in features) */
+} nf4_weight;
+
+/* Workspace selectors for nf4_workspace_bytes(). */
+#define NF4_OP_DOUBLE_QUANTIZE 1
+#define NF4_OP_LINEAR_FWD 2
+#define NF4_OP_LINEAR_BWD 3
+
+/* [BQ]+[NF]: blockwise absmax NF4 quantization (stub nf4_quantize(w, block=64)).
+ * For each block of 64 consecutive values (the last may be partial):
+ * absmax[b] = max|w|; each value becomes the code of the nearest NF4 level of
+ * w/absmax (IEEE fp32 division; a value exactly between two levels takes the
+ * lower code; an all-zero block gives code 7, the exact-zero level).
+ *   w       n values, dtype NF4_F32 or NF4_BF16 (widened exactly to fp32)
+ *   n       number of values, >= 0 (n == 0 enqueues nothing)
+ *   blocksize  must be 64
+ *   codes   out: ceil(n/2) bytes, two codes per byte, low nibble first; the
+ *           high nibble past an odd n is 0
+ *   absmax  out: ceil(n/64) fp32 first-level constants c1 */
+nf4_status nf4_quantize(const void* w, nf4_dtype dtype, int64_t n, int32_t blocksize,
+                        uint8_t* codes, float* absmax, void* stream);
+
+/* [DQ]: double quantization of the first-level constants (stub
+ * double_quantize(c1, block=256)).  mean = fp32(S / n1), S the float64 sum of
+ * c1 over an aligned pairwise tree; d = fp32(c1 - mean); per block of 256:
+ * c2 = max|d|, q = E4M3 round-to-nearest-even of 448 * fp32(d / c2) (0 when
+ * c2 == 0).  The mean never leaves the device.
+ *   absmax  n1 fp32 values >= +0 (the output of nf4_quantize)
+ *   blocksize2  must be 256
+ *   q       out: n1 bytes;  c2 out: ceil(n1/256) fp32;  mean out: 1 fp32
+ *   workspace   nf4_workspace_bytes(NF4_OP_DOUBLE_QUANTIZE, 0, n1, 0, 0) bytes,
+ *               8-byte aligned (partial sums). */
+nf4_status nf4_double_quantize(const float* absmax, int64_t n1, int32_t blocksize2, uint8_t* q,
+                               float* c2, float* mean, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* [DQ]: two-level constant decode (stub double_dequantize(q, c2, mean)):
+ * c1'[i] = fma(E4M3(q[i]), fp32(c2[i/256] / 448), mean), one rounding.
+ *   c1_out  out: n1 fp32 */
+nf4_status nf4_double_dequantize(const uint8_t* q, const float* c2, const float* mean, int64_t n1,
+                                 int32_t blocksize2, float* c1_out, void* stream);
+
+/* [BQ]+[DQ]: dequantization of a whole weight (stub nf4_dequantize(codes,
+ * absmax, shape), with the double-quantized constants in place of absmax):
+ * out[i] = fp32(level[code_i] * c1'[i/64]); NF4_BF16 output rounds that value
+ * to nearest even.
+ *   out     rows*cols values of out_dtype */
+nf4_status nf4_dequantize(const nf4_weight* W, void* out, nf4_dtype out_dtype, void* stream);
+
+/* [PT]+[E2E]+[RW]: QLoRA linear forward.
+ *   Y = X W'^T + s (X A^T) B^T,  s = alpha / r,  W' = dequant(W) rounded to bf16
+ * with the dequantization fused into the matrix multiply.
+ *   W       N x K weight, K a multiple of 64, N a multiple of 8
+ *   X       bf16 M x K;  M >= 0 (M == 0 enqueues nothing)
+ *   A       bf16 r x K;  B  bf16 N x r;  1 <= r <= 128, r a multiple of 8
+ *   Y       out: bf16 M x N
+ *   T_out   out: bf16 M x r copy of X A^T for the backward, or NULL
+ *   workspace  nf4_workspace_bytes(NF4_OP_LINEAR_FWD, M, N, K, r) bytes,
+ *              256-byte aligned (may be NULL if that is 0) */
+nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const void* A,
+                            const void* B, int32_t r, float alpha, void* Y, void* T_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* [E2E]+[PT]: QLoRA linear backward; the 4-bit weight receives no gradient.
+ * With U = dY B:
+ *   dX = dY W' + s U A   (bf16 M x K)
+ *   dA = s U^T X         (fp32 r x K, overwritten)
+ *   dB = s dY^T T        (fp32 N x r, overwritten), T = X A^T
+ *   T       bf16 M x r from qlora_linear_fwd, or NULL to recompute it
+ *   dX      may be NULL to skip the input gradient
+ * Shapes and limits as for qlora_linear_fwd; M == 0 writes dA = dB = 0. */
+nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, int64_t M,
+                            const void* A, const void* B, int32_t r, float alpha, const void* T,
+                            void* dX, float* dA, float* dB, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace an operation needs (0 = none).  For
+ * NF4_OP_DOUBLE_QUANTIZE pass n1 as N. */
+size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* [DQ] storage accounting for n values: codes ceil(n/2) bytes, q ceil(n/64)
+ * bytes, c2 4*ceil(n1/256) bytes -- 4 + 8/64 + 32/(64*256) ~ 4.127 bits per
+ * value.  Host-only; any output pointer may be NULL. */
+void nf4_storage_bytes(int64_t n, int32_t blocksize, int32_t blocksize2, size_t* codes_bytes,
+                       size_t* q_bytes, size_t* c2_bytes);
+
+/* [NF]: host copy of the 16 NF4 levels, ascending (code 7 = 0, 0 = -1, 15 = +1). */
+void nf4_codebook(float out[16]);
+
+/* Message for the last error returned on the calling thread ("" if none). */
+const char* nf4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */
