@@ -1,0 +1,305 @@
+"""Benchmark of the QLoRA NF4 linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is the layer's training pass over one batch of synthetic input: for
+the default workload (one LLaMA-65B-shaped decoder layer: q, k, v, o, gate, up,
+down; 4096 tokens; LoRA r = 64, alpha = 16 on every projection) the seven
+forwards in layer order, then the seven backwards in reverse order.  The
+frozen weights are quantized once beforehand (as in training); that codec
+path, and the few-token dequant-GEMV, are measured in the same run and
+reported under "paths".  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `roofline` covers the dominant kernel (the fused
+dequant GEMM of the forward), timed with HIP events that the library records
+around each of its launches on the launch stream; `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA NF4 linear fwd+bwd TFLOP/s (% MFMA peak); NF4 dequant/quant GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+NF4_BYTES_PER_PARAM = 0.5 + 1.0 / 64 + 4.0 / (64 * 256)
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="llama65b_layer",
+                   choices=["llama65b_layer", "llama7b_layer", "tiny"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-paths", action="store_true", help="skip the codec and GEMV path figures")
+    p.add_argument("--cpu-tokens", type=int, default=32, help="tokens in the CPU-oracle sample")
+    return p.parse_args()
+
+
+def layer_flops(M, projs, r):
+    """Algorithmic flops of one fwd+bwd pass (no dW; T saved from the forward)."""
+    fwd = bwd = 0
+    for _, N, K in projs:
+        fwd += 2 * M * N * K + 2 * M * K * r + 2 * M * r * N
+        bwd += 2 * M * N * K + 2 * M * N * r + 2 * M * r * K + 2 * r * M * K + 2 * N * M * r
+    return fwd, bwd
+
+
+def build_layer(workload, dev):
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+    from workloads import (LLAMA7B, LLAMA65B, Draw, layer_projections, linear_inputs, seed_of)
+
+    if workload == "tiny":
+        projs = [("w", 256, 256)]
+        M, r, alpha = 16, 8, 16.0
+    elif workload == "llama7b_layer":
+        projs = layer_projections(LLAMA7B["d"], LLAMA7B["ffn"])
+        M, r, alpha = 2048, 64, 16.0
+    else:
+        projs = layer_projections(LLAMA65B["d"], LLAMA65B["ffn"])
+        M, r, alpha = 4096, 64, 16.0
+    layer = []
+    for i, (name, N, K) in enumerate(projs):
+        W, X, A, B, dY = linear_inputs(N, K, M, r, seed=seed_of(5, i, N, K), device=dev)
+        Wq = nf4.quantize_weight(W)
+        layer.append(dict(name=name, N=N, K=K, W=W, Wq=Wq, X=X, A=A, B=B, dY=dY))
+    torch.cuda.synchronize()
+    return layer, projs, M, r, alpha
+
+
+def event_pool(n):
+    """n pairs of timing events.  torch creates the underlying hipEvent on the first
+    record, so each is recorded once here, outside any timed region."""
+    import torch
+
+    pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+    for a, b in pool:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    return iter(pool)
+
+
+def run_step(layer, alpha, events=None, pool=None):
+    import bit_nf4_quantized_09_amd as nf4
+
+    saved = []
+    for p in layer:
+        if events is not None:
+            ev = next(pool)
+            events["fwd"].append((ev, p))
+            nf4.nf4_profile_next_fused(*ev)
+        Y, T = nf4.qlora_linear_fwd(p["Wq"], p["X"], p["A"], p["B"], alpha)
+        saved.append((Y, T))
+    grads = []
+    for p, (Y, T) in zip(reversed(layer), reversed(saved)):
+        if events is not None:
+            ev = next(pool)
+            events["bwd"].append((ev, p))
+            nf4.nf4_profile_next_fused(*ev)
+        grads.append(nf4.qlora_linear_bwd(p["Wq"], p["X"], p["dY"], p["A"], p["B"], alpha, T=T))
+    return saved, grads
+
+
+def kernel_roofline(events, M, r, kind):
+    """Average duration of the fused kernel launches and its achieved TFLOP/s."""
+    tot_ms = 0.0
+    tot_flops = 0
+    for (start, stop), p in events[kind]:
+        tot_ms += start.elapsed_time(stop)
+        N, K = p["N"], p["K"]
+        tot_flops += 2 * M * N * K + (2 * M * N * r if kind == "fwd" else 2 * M * K * r)
+    n = len(events[kind])
+    avg_ms = tot_ms / n
+    achieved = tot_flops / (tot_ms / 1e3) / 1e12
+    return dict(kernel="k_fused_fwd" if kind == "fwd" else "k_fused_bwd_dx", launches=n,
+                avg_us=avg_ms * 1e3, flops_per_launch=tot_flops / n, achieved=achieved)
+
+
+def codec_paths(layer, dev, reps=3):
+    """GB/s of quantize, double-quantize and dequantize over the layer's fp32 weights."""
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+
+    n_total = sum(p["N"] * p["K"] for p in layer)
+    res = {}
+    for _ in range(1):   # warm-up pass
+        for p in layer:
+            c, a = nf4.nf4_quantize(p["W"])
+            nf4.nf4_double_quantize(a)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / 1e3 / reps
+
+    absmax = {}
+
+    def quant():
+        for p in layer:
+            absmax[p["name"]] = nf4.nf4_quantize(p["W"])[1]
+
+    tq = timed(quant)
+    bq = n_total * (4 + 0.5 + 4 / 64)
+    res["quantize_fp32"] = dict(GBps=bq / tq / 1e9, ms=tq * 1e3, bytes=bq)
+
+    def dq():
+        for p in layer:
+            nf4.nf4_double_quantize(absmax[p["name"]])
+
+    tdq = timed(dq)
+    bdq = n_total * (4 / 64 + 1 / 64 + 4 / (64 * 256))
+    res["double_quantize"] = dict(GBps=bdq / tdq / 1e9, ms=tdq * 1e3, bytes=bdq)
+
+    def deq():
+        for p in layer:
+            nf4.nf4_dequantize(p["Wq"], torch.float32)
+
+    tdeq = timed(deq)
+    bdeq = n_total * (NF4_BYTES_PER_PARAM + 4)
+    res["dequantize_fp32"] = dict(GBps=bdeq / tdeq / 1e9, ms=tdeq * 1e3, bytes=bdeq)
+    for v in res.values():
+        v["frac_hbm"] = v["GBps"] / PEAK_HBM_GBS
+    res["params"] = n_total
+    return res
+
+
+def gemv_paths(layer, dev, r, alpha, reps=5):
+    """Few-token dequant-GEMV: GB/s over the layer's weights (rotating > 256 MB so the
+    Infinity Cache cannot hold them), M in {1, 4, 16}."""
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+    from workloads import Draw, seed_of
+
+    out = {}
+    for M in (1, 4, 16):
+        d = Draw(seed_of(6, M), dev)
+        xs = {p["name"]: d.bf16((M, p["K"]), 1.0) for p in layer}
+        for p in layer:
+            nf4.qlora_linear_fwd(p["Wq"], xs[p["name"]], p["A"], p["B"], alpha)
+        torch.cuda.synchronize()
+        evs = []
+        pool = event_pool(reps * len(layer))
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            for p in layer:
+                ev = next(pool)
+                nf4.nf4_profile_next_fused(*ev)
+                nf4.qlora_linear_fwd(p["Wq"], xs[p["name"]], p["A"], p["B"], alpha)
+                evs.append((ev, p))
+        t1.record()
+        torch.cuda.synchronize()
+        call_s = t0.elapsed_time(t1) / 1e3 / len(evs)
+        kern_s = sum(a.elapsed_time(b) for (a, b), _ in evs) / 1e3 / len(evs)
+        # algorithmic bytes of the fused GEMV launch: packed weight + B + X + Ts + Y
+        kbytes = sum(NF4_BYTES_PER_PARAM * p["N"] * p["K"] + 2 * r * p["N"] + 2 * M * p["K"]
+                     + 2 * M * r + 2 * M * p["N"] for _, p in evs) / len(evs)
+        out["M%d" % M] = dict(kernel_GBps=kbytes / kern_s / 1e9,
+                              kernel_frac_hbm=kbytes / kern_s / 1e9 / PEAK_HBM_GBS,
+                              kernel_avg_us=kern_s * 1e6, call_avg_us=call_s * 1e6,
+                              launches=len(evs))
+    return out
+
+
+def cpu_baseline(layer, alpha, r, tokens):
+    """The CPU oracle (float64, OpenMP) on `tokens` tokens through every projection."""
+    import numpy as np
+    import oracle
+    from workloads import host_f32
+
+    t_total = 0.0
+    flops = 0
+    for p in layer:
+        codes, absmax = oracle.nf4_quantize(host_f32(p["W"]).reshape(-1))
+        q, c2, mean = oracle.double_quantize(absmax)
+        Wd = oracle.nf4_dequantize(codes, q, c2, mean, (p["N"], p["K"]))
+        X = host_f32(p["X"][:tokens])
+        dY = host_f32(p["dY"][:tokens])
+        A, B = host_f32(p["A"]), host_f32(p["B"])
+        t0 = time.perf_counter()
+        oracle.qlora_linear_fwd(Wd, X, A, B, alpha)
+        oracle.qlora_linear_bwd(Wd, X, dY, A, B, alpha)
+        t_total += time.perf_counter() - t0
+        f, b = layer_flops(tokens, [(p["name"], p["N"], p["K"])], r)
+        flops += f + b
+        del Wd
+    return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
+                kind="oracle", seconds=t_total,
+                sample="fwd+bwd of %d tokens through all %d projections (same weights, "
+                       "float64 oracle)" % (tokens, len(layer)))
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    layer, projs, M, r, alpha = build_layer(args.workload, dev)
+    fwd_flops, bwd_flops = layer_flops(M, projs, r)
+
+    for _ in range(args.warmup):
+        run_step(layer, alpha)
+    torch.cuda.synchronize()
+
+    events = {"fwd": [], "bwd": []}
+    pool = event_pool(args.steps * 2 * len(layer))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(layer, alpha, events, pool)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = (fwd_flops + bwd_flops) / (ms / 1e3) / 1e12
+
+    kf = kernel_roofline(events, M, r, "fwd")
+    kb = kernel_roofline(events, M, r, "bwd")
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian weights/activations at LLaMA shapes)",
+        "config": {"workload": args.workload, "tokens": M, "projections": [p[0] for p in projs],
+                   "shapes_NxK": [[p[1], p[2]] for p in projs], "r": r, "alpha": alpha,
+                   "nf4_blocksize": 64, "dq_blocksize": 256, "parallelism": "single-gpu",
+                   "fwd_tflop": fwd_flops / 1e12, "bwd_tflop": bwd_flops / 1e12,
+                   "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "kernel": kf["kernel"], "achieved": round(kf["achieved"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kf["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_us": round(kf["avg_us"], 2), "launches": kf["launches"],
+                     "bwd_dx_kernel": {"kernel": kb["kernel"], "achieved": round(kb["achieved"], 2),
+                                       "frac": round(kb["achieved"] / PEAK_BF16_TFLOPS, 4),
+                                       "avg_us": round(kb["avg_us"], 2)}},
+    }
+    if not args.no_paths and args.workload != "tiny":
+        line["paths"] = {"codec": codec_paths(layer, dev), "gemv": gemv_paths(layer, dev, r, alpha)}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(layer, alpha, r, min(args.cpu_tokens, M))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

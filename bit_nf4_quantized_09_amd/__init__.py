@@ -23,6 +23,7 @@ __all__ = [
     "NF4Error", "NF4Weight", "lib_path", "load_library", "nf4_quantize", "nf4_double_quantize",
     "nf4_double_dequantize", "nf4_dequantize", "quantize_weight", "qlora_linear_fwd",
     "qlora_linear_bwd", "nf4_storage_bytes", "nf4_codebook", "nf4_workspace_bytes",
+    "nf4_profile_next_fused",
     "NF4_OP_DOUBLE_QUANTIZE", "NF4_OP_LINEAR_FWD", "NF4_OP_LINEAR_BWD",
 ]
 
@@ -86,6 +87,8 @@ def load_library():
                                     ctypes.POINTER(_sz)]
     L.nf4_codebook.restype = None
     L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.nf4_profile_next_fused.restype = None
+    L.nf4_profile_next_fused.argtypes = [_vp, _vp]
     L.nf4_last_error.restype = ctypes.c_char_p
     L.nf4_last_error.argtypes = []
     _lib = L
@@ -143,6 +146,14 @@ class NF4Weight:
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.codes, self.q, self.c2, self.mean))
+
+
+def nf4_profile_next_fused(start: "torch.cuda.Event", stop: "torch.cuda.Event"):
+    """Arm the library's profiling hook: the next fused dequant kernel launched on this
+    thread records `start` before and `stop` after itself on its stream."""
+    start_h = ctypes.c_void_p(start.cuda_event) if start is not None else None
+    stop_h = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
+    load_library().nf4_profile_next_fused(start_h, stop_h)
 
 
 def nf4_codebook():

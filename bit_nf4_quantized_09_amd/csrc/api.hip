@@ -120,6 +120,12 @@ extern "C" {
 
 const char* nf4_last_error(void) { return g_last_error.c_str(); }
 
+void nf4_profile_next_fused(void* start_event, void* stop_event) {
+    nf4::FusedEvents& ev = nf4::fused_events();
+    ev.start = (hipEvent_t)start_event;
+    ev.stop = (hipEvent_t)stop_event;
+}
+
 void nf4_codebook(float out[16]) {
     if (!out) return;
     memcpy(out, table().lv, sizeof(float) * 16);

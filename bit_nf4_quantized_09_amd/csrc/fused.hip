@@ -185,6 +185,27 @@ void k_fused_fwd(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
 
 static bool g_fwd_attr = false, g_bwd_attr = false;
 
+FusedEvents& fused_events() {
+    static thread_local FusedEvents ev;
+    return ev;
+}
+
+// Launch `fn` between the armed profiling events (if any), then disarm.
+template <typename F>
+static hipError_t with_events(hipStream_t st, F&& fn) {
+    FusedEvents& ev = fused_events();
+    const FusedEvents armed = ev;
+    ev = FusedEvents{};
+    if (armed.start) {
+        hipError_t e = hipEventRecord(armed.start, st);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = fn();
+    if (e != hipSuccess) return e;
+    if (armed.stop) return hipEventRecord(armed.stop, st);
+    return hipSuccess;
+}
+
 hipError_t launch_fused_fwd(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Ts,
                             const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
                             hipStream_t st) {
@@ -196,9 +217,11 @@ hipError_t launch_fused_fwd(const WeightView& W, const uint16_t* X, int64_t M, c
         g_fwd_attr = true;
     }
     dim3 grid((unsigned)((W.rows + FT - 1) / FT), (unsigned)((M + FT - 1) / FT));
-    hipLaunchKernelGGL(k_fused_fwd, grid, dim3(256), FLDS, st, W.codes, W.q, W.c2, W.mean, W.rows,
-                       W.cols, X, M, Ts, Bl, r, Y, tab);
-    return hipGetLastError();
+    return with_events(st, [&] {
+        hipLaunchKernelGGL(k_fused_fwd, grid, dim3(256), FLDS, st, W.codes, W.q, W.c2, W.mean,
+                           W.rows, W.cols, X, M, Ts, Bl, r, Y, tab);
+        return hipGetLastError();
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -382,9 +405,11 @@ hipError_t launch_fused_bwd_dx(const WeightView& W, const uint16_t* dY, int64_t 
         g_bwd_attr = true;
     }
     dim3 grid((unsigned)((W.cols + FT - 1) / FT), (unsigned)((M + FT - 1) / FT));
-    hipLaunchKernelGGL(k_fused_bwd_dx, grid, dim3(256), FLDS, st, W.codes, W.q, W.c2, W.mean,
-                       W.rows, W.cols, dY, M, Us, Al, r, dX, tab);
-    return hipGetLastError();
+    return with_events(st, [&] {
+        hipLaunchKernelGGL(k_fused_bwd_dx, grid, dim3(256), FLDS, st, W.codes, W.q, W.c2, W.mean,
+                           W.rows, W.cols, dY, M, Us, Al, r, dX, tab);
+        return hipGetLastError();
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -499,9 +524,11 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
                              hipStream_t st) {
     if (M == 0 || W.rows == 0) return hipSuccess;
     dim3 grid((unsigned)((W.rows + GV_ROWS - 1) / GV_ROWS));
-    hipLaunchKernelGGL(k_fused_gemv, grid, dim3(256), 0, st, W.codes, W.q, W.c2, W.mean, W.rows,
-                       W.cols, X, (int)M, Ts, Bl, r, Y, tab);
-    return hipGetLastError();
+    return with_events(st, [&] {
+        hipLaunchKernelGGL(k_fused_gemv, grid, dim3(256), 0, st, W.codes, W.q, W.c2, W.mean,
+                           W.rows, W.cols, X, (int)M, Ts, Bl, r, Y, tab);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace nf4

@@ -43,6 +43,13 @@ hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, 
 hipError_t launch_lora_t_small(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int r,
                                uint16_t* T, uint16_t* Ts, float s, hipStream_t st);
 
+// ---- profiling hook: events around the next fused launch on this thread ----
+struct FusedEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+FusedEvents& fused_events();
+
 // ---- fused dequant products -------------------------------------------------
 // Y = X W'^T + Ts B^T, Ts = s T   (MFMA GEMM, dequantization fused into the W operand load)
 hipError_t launch_fused_fwd(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Ts,

@@ -149,6 +149,13 @@ void nf4_storage_bytes(int64_t n, int32_t blocksize, int32_t blocksize2, size_t*
 /* [NF]: host copy of the 16 NF4 levels, ascending (code 7 = 0, 0 = -1, 15 = +1). */
 void nf4_codebook(float out[16]);
 
+/* Profiling hook: the next fused dequant kernel (forward GEMM, dequant-GEMV or
+ * backward dX GEMM) that the calling thread launches records the hipEvent_t
+ * `start` on its stream right before itself and `stop` right after, then the
+ * hook disarms.  Events are created and owned by the caller; NULL, NULL
+ * disarms without recording. */
+void nf4_profile_next_fused(void* start_event, void* stop_event);
+
 /* Message for the last error returned on the calling thread ("" if none). */
 const char* nf4_last_error(void);
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted(["nf4_quantize", "nf4_double_quantize", "nf4_double_dequantize",
                             "nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
                             "nf4_workspace_bytes", "nf4_storage_bytes", "nf4_codebook",
-                            "nf4_last_error"])
+                            "nf4_last_error", "nf4_profile_next_fused"])
     for name in names:
         assert hasattr(L, name), name
     # and the C symbols are unmangled (extern "C")
@@ -78,10 +78,6 @@ def test_workspace_sizes():
 
 
 # --- argument validation: every case below fails before any HIP call -------------
-
-def _status(fn, *args):
-    return fn(*args)
-
 
 def test_quantize_rejects_bad_arguments():
     L = nf4.load_library()
