@@ -114,6 +114,21 @@ nf4_status check_lora(const void* A, const void* B, int32_t r, float alpha) {
 
 size_t rank_buffer_bytes(int64_t M, int32_t r) { return align256((size_t)M * (size_t)r * 2); }
 
+// Workspace layouts (256-byte aligned pieces):
+//   forward : [s*T bf16 M x r][T bf16 M x r, when T_out is NULL][fp32 split-contraction slices]
+//   backward: [s*U bf16 M x r][T bf16 M x r, when T is NULL][fp32 split-contraction slices]
+size_t fwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+    (void)N;
+    return nf4::skinny_partial_bytes(M, r, K);
+}
+size_t bwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+    size_t b = nf4::skinny_partial_bytes(M, r, N);
+    const size_t c[3] = {nf4::skinny_partial_bytes(M, r, K), nf4::skinny_partial_bytes(K, r, M),
+                         nf4::skinny_partial_bytes(N, r, M)};
+    for (size_t x : c) b = x > b ? x : b;
+    return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,8 +163,8 @@ size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t 
     if (M < 0 || N < 0 || r < 0) return 0;
     switch (op) {
         case NF4_OP_DOUBLE_QUANTIZE: return nf4::double_quantize_ws_bytes(N);
-        case NF4_OP_LINEAR_FWD: return 2 * rank_buffer_bytes(M, r);
-        case NF4_OP_LINEAR_BWD: return 2 * rank_buffer_bytes(M, r);
+        case NF4_OP_LINEAR_FWD: return 2 * rank_buffer_bytes(M, r) + fwd_partial_bytes(M, N, K, r);
+        case NF4_OP_LINEAR_BWD: return 2 * rank_buffer_bytes(M, r) + bwd_partial_bytes(M, N, K, r);
         default: return 0;
     }
 }
@@ -222,14 +237,14 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     if (!X || !Y) return fail(NF4_ERR_ARG, "X or Y is NULL");
     if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(T_out, 16))
         return fail(NF4_ERR_ARG, "X, Y and T_out must be 16-byte aligned");
-    // workspace: [s*T bf16 M x r][T bf16 M x r when T_out is NULL]
     const size_t rb = rank_buffer_bytes(M, r);
-    const size_t need = T_out ? rb : 2 * rb;
+    const size_t need = 2 * rb + fwd_partial_bytes(M, v.rows, v.cols, r);
     if (!workspace || workspace_bytes < need)
         return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LINEAR_FWD)");
     if (!aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
     uint16_t* Ts = (uint16_t*)workspace;
     uint16_t* Tb = T_out ? (uint16_t*)T_out : (uint16_t*)((char*)workspace + rb);
+    float* part = (float*)((char*)workspace + 2 * rb);
     const float s = alpha / (float)r;
     hipStream_t hs = (hipStream_t)stream;
     const uint16_t* x = (const uint16_t*)X;
@@ -240,8 +255,9 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
         e = nf4::launch_fused_gemv(v, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, table(), hs);
         return hip_status(e, "qlora_linear_fwd (gemv)");
     }
-    e = nf4::launch_lora_gemm(x, false, (const uint16_t*)A, false, M, r, v.cols, 1.0f, Tb, false, Ts,
-                              s, hs);
+    // T = X A^T (kept for the backward) and s*T for the epilogue of the fused product
+    e = nf4::launch_lora_gemm(x, false, (const uint16_t*)A, false, M, r, v.cols, part, 1.0f, Tb,
+                              false, false, Ts, s, hs);
     if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
     e = nf4::launch_fused_fwd(v, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, table(), hs);
     return hip_status(e, "qlora_linear_fwd (gemm)");
@@ -263,10 +279,10 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(T, 16) || !aligned(dX, 16))
         return fail(NF4_ERR_ARG, "X, dY, T and dX must be 16-byte aligned");
     const size_t rb = rank_buffer_bytes(M, r);
-    const size_t need = T ? rb : 2 * rb;
-    if (M > 0 && (!workspace || workspace_bytes < need))
+    const size_t need = 2 * rb + bwd_partial_bytes(M, v.rows, v.cols, r);
+    if (!workspace || workspace_bytes < need)
         return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LINEAR_BWD)");
-    if (M > 0 && !aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
+    if (!aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
     const float s = alpha / (float)r;
     hipStream_t hs = (hipStream_t)stream;
     const uint16_t* x = (const uint16_t*)X;
@@ -275,15 +291,17 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     const uint16_t* bl = (const uint16_t*)B;
     uint16_t* Us = (uint16_t*)workspace;       // s * dY B
     const uint16_t* Tb = (const uint16_t*)T;
+    float* part = (float*)((char*)workspace + 2 * rb);
     hipError_t e;
     if (M > 0) {
         // Us = s dY B   (B stored N x r: contraction-strided)
-        e = nf4::launch_lora_gemm(g, false, bl, true, M, r, v.rows, s, Us, false, nullptr, 0.0f, hs);
+        e = nf4::launch_lora_gemm(g, false, bl, true, M, r, v.rows, part, s, Us, false, false,
+                                  nullptr, 0.0f, hs);
         if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (U)");
         if (!Tb) {
             uint16_t* Tw = (uint16_t*)((char*)workspace + rb);
-            e = nf4::launch_lora_gemm(x, false, al, false, M, r, v.cols, 1.0f, Tw, false, nullptr,
-                                      0.0f, hs);
+            e = nf4::launch_lora_gemm(x, false, al, false, M, r, v.cols, part, 1.0f, Tw, false, false,
+                                      nullptr, 0.0f, hs);
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (T)");
             Tb = Tw;
         }
@@ -292,10 +310,13 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dX)");
         }
     }
-    // dA = (s U)^T X  (r x K), dB = s dY^T T  (N x r); contraction over the M tokens
-    e = nf4::launch_lora_gemm(Us, true, x, true, r, v.cols, M, 1.0f, dA, true, nullptr, 0.0f, hs);
+    // dA^T = X^T (s U)  (K x r, stored transposed as dA r x K); dB = s dY^T T (N x r);
+    // both contract over the M tokens (stored token-major: contraction-strided)
+    e = nf4::launch_lora_gemm(x, true, Us, true, v.cols, r, M, part, 1.0f, dA, true, true, nullptr,
+                              0.0f, hs);
     if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dA)");
-    e = nf4::launch_lora_gemm(g, true, Tb, true, v.rows, r, M, s, dB, true, nullptr, 0.0f, hs);
+    e = nf4::launch_lora_gemm(g, true, Tb, true, v.rows, r, M, part, s, dB, true, false, nullptr,
+                              0.0f, hs);
     return hip_status(e, "qlora_linear_bwd (dB)");
 }
 

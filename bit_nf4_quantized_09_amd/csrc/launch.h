@@ -31,13 +31,16 @@ hipError_t launch_dequantize(const WeightView& W, void* out, bool out_bf16, cons
                              hipStream_t s);
 
 // ---- LoRA side products (bf16 operands, fp32 accumulation) ----------------
-// C[i][j] = scale * sum_p Aop[i][p] * Bop[p][j], output bf16 or fp32, ldc = Nc;
-// if C2 != NULL it also receives bf16(scale2 * sum) (same layout).
+// C[i][j] = scale * sum_p Aop[i][p] * Bop[p][j] over p < P, i < Mc, j < Nc.
 // a_trans == false: Aop is row-major [Mc x P] (lda = P);  true: stored [P x Mc] (lda = Mc).
 // b_trans == false: Bop^T is row-major [Nc x P] (ldb = P); true: Bop stored [P x Nc] (ldb = Nc).
+// C is bf16 or fp32, stored [Mc x Nc] or (c_trans) [Nc x Mc]; C2, if given, receives
+// bf16(scale2 * sum) in the same layout.  `part` is fp32 workspace of
+// skinny_partial_bytes(Mc, Nc, P) bytes for the split-contraction slices.
+size_t skinny_partial_bytes(int64_t Mc, int64_t Nc, int64_t P);
 hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, bool b_trans,
-                            int64_t Mc, int64_t Nc, int64_t P, float scale, void* C, bool c_f32,
-                            uint16_t* C2, float scale2, hipStream_t s);
+                            int64_t Mc, int64_t Nc, int64_t P, float* part, float scale, void* C,
+                            bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s);
 // T = X A^T for few tokens (M <= 16): X [M x K], A [r x K] -> T bf16 [M x r] and
 // Ts = bf16(s * X A^T).
 hipError_t launch_lora_t_small(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int r,

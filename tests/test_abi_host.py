@@ -75,6 +75,12 @@ def test_workspace_sizes():
     bwd = nf4.nf4_workspace_bytes(nf4.NF4_OP_LINEAR_BWD, 4096, 8192, 8192, 64)
     assert fwd >= 2 * 4096 * 64 * 2 and bwd >= 2 * 4096 * 64 * 2
     assert nf4.nf4_workspace_bytes(99, 1, 1, 1, 1) == 0
+    # empty token batch: the backward still writes dA = dB = 0 through the slice buffer
+    assert nf4.nf4_workspace_bytes(nf4.NF4_OP_LINEAR_FWD, 0, 256, 256, 8) >= 0
+    assert nf4.nf4_workspace_bytes(nf4.NF4_OP_LINEAR_BWD, 0, 256, 256, 8) >= 256 * 8 * 4
+    for M in (1, 16, 17, 300, 4096):
+        for N, K in ((256, 256), (8192, 22016), (22016, 8192)):
+            assert nf4.nf4_workspace_bytes(nf4.NF4_OP_LINEAR_BWD, M, N, K, 64) >= 2 * M * 64 * 2
 
 
 # --- argument validation: every case below fails before any HIP call -------------
