@@ -22,84 +22,148 @@
 
 namespace nf4 {
 
-constexpr int FT = 256;                 // output tile edge (M and N/K directions)
-constexpr int FSTAGE = 65536;           // bytes per pipeline stage: 2 tiles of 256 x 64 bf16
-constexpr int FLDS = 2 * FSTAGE;        // 128 KB of the 160 KB LDS
+constexpr int FT = 256;                 // output tile edge (tokens x features)
+constexpr int FA_BYTES = 32768;         // A tile: 256 tokens x 64 contraction values (bf16)
+constexpr int FW_BYTES = 32768;         // W' tile: 256 x 64 (forward) or 64 x 256 (backward)
+constexpr int FSTAGE = FA_BYTES + FW_BYTES;
+constexpr int FLDS = 2 * FSTAGE;        // two pipeline stages: 128 KB of the 160 KB LDS
 
-// Row-major [row][64 bf16] tile, 16-byte chunk c of row r stored at c ^ (r & 7).
+// [rows][64 bf16] tile with 128-byte rows: 16-byte chunk c of row r sits at chunk
+// position c ^ g(r), g(r) = (r ^ (r >> 3)) & 7.  Any 16 consecutive rows reading the
+// same chunk (one b128 pass of 16 lanes) then cover all 64 banks exactly once, and so
+// do 8 consecutive rows (32-bank view).
 __device__ __forceinline__ int tile_off(int row, int chunk) {
-    return row * 128 + ((chunk ^ (row & 7)) << 4);
+    return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
 }
 
-// Transposed tile for the backward W' operand: element (k, n) of a
-// [256 k][64 n] tile; chunk n/8 of row k is stored at (n/8) ^ swz(k).
-__device__ __forceinline__ int tt_swz(int k) { return (k & 7) ^ ((k >> 6) & 3); }
-__device__ __forceinline__ int ttile_off(int k, int n) {
-    return k * 128 + ((((n >> 3) ^ tt_swz(k)) & 7) << 4) + ((n & 7) << 1);
+// Backward W' tile [64 n][256 k] with 512-byte rows, read by ds_read_b64_tr_b16:
+// 32-byte segment u (16 k values) of row r sits at u ^ 2(r & 3), so the 4 rows x 2
+// segments that 32 lanes read in one pass land on distinct banks.
+__device__ __forceinline__ int wt_off(int row, int k) {
+    return row * 512 + (((k >> 4) ^ ((row & 3) << 1)) << 5) + ((k & 15) << 1);
 }
 
-// ---------------------------------------------------------------------------
-// Forward
-// ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i & 3) of the 4-element vectors addressed by lanes
+// 4e + (i >> 2), e = 0..3.  With lane j addressing row (j >> 2), columns 4(j & 3)..+3
+// of a 4 x 16 block, lane i receives column i of rows 0..3.
+__device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(const __attribute__((address_space(3))) uint8_t*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+struct FusedArgs {
+    const uint8_t* codes;
+    const uint8_t* qc;
+    const float* c2;
+    const float* mean;
+    int64_t N, K;             // frozen weight rows (out features) and columns (in features)
+    const uint16_t* A;        // X [M x K] (forward) or dY [M x N] (backward)
+    int64_t M;
+    const uint16_t* Rk;       // forward: s*T [M x r]; backward: s*U [M x r]
+    const uint16_t* Lr;       // forward: B [N x r];   backward: A [r x K]
+    int r;
+    uint16_t* out;            // forward: Y [M x N];   backward: dX [M x K]
+};
+
+// Packed codes of one (row, 64-block) plus its 8-bit constant and second-level constant.
+struct BlockCodes {
+    uint4 w0, w1;
+    uint32_t q;
+    float c2;
+};
+
+template <bool BWD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_fused_fwd(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ qc,
-                 const float* __restrict__ c2, const float* __restrict__ mean_p, int64_t N,
-                 int64_t K, const uint16_t* __restrict__ X, int64_t M,
-                 const uint16_t* __restrict__ Ts, const uint16_t* __restrict__ Bl, int r,
-                 uint16_t* __restrict__ Y, Nf4Table tab) {
+void k_fused(FusedArgs a, Nf4Table tab) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t n0 = (int64_t)blockIdx.x * FT, m0 = (int64_t)blockIdx.y * FT;
-    const int64_t KB = K >> 6;
-    const float mean = *mean_p;
+    // forward tiles (tokens, out features); backward tiles (tokens, in features)
+    const int64_t c0 = (int64_t)blockIdx.x * FT, m0 = (int64_t)blockIdx.y * FT;
+    const int64_t KB = a.K >> 6;
+    const int64_t ldA = BWD ? a.N : a.K;                 // row length of the A operand
+    const int64_t steps = BWD ? (a.N + 63) >> 6 : KB;   // 64-deep contraction steps
+    const float mean = *a.mean;
 
-    // this lane dequantizes row n0 + tid of W
-    const int64_t wrow = n0 + tid;
-    const bool wvalid = wrow < N;
-    const uint8_t* wcode = codes + wrow * (K >> 1);
-    const int64_t cidx0 = wrow * KB;
-
-    uint4 xr[8];
-    uint4 wc0 = make_uint4(0, 0, 0, 0), wc1 = make_uint4(0, 0, 0, 0);
-    uint32_t qb = 0;
-    float c2v = 0.0f;
-
-    auto load_step = [&](int64_t kb) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int qi = tid + 256 * i;
-            const int row = qi >> 3, c = qi & 7;
-            const int64_t gm = m0 + row;
-            xr[i] = (gm < M) ? *reinterpret_cast<const uint4*>(X + gm * K + kb * 64 + c * 8)
-                             : make_uint4(0, 0, 0, 0);
+    // ---- this lane's share of the packed weight: one (row, 64-block) per step ----
+    // forward: row c0 + tid, block = step; backward: row 64*step + tid/4, block c0/64 + tid%4
+    const int nl = tid >> 2, jb = tid & 3;
+    const int64_t kblk_b = (c0 >> 6) + jb < KB ? (c0 >> 6) + jb : KB - 1;
+    const int64_t wrow_f = c0 + tid < a.N ? c0 + tid : a.N - 1;
+    auto load_codes = [&](int64_t step) {
+        int64_t n, blk;
+        if constexpr (BWD) {
+            n = step * 64 + nl;
+            n = n < a.N ? n : a.N - 1;
+            blk = kblk_b;
+        } else {
+            n = wrow_f;
+            blk = step;
         }
-        if (wvalid) {
-            wc0 = *reinterpret_cast<const uint4*>(wcode + kb * 32);
-            wc1 = *reinterpret_cast<const uint4*>(wcode + kb * 32 + 16);
-            qb = qc[cidx0 + kb];
-            c2v = c2[(cidx0 + kb) >> 8];
-        }
+        const uint8_t* p = a.codes + n * (a.K >> 1) + blk * 32;
+        BlockCodes bc;
+        bc.w0 = *reinterpret_cast<const uint4*>(p);
+        bc.w1 = *reinterpret_cast<const uint4*>(p + 16);
+        bc.q = a.qc[n * KB + blk];
+        bc.c2 = a.c2[(n * KB + blk) >> 8];
+        return bc;
     };
-    auto store_step = [&](int stage) {
-        uint8_t* sX = lds + stage * FSTAGE;
-        uint8_t* sW = sX + 32768;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int qi = tid + 256 * i;
-            const int row = qi >> 3, c = qi & 7;
-            *reinterpret_cast<uint4*>(sX + tile_off(row, c)) = xr[i];
-        }
-        const float c1p = wvalid ? decode_c1(qb, c2_step(c2v), mean) : 0.0f;
+    auto dequant_store = [&](uint8_t* sW, const BlockCodes& bc) {
+        const float c1p = decode_c1(bc.q, c2_step(bc.c2), mean);
         const ScaledTable st = make_scaled_table(tab, c1p);
-        const uint32_t words[8] = {wc0.x, wc0.y, wc0.z, wc0.w, wc1.x, wc1.y, wc1.z, wc1.w};
+        const uint32_t words[8] = {bc.w0.x, bc.w0.y, bc.w0.z, bc.w0.w, bc.w1.x, bc.w1.y, bc.w1.z, bc.w1.w};
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             uint32_t o[4];
             decode8(st, words[c], o);
-            *reinterpret_cast<uint4*>(sW + tile_off(tid, c)) = make_uint4(o[0], o[1], o[2], o[3]);
+            const uint4 v = make_uint4(o[0], o[1], o[2], o[3]);
+            if constexpr (BWD) *reinterpret_cast<uint4*>(sW + wt_off(nl, jb * 64 + c * 8)) = v;
+            else *reinterpret_cast<uint4*>(sW + tile_off(tid, c)) = v;
         }
     };
+
+    // ---- A operand tile: 256 tokens x 64 contraction values, 8 chunks per lane ----
+    // chunk i of this lane: tile row (tid + 256 i) / 8, contraction chunk (tid & 7)
+    const int achunk = tid & 7;
+    int64_t arow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t gm = m0 + ((tid + 256 * i) >> 3);
+        arow[i] = (gm < a.M ? gm : a.M - 1) * ldA;       // rows past M only feed discarded outputs
+    }
+    // eight named registers (not an array: keeps them out of scratch)
+    uint4 x0, x1, x2, x3, x4, x5, x6, x7;
+#define FUSED_LOAD_ONE(xi, i_, gp_)                                                          \
+    do {                                                                                     \
+        if constexpr (BWD) {                                                                 \
+            const uint4 v_ = *reinterpret_cast<const uint4*>(a.A + arow[i_] + ((gp_) < a.N ? (gp_) : 0)); \
+            xi = (gp_) < a.N ? v_ : make_uint4(0, 0, 0, 0);                                  \
+        } else {                                                                             \
+            xi = *reinterpret_cast<const uint4*>(a.A + arow[i_] + (gp_));                    \
+        }                                                                                    \
+    } while (0)
+#define FUSED_LOAD_A(step)                                                                   \
+    do {                                                                                     \
+        const int64_t gp_ = (step) * 64 + achunk * 8;                                        \
+        FUSED_LOAD_ONE(x0, 0, gp_); FUSED_LOAD_ONE(x1, 1, gp_);                              \
+        FUSED_LOAD_ONE(x2, 2, gp_); FUSED_LOAD_ONE(x3, 3, gp_);                              \
+        FUSED_LOAD_ONE(x4, 4, gp_); FUSED_LOAD_ONE(x5, 5, gp_);                              \
+        FUSED_LOAD_ONE(x6, 6, gp_); FUSED_LOAD_ONE(x7, 7, gp_);                              \
+    } while (0)
+#define FUSED_STORE_ONE(sA, xi, i_) \
+    *reinterpret_cast<uint4*>((sA) + tile_off((tid + 256 * (i_)) >> 3, achunk)) = xi
+#define FUSED_STORE_A(sA)                                                                    \
+    do {                                                                                     \
+        FUSED_STORE_ONE(sA, x0, 0); FUSED_STORE_ONE(sA, x1, 1);                              \
+        FUSED_STORE_ONE(sA, x2, 2); FUSED_STORE_ONE(sA, x3, 3);                              \
+        FUSED_STORE_ONE(sA, x4, 4); FUSED_STORE_ONE(sA, x5, 5);                              \
+        FUSED_STORE_ONE(sA, x6, 6); FUSED_STORE_ONE(sA, x7, 7);                              \
+    } while (0)
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -107,83 +171,189 @@ void k_fused_fwd(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+    // B fragment of MFMA column tile j, substep sub (16 contraction values)
+    auto read_b = [&](const uint8_t* sB, int j, int sub) -> bf16x8 {
+        if constexpr (BWD) {
+            const int g = lane >> 4, jl = lane & 15;
+            const int row = 16 * sub + 8 * (g >> 1) + (jl >> 2);
+            const int k = wn * 128 + j * 32 + 16 * (g & 1) + 4 * (jl & 3);
+            const uint2 lo = ds_read_tr16(sB + wt_off(row, k));
+            const uint2 hi = ds_read_tr16(sB + wt_off(row + 4, k));
+            return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+            const int rb = wn * 128 + j * 32 + (lane & 31);
+            return *reinterpret_cast<const bf16x8*>(sB + tile_off(rb, 2 * sub + (lane >> 5)));
+        }
+    };
     auto mfma_step = [&](const uint8_t* sA, const uint8_t* sB, int nsub) {
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
             if (sub < nsub) {
                 const int ch = 2 * sub + (lane >> 5);
-                bf16x8 a[4], b[4];
+                bf16x8 fa[4], fb[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ra = wm * 128 + i * 32 + (lane & 31);
-                    a[i] = *reinterpret_cast<const bf16x8*>(sA + tile_off(ra, ch));
-                }
+                for (int i = 0; i < 4; ++i)
+                    fa[i] = *reinterpret_cast<const bf16x8*>(sA + tile_off(wm * 128 + i * 32 + (lane & 31), ch));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int rb = wn * 128 + j * 32 + (lane & 31);
-                    b[j] = *reinterpret_cast<const bf16x8*>(sB + tile_off(rb, ch));
-                }
+                for (int j = 0; j < 4; ++j) fb[j] = read_b(sB, j, sub);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
             }
         }
     };
 
-    load_step(0);
-    store_step(0);
+    // ---- prologue: stage 0 <- step 0; codes of step 1 in registers ----
+    {
+        FUSED_LOAD_A(0);
+        const BlockCodes b0 = load_codes(0);
+        FUSED_STORE_A(lds);
+        dequant_store(lds + FA_BYTES, b0);
+    }
+    BlockCodes wcur = load_codes(steps > 1 ? 1 : 0);
     __syncthreads();
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        const int stage = (int)(kb & 1);
-        if (kb + 1 < KB) load_step(kb + 1);
-        mfma_step(lds + stage * FSTAGE, lds + stage * FSTAGE + 32768, 4);
-        if (kb + 1 < KB) store_step(stage ^ 1);
+
+    // ---- main loop: the MFMAs of step `it` overlap the dequantization of step it+1 ----
+    // The body is laid out by hand as 8 regions fenced by sched_barrier: region r
+    // issues MFMAs 8r..8r+7 of this step (substep r/2), one slice of the
+    // dequantization of the next step (region 0: block constant and scaled table;
+    // region r > 0: codes 8(r-1)..8r-1 and their LDS write) and half of the
+    // fragment reads of the following substep.  Inside a region, each MFMA is
+    // followed by a few VALU instructions, so the VALU work executes while the
+    // matrix core is busy.
+    for (int64_t it = 0; it < steps; ++it) {
+        const int st = (int)(it & 1);
+        const uint8_t* cur = lds + st * FSTAGE;
+        uint8_t* nxt = lds + (st ^ 1) * FSTAGE;
+        const int64_t n1 = it + 1 < steps ? it + 1 : steps - 1;
+        const int64_t n2 = it + 2 < steps ? it + 2 : steps - 1;
+        FUSED_LOAD_A(n1);
+        const BlockCodes wnxt = load_codes(n2);
+        const uint32_t words[8] = {wcur.w0.x, wcur.w0.y, wcur.w0.z, wcur.w0.w,
+                                   wcur.w1.x, wcur.w1.y, wcur.w1.z, wcur.w1.w};
+        uint8_t* sWn = nxt + FA_BYTES;
+        const uint8_t* sA = cur;
+        const uint8_t* sB = cur + FA_BYTES;
+
+        bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fa[0][i] = *reinterpret_cast<const bf16x8*>(sA + tile_off(wm * 128 + i * 32 + (lane & 31), (lane >> 5)));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[0][j] = read_b(sB, j, 0);
+        __builtin_amdgcn_sched_barrier(0);
+
+        ScaledTable tbl;
+#pragma unroll
+        for (int rg = 0; rg < 8; ++rg) {
+            const int sub = rg >> 1, half = rg & 1, fc = sub & 1;
+            // next-substep fragments: region 2s loads A, region 2s+1 loads B
+            if (sub < 3) {
+                const int ch = 2 * (sub + 1) + (lane >> 5);
+                if (half == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        fa[fc ^ 1][i] = *reinterpret_cast<const bf16x8*>(sA + tile_off(wm * 128 + i * 32 + (lane & 31), ch));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) fb[fc ^ 1][j] = read_b(sB, j, sub + 1);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int i = (half * 8 + t) >> 2, j = t & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fc][i], fb[fc][j], acc[i][j], 0, 0, 0);
+            }
+            if (rg == 0) {
+                tbl = make_scaled_table(tab, decode_c1(wcur.q, c2_step(wcur.c2), mean));
+            } else {
+                const int c = rg - 1;
+                uint32_t o[4];
+                decode8(tbl, words[c], o);
+                const uint4 v = make_uint4(o[0], o[1], o[2], o[3]);
+                if constexpr (BWD) *reinterpret_cast<uint4*>(sWn + wt_off(nl, jb * 64 + c * 8)) = v;
+                else *reinterpret_cast<uint4*>(sWn + tile_off(tid, c)) = v;
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);     // VALU
+                if (t < (BWD && half ? 8 : 4) && sub < 3)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        {
+            uint32_t o[4];
+            decode8(tbl, words[7], o);
+            const uint4 v = make_uint4(o[0], o[1], o[2], o[3]);
+            if constexpr (BWD) *reinterpret_cast<uint4*>(sWn + wt_off(nl, jb * 64 + 56)) = v;
+            else *reinterpret_cast<uint4*>(sWn + tile_off(tid, 7)) = v;
+        }
+        FUSED_STORE_A(nxt);
+        wcur = wnxt;
         __syncthreads();
     }
 
-    // LoRA: acc += (s T) B^T, rank chunks of 64 staged through stage 0 (Ts holds s * T)
-    if (r > 0) {
-        for (int rc = 0; rc < r; rc += 64) {
-            uint8_t* sT = lds;
-            uint8_t* sB = lds + 32768;
+#undef FUSED_LOAD_ONE
+#undef FUSED_LOAD_A
+#undef FUSED_STORE_ONE
+#undef FUSED_STORE_A
+
+    // ---- rank-r adapter term, staged through stage 0 in rank chunks of 64 ----
+    //   forward : acc += (s T) B^T   (A operand s*T [M x r], B operand rows of B [N x r])
+    //   backward: acc += (s U) A     (A operand s*U [M x r], B operand A [r x K], transposed read)
+    for (int rc = 0; rc < a.r; rc += 64) {
+        uint8_t* sR = lds;
+        uint8_t* sL = lds + FA_BYTES;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int qi = tid + 256 * i;
+        for (int i = 0; i < 8; ++i) {
+            const int qi = tid + 256 * i;
+            {
                 const int row = qi >> 3, c = qi & 7;
                 const int col = rc + 8 * c;
-                const int64_t gm = m0 + row, gn = n0 + row;
-                uint4 tv = make_uint4(0, 0, 0, 0), bv = make_uint4(0, 0, 0, 0);
-                if (col < r) {
-                    if (gm < M) tv = *reinterpret_cast<const uint4*>(Ts + gm * r + col);
-                    if (gn < N) bv = *reinterpret_cast<const uint4*>(Bl + gn * r + col);
-                }
-                *reinterpret_cast<uint4*>(sT + tile_off(row, c)) = tv;
-                *reinterpret_cast<uint4*>(sB + tile_off(row, c)) = bv;
+                const int64_t gm = m0 + row;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (col < a.r && gm < a.M) v = *reinterpret_cast<const uint4*>(a.Rk + gm * a.r + col);
+                *reinterpret_cast<uint4*>(sR + tile_off(row, c)) = v;
             }
-            __syncthreads();
-            const int left = r - rc;
-            mfma_step(sT, sB, left >= 64 ? 4 : (left + 15) / 16);
-            __syncthreads();
+            if constexpr (BWD) {
+                const int j = qi >> 5, c = qi & 31;          // rank row j, 8 features per chunk
+                const int64_t gk = c0 + 8 * c;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (rc + j < a.r && gk < a.K) v = *reinterpret_cast<const uint4*>(a.Lr + (int64_t)(rc + j) * a.K + gk);
+                *reinterpret_cast<uint4*>(sL + wt_off(j, 8 * c)) = v;
+            } else {
+                const int row = qi >> 3, c = qi & 7;
+                const int col = rc + 8 * c;
+                const int64_t gn = c0 + row;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (col < a.r && gn < a.N) v = *reinterpret_cast<const uint4*>(a.Lr + gn * a.r + col);
+                *reinterpret_cast<uint4*>(sL + tile_off(row, c)) = v;
+            }
         }
+        __syncthreads();
+        const int left = a.r - rc;
+        mfma_step(sR, sL, left >= 64 ? 4 : (left + 15) / 16);
+        __syncthreads();
     }
 
-    // store bf16
+    // ---- store bf16 ----
+    const int64_t ncols = BWD ? a.K : a.N;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+            const int64_t col = c0 + wn * 128 + j * 32 + (lane & 31);
 #pragma unroll
             for (int reg = 0; reg < 16; ++reg) {
                 const int64_t row = m0 + wm * 128 + i * 32 + 8 * (reg >> 2) + 4 * (lane >> 5) + (reg & 3);
-                if (row < M && col < N) Y[row * N + col] = f32_to_bf16(acc[i][j][reg]);
+                if (row < a.M && col < ncols) a.out[row * ncols + col] = f32_to_bf16(acc[i][j][reg]);
             }
         }
 }
-
-static bool g_fwd_attr = false, g_bwd_attr = false;
 
 FusedEvents& fused_events() {
     static thread_local FusedEvents ev;
@@ -206,210 +376,36 @@ static hipError_t with_events(hipStream_t st, F&& fn) {
     return hipSuccess;
 }
 
-hipError_t launch_fused_fwd(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Ts,
-                            const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
-                            hipStream_t st) {
-    if (M == 0 || W.rows == 0) return hipSuccess;
-    if (!g_fwd_attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_fused_fwd,
+template <bool BWD>
+static hipError_t launch_fused(const FusedArgs& fa, int64_t ncols, const Nf4Table& tab, hipStream_t st) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_fused<BWD>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, FLDS);
         if (e != hipSuccess) return e;
-        g_fwd_attr = true;
+        attr_set = true;
     }
-    dim3 grid((unsigned)((W.rows + FT - 1) / FT), (unsigned)((M + FT - 1) / FT));
+    dim3 grid((unsigned)((ncols + FT - 1) / FT), (unsigned)((fa.M + FT - 1) / FT));
     return with_events(st, [&] {
-        hipLaunchKernelGGL(k_fused_fwd, grid, dim3(256), FLDS, st, W.codes, W.q, W.c2, W.mean,
-                           W.rows, W.cols, X, M, Ts, Bl, r, Y, tab);
+        hipLaunchKernelGGL(k_fused<BWD>, grid, dim3(256), FLDS, st, fa, tab);
         return hipGetLastError();
     });
 }
 
-// ---------------------------------------------------------------------------
-// Backward dX: tile (256 tokens) x (256 input features), contraction over N in
-// steps of 64 output rows of W.  Lane t dequantizes row n = 64-step + t/4,
-// NF4 block (t % 4) of the tile's 4 K-blocks, and scatters the 64 bf16 values
-// into the transposed tile so that MFMA B fragments are 16-byte LDS reads.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_fused_bwd_dx(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ qc,
-                    const float* __restrict__ c2, const float* __restrict__ mean_p, int64_t N,
-                    int64_t K, const uint16_t* __restrict__ dY, int64_t M,
-                    const uint16_t* __restrict__ Us, const uint16_t* __restrict__ Al, int r,
-                    uint16_t* __restrict__ dX, Nf4Table tab) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t k0 = (int64_t)blockIdx.x * FT, m0 = (int64_t)blockIdx.y * FT;
-    const int64_t KB = K >> 6;
-    const int64_t NB = (N + 63) >> 6;
-    const float mean = *mean_p;
-
-    const int nl = tid >> 2, jb = tid & 3;          // this lane's (row in step, K-block in tile)
-    const int64_t kbi = (k0 >> 6) + jb;
-
-    uint4 gr[8];
-    uint4 wc0 = make_uint4(0, 0, 0, 0), wc1 = make_uint4(0, 0, 0, 0);
-    uint32_t qb = 0;
-    float c2v = 0.0f;
-    bool wvalid = false;
-
-    auto load_step = [&](int64_t nb) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int qi = tid + 256 * i;
-            const int row = qi >> 3, c = qi & 7;
-            const int64_t gm = m0 + row, gn = nb * 64 + 8 * c;
-            gr[i] = (gm < M && gn < N) ? *reinterpret_cast<const uint4*>(dY + gm * N + gn)
-                                       : make_uint4(0, 0, 0, 0);
-        }
-        const int64_t n = nb * 64 + nl;
-        wvalid = (n < N) && (kbi < KB);
-        if (wvalid) {
-            const uint8_t* p = codes + n * (K >> 1) + kbi * 32;
-            wc0 = *reinterpret_cast<const uint4*>(p);
-            wc1 = *reinterpret_cast<const uint4*>(p + 16);
-            qb = qc[n * KB + kbi];
-            c2v = c2[(n * KB + kbi) >> 8];
-        } else {
-            wc0 = make_uint4(0, 0, 0, 0);
-            wc1 = make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_step = [&](int stage) {
-        uint8_t* sG = lds + stage * FSTAGE;
-        uint8_t* sW = sG + 32768;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int qi = tid + 256 * i;
-            const int row = qi >> 3, c = qi & 7;
-            *reinterpret_cast<uint4*>(sG + tile_off(row, c)) = gr[i];
-        }
-        const float c1p = wvalid ? decode_c1(qb, c2_step(c2v), mean) : 0.0f;
-        const ScaledTable stb = make_scaled_table(tab, c1p);
-        const uint32_t words[8] = {wc0.x, wc0.y, wc0.z, wc0.w, wc1.x, wc1.y, wc1.z, wc1.w};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            uint32_t o[4];
-            decode8(stb, words[c], o);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int k = jb * 64 + c * 8 + e;
-                const uint16_t h = (uint16_t)(o[e >> 1] >> (16 * (e & 1)));
-                *reinterpret_cast<uint16_t*>(sW + ttile_off(k, nl)) = h;
-            }
-        }
-    };
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-    // A fragments from a row-major [256][64] tile, B fragments from the transposed tile
-    auto mfma_step = [&](const uint8_t* sA, const uint8_t* sBt, int nsub) {
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            if (sub < nsub) {
-                const int ch = 2 * sub + (lane >> 5);
-                bf16x8 a[4], b[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ra = wm * 128 + i * 32 + (lane & 31);
-                    a[i] = *reinterpret_cast<const bf16x8*>(sA + tile_off(ra, ch));
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int kk = wn * 128 + j * 32 + (lane & 31);
-                    b[j] = *reinterpret_cast<const bf16x8*>(sBt + ttile_off(kk, ch * 8));
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-            }
-        }
-    };
-
-    load_step(0);
-    store_step(0);
-    __syncthreads();
-    for (int64_t nb = 0; nb < NB; ++nb) {
-        const int stage = (int)(nb & 1);
-        if (nb + 1 < NB) load_step(nb + 1);
-        mfma_step(lds + stage * FSTAGE, lds + stage * FSTAGE + 32768, 4);
-        if (nb + 1 < NB) store_step(stage ^ 1);
-        __syncthreads();
-    }
-
-    // LoRA: acc += (s U) A, Us [M x r] row-major holds s * U, A [r x K] row-major
-    if (r > 0) {
-        for (int rc = 0; rc < r; rc += 64) {
-            uint8_t* sU = lds;
-            uint8_t* sA = lds + 32768;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int qi = tid + 256 * i;
-                // U tile: row = token, 8 chunks of 8 ranks
-                {
-                    const int row = qi >> 3, c = qi & 7;
-                    const int col = rc + 8 * c;
-                    const int64_t gm = m0 + row;
-                    uint4 v = make_uint4(0, 0, 0, 0);
-                    if (col < r && gm < M) v = *reinterpret_cast<const uint4*>(Us + gm * r + col);
-                    *reinterpret_cast<uint4*>(sU + tile_off(row, c)) = v;
-                }
-                // A tile transposed: rank j = qi / 32, 8 features per chunk
-                {
-                    const int j = qi >> 5, c = qi & 31;
-                    const int64_t gk = k0 + 8 * c;
-                    uint4 v = make_uint4(0, 0, 0, 0);
-                    if (rc + j < r && gk < K) v = *reinterpret_cast<const uint4*>(Al + (int64_t)(rc + j) * K + gk);
-                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint16_t h = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-                        *reinterpret_cast<uint16_t*>(sA + ttile_off(8 * c + e, j)) = h;
-                    }
-                }
-            }
-            __syncthreads();
-            const int left = r - rc;
-            mfma_step(sU, sA, left >= 64 ? 4 : (left + 15) / 16);
-            __syncthreads();
-        }
-    }
-
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = k0 + wn * 128 + j * 32 + (lane & 31);
-#pragma unroll
-            for (int reg = 0; reg < 16; ++reg) {
-                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (reg >> 2) + 4 * (lane >> 5) + (reg & 3);
-                if (row < M && col < K) dX[row * K + col] = f32_to_bf16(acc[i][j][reg]);
-            }
-        }
+hipError_t launch_fused_fwd(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Ts,
+                            const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
+                            hipStream_t st) {
+    if (M == 0 || W.rows == 0) return hipSuccess;
+    FusedArgs fa{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, X, M, Ts, Bl, r, Y};
+    return launch_fused<false>(fa, W.rows, tab, st);
 }
 
 hipError_t launch_fused_bwd_dx(const WeightView& W, const uint16_t* dY, int64_t M, const uint16_t* Us,
                                const uint16_t* Al, int r, uint16_t* dX, const Nf4Table& tab,
                                hipStream_t st) {
     if (M == 0 || W.cols == 0) return hipSuccess;
-    if (!g_bwd_attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_fused_bwd_dx,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, FLDS);
-        if (e != hipSuccess) return e;
-        g_bwd_attr = true;
-    }
-    dim3 grid((unsigned)((W.cols + FT - 1) / FT), (unsigned)((M + FT - 1) / FT));
-    return with_events(st, [&] {
-        hipLaunchKernelGGL(k_fused_bwd_dx, grid, dim3(256), FLDS, st, W.codes, W.q, W.c2, W.mean,
-                           W.rows, W.cols, dY, M, Us, Al, r, dX, tab);
-        return hipGetLastError();
-    });
+    FusedArgs fa{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, dY, M, Us, Al, r, dX};
+    return launch_fused<true>(fa, W.cols, tab, st);
 }
 
 // ---------------------------------------------------------------------------
