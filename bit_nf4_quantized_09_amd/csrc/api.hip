@@ -91,6 +91,8 @@ nf4_status check_weight(const nf4_weight* W, WeightView& v, bool linear) {
         if (W->cols % 64 != 0) return fail(NF4_ERR_UNSUPPORTED, "K (cols) must be a multiple of 64");
         if (W->rows % 8 != 0) return fail(NF4_ERR_UNSUPPORTED, "N (rows) must be a multiple of 8");
         if (W->rows == 0 || W->cols == 0) return fail(NF4_ERR_ARG, "empty weight");
+        // the fused kernels address the packed weight through 32-bit buffer offsets
+        if (n / 2 >= ((int64_t)1 << 31)) return fail(NF4_ERR_UNSUPPORTED, "weight larger than 2^32 values");
     }
     if (!aligned(W->codes, 16)) return fail(NF4_ERR_ARG, "codes must be 16-byte aligned");
     if (!aligned(W->c2, 4) || !aligned(W->mean, 4)) return fail(NF4_ERR_ARG, "misaligned c2/mean");

@@ -56,6 +56,22 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// Raw buffer access: a 128-bit descriptor in SGPRs, a per-lane 32-bit byte offset
+// and a wave-uniform byte offset.  Reads at or past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int64_t nrec = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
 struct FusedArgs {
     const uint8_t* codes;
     const uint8_t* qc;
@@ -70,11 +86,17 @@ struct FusedArgs {
     uint16_t* out;            // forward: Y [M x N];   backward: dX [M x K]
 };
 
+// One lane's eight 16-byte chunks of an A tile.
+struct XRegs {
+    uint4 r0, r1, r2, r3, r4, r5, r6, r7;
+};
+
 // Packed codes of one (row, 64-block) plus its 8-bit constant and second-level constant.
 struct BlockCodes {
     uint4 w0, w1;
     uint32_t q;
     float c2;
+    bool valid;
 };
 
 template <bool BWD>
@@ -91,30 +113,31 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     const float mean = *a.mean;
 
     // ---- this lane's share of the packed weight: one (row, 64-block) per step ----
-    // forward: row c0 + tid, block = step; backward: row 64*step + tid/4, block c0/64 + tid%4
+    // forward: row c0 + tid, block = step; backward: row 64*step + tid/4, block c0/64 + tid%4.
+    // Rows past N read zero codes; the backward zeroes their block constant as well.
     const int nl = tid >> 2, jb = tid & 3;
     const int64_t kblk_b = (c0 >> 6) + jb < KB ? (c0 >> 6) + jb : KB - 1;
-    const int64_t wrow_f = c0 + tid < a.N ? c0 + tid : a.N - 1;
+    const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes, a.N * (a.K >> 1));
+    const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(a.qc, a.N * KB);
+    const __amdgpu_buffer_rsrc_t rs_c2 = make_rsrc(a.c2, ((a.N * KB + 255) >> 8) * 4);
+    const int64_t my_row0 = BWD ? nl : c0 + tid;          // row at step 0
+    const uint32_t code_voff = (uint32_t)(my_row0 * (a.K >> 1) + (BWD ? kblk_b * 32 : 0));
+    const uint32_t q_voff = (uint32_t)(my_row0 * KB + (BWD ? kblk_b : 0));
     auto load_codes = [&](int64_t step) {
-        int64_t n, blk;
-        if constexpr (BWD) {
-            n = step * 64 + nl;
-            n = n < a.N ? n : a.N - 1;
-            blk = kblk_b;
-        } else {
-            n = wrow_f;
-            blk = step;
-        }
-        const uint8_t* p = a.codes + n * (a.K >> 1) + blk * 32;
+        // per-step advance: forward one block (32 bytes), backward 64 rows
+        const uint32_t cs = (uint32_t)(BWD ? step * 64 * (a.K >> 1) : step * 32);
+        const uint32_t qs = (uint32_t)(BWD ? step * 64 * KB : step);
+        const int64_t cidx = (int64_t)q_voff + qs;           // global index of the constant
         BlockCodes bc;
-        bc.w0 = *reinterpret_cast<const uint4*>(p);
-        bc.w1 = *reinterpret_cast<const uint4*>(p + 16);
-        bc.q = a.qc[n * KB + blk];
-        bc.c2 = a.c2[(n * KB + blk) >> 8];
+        bc.w0 = buf_load16(rs_codes, code_voff, cs);
+        bc.w1 = buf_load16(rs_codes, code_voff + 16, cs);
+        bc.q = buf_load1(rs_q, q_voff, qs);
+        bc.c2 = buf_loadf(rs_c2, (uint32_t)((cidx >> 8) * 4), 0);
+        bc.valid = (my_row0 + (BWD ? step * 64 : 0)) < a.N;
         return bc;
     };
     auto dequant_store = [&](uint8_t* sW, const BlockCodes& bc) {
-        const float c1p = decode_c1(bc.q, c2_step(bc.c2), mean);
+        const float c1p = bc.valid ? decode_c1(bc.q, c2_step(bc.c2), mean) : 0.0f;
         const ScaledTable st = make_scaled_table(tab, c1p);
         const uint32_t words[8] = {bc.w0.x, bc.w0.y, bc.w0.z, bc.w0.w, bc.w1.x, bc.w1.y, bc.w1.z, bc.w1.w};
 #pragma unroll
@@ -128,42 +151,37 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     };
 
     // ---- A operand tile: 256 tokens x 64 contraction values, 8 chunks per lane ----
-    // chunk i of this lane: tile row (tid + 256 i) / 8, contraction chunk (tid & 7)
+    // chunk i of this lane: tile row (tid >> 3) + 32 i, contraction chunk (tid & 7).  The
+    // buffer spans this block's rows only, so rows past M read zero.  Backward columns
+    // past N read finite data of the next row (or zero) and meet zeroed W' rows.
     const int achunk = tid & 7;
-    int64_t arow[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t gm = m0 + ((tid + 256 * i) >> 3);
-        arow[i] = (gm < a.M ? gm : a.M - 1) * ldA;       // rows past M only feed discarded outputs
-    }
-    // eight named registers (not an array: keeps them out of scratch)
-    uint4 x0, x1, x2, x3, x4, x5, x6, x7;
-#define FUSED_LOAD_ONE(xi, i_, gp_)                                                          \
-    do {                                                                                     \
-        if constexpr (BWD) {                                                                 \
-            const uint4 v_ = *reinterpret_cast<const uint4*>(a.A + arow[i_] + ((gp_) < a.N ? (gp_) : 0)); \
-            xi = (gp_) < a.N ? v_ : make_uint4(0, 0, 0, 0);                                  \
-        } else {                                                                             \
-            xi = *reinterpret_cast<const uint4*>(a.A + arow[i_] + (gp_));                    \
-        }                                                                                    \
-    } while (0)
-#define FUSED_LOAD_A(step)                                                                   \
-    do {                                                                                     \
-        const int64_t gp_ = (step) * 64 + achunk * 8;                                        \
-        FUSED_LOAD_ONE(x0, 0, gp_); FUSED_LOAD_ONE(x1, 1, gp_);                              \
-        FUSED_LOAD_ONE(x2, 2, gp_); FUSED_LOAD_ONE(x3, 3, gp_);                              \
-        FUSED_LOAD_ONE(x4, 4, gp_); FUSED_LOAD_ONE(x5, 5, gp_);                              \
-        FUSED_LOAD_ONE(x6, 6, gp_); FUSED_LOAD_ONE(x7, 7, gp_);                              \
-    } while (0)
-#define FUSED_STORE_ONE(sA, xi, i_) \
-    *reinterpret_cast<uint4*>((sA) + tile_off((tid + 256 * (i_)) >> 3, achunk)) = xi
-#define FUSED_STORE_A(sA)                                                                    \
-    do {                                                                                     \
-        FUSED_STORE_ONE(sA, x0, 0); FUSED_STORE_ONE(sA, x1, 1);                              \
-        FUSED_STORE_ONE(sA, x2, 2); FUSED_STORE_ONE(sA, x3, 3);                              \
-        FUSED_STORE_ONE(sA, x4, 4); FUSED_STORE_ONE(sA, x5, 5);                              \
-        FUSED_STORE_ONE(sA, x6, 6); FUSED_STORE_ONE(sA, x7, 7);                              \
-    } while (0)
+    const int64_t arows = a.M - m0 < FT ? a.M - m0 : FT;
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A + m0 * ldA, arows * ldA * 2);
+    const uint32_t a_voff = (uint32_t)(((tid >> 3) * ldA + achunk * 8) * 2);
+    const uint32_t a_rstride = (uint32_t)(32 * ldA * 2);    // bytes between chunk i and i+1
+
+    // Two register sets of the A tile: a set holds one step's 8 chunks from their
+    // load until their LDS write one step later (named members, not an array, so
+    // that they stay in registers).
+    XRegs xa, xb;
+    auto load_a = [&](XRegs& X, int64_t step) {
+        const uint32_t s0 = (uint32_t)(step * 128);
+        X.r0 = buf_load16(rs_a, a_voff, s0);
+        X.r1 = buf_load16(rs_a, a_voff, s0 + a_rstride);
+        X.r2 = buf_load16(rs_a, a_voff, s0 + 2 * a_rstride);
+        X.r3 = buf_load16(rs_a, a_voff, s0 + 3 * a_rstride);
+        X.r4 = buf_load16(rs_a, a_voff, s0 + 4 * a_rstride);
+        X.r5 = buf_load16(rs_a, a_voff, s0 + 5 * a_rstride);
+        X.r6 = buf_load16(rs_a, a_voff, s0 + 6 * a_rstride);
+        X.r7 = buf_load16(rs_a, a_voff, s0 + 7 * a_rstride);
+    };
+    auto store_a = [&](const XRegs& X, uint8_t* sA) {
+        auto one = [&](const uint4& xi, int i) {
+            *reinterpret_cast<uint4*>(sA + tile_off((tid + 256 * i) >> 3, achunk)) = xi;
+        };
+        one(X.r0, 0); one(X.r1, 1); one(X.r2, 2); one(X.r3, 3);
+        one(X.r4, 4); one(X.r5, 5); one(X.r6, 6); one(X.r7, 7);
+    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -205,13 +223,14 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         }
     };
 
-    // ---- prologue: stage 0 <- step 0; codes of step 1 in registers ----
+    // ---- prologue: stage 0 <- step 0; A tile and codes of step 1 in registers ----
     {
-        FUSED_LOAD_A(0);
+        load_a(xa, 0);
         const BlockCodes b0 = load_codes(0);
-        FUSED_STORE_A(lds);
+        store_a(xa, lds);
         dequant_store(lds + FA_BYTES, b0);
     }
+    load_a(xb, steps > 1 ? 1 : 0);
     BlockCodes wcur = load_codes(steps > 1 ? 1 : 0);
     __syncthreads();
 
@@ -223,13 +242,14 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     // fragment reads of the following substep.  Inside a region, each MFMA is
     // followed by a few VALU instructions, so the VALU work executes while the
     // matrix core is busy.
-    for (int64_t it = 0; it < steps; ++it) {
+    // step `it` (stage it & 1): xn receives the A tile of step it+2, xw holds that of
+    // step it+1 and is written to the other stage at the end.
+    auto step_body = [&](int64_t it, XRegs& xn, const XRegs& xw) {
         const int st = (int)(it & 1);
         const uint8_t* cur = lds + st * FSTAGE;
         uint8_t* nxt = lds + (st ^ 1) * FSTAGE;
-        const int64_t n1 = it + 1 < steps ? it + 1 : steps - 1;
         const int64_t n2 = it + 2 < steps ? it + 2 : steps - 1;
-        FUSED_LOAD_A(n1);
+        load_a(xn, n2);
         const BlockCodes wnxt = load_codes(n2);
         const uint32_t words[8] = {wcur.w0.x, wcur.w0.y, wcur.w0.z, wcur.w0.w,
                                    wcur.w1.x, wcur.w1.y, wcur.w1.z, wcur.w1.w};
@@ -267,7 +287,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fc][i], fb[fc][j], acc[i][j], 0, 0, 0);
             }
             if (rg == 0) {
-                tbl = make_scaled_table(tab, decode_c1(wcur.q, c2_step(wcur.c2), mean));
+                tbl = make_scaled_table(tab, wcur.valid ? decode_c1(wcur.q, c2_step(wcur.c2), mean) : 0.0f);
             } else {
                 const int c = rg - 1;
                 uint32_t o[4];
@@ -292,15 +312,17 @@ void k_fused(FusedArgs a, Nf4Table tab) {
             if constexpr (BWD) *reinterpret_cast<uint4*>(sWn + wt_off(nl, jb * 64 + 56)) = v;
             else *reinterpret_cast<uint4*>(sWn + tile_off(tid, 7)) = v;
         }
-        FUSED_STORE_A(nxt);
+        store_a(xw, nxt);
         wcur = wnxt;
         __syncthreads();
+    };
+    int64_t it = 0;
+    for (; it + 1 < steps; it += 2) {
+        step_body(it, xa, xb);
+        step_body(it + 1, xb, xa);
     }
+    if (it < steps) step_body(it, xa, xb);
 
-#undef FUSED_LOAD_ONE
-#undef FUSED_LOAD_A
-#undef FUSED_STORE_ONE
-#undef FUSED_STORE_A
 
     // ---- rank-r adapter term, staged through stage 0 in rank chunks of 64 ----
     //   forward : acc += (s T) B^T   (A operand s*T [M x r], B operand rows of B [N x r])

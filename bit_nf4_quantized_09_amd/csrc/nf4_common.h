@@ -31,11 +31,12 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+// Two fp32 -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo;
-    __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
@@ -126,25 +127,35 @@ __device__ __forceinline__ ScaledTable make_scaled_table(const Nf4Table& t, floa
     return s;
 }
 
-// Byte lane k of `sel` holds a code 0..15; returns the table bytes for them.
-__device__ __forceinline__ void lookup4(const ScaledTable& s, uint32_t sel, uint32_t& lo, uint32_t& hi) {
+// Byte lane k of `sel` holds a code 0..15 and byte lane k of `hi8` is 0xFF exactly
+// where that code is >= 8; returns the table's low and high bytes for the 4 codes.
+__device__ __forceinline__ void lookup4(const ScaledTable& s, uint32_t sel, uint32_t hi8, uint32_t& lo,
+                                        uint32_t& hi) {
     const uint32_t s7 = sel & 0x07070707u;
-    const uint32_t m = ((sel >> 3) & 0x01010101u) * 0xFFu;   // 0xFF where code >= 8
     const uint32_t la = __builtin_amdgcn_perm(s.lo[1], s.lo[0], s7);
     const uint32_t lb = __builtin_amdgcn_perm(s.lo[3], s.lo[2], s7);
     const uint32_t ha = __builtin_amdgcn_perm(s.hi[1], s.hi[0], s7);
     const uint32_t hb = __builtin_amdgcn_perm(s.hi[3], s.hi[2], s7);
-    lo = (lb & m) | (la & ~m);
-    hi = (hb & m) | (ha & ~m);
+    lo = (lb & hi8) | (la & ~hi8);
+    hi = (hb & hi8) | (ha & ~hi8);
 }
+
+// v_perm_b32 selector values 8..11 return 0x00 or 0xFF from the sign bit of byte 1 or
+// 3 of either source: 8 -> src1 byte 1, 9 -> src1 byte 3, 10 -> src0 byte 1,
+// 11 -> src0 byte 3.  With the bit of interest moved to those sign positions this
+// spreads one bit per byte lane into a full byte mask in a single instruction.
+constexpr uint32_t SIGN_SPREAD = 0x090B080Au;
 
 // 8 codes (nibble i = element i) -> 8 bf16 in element order (4 registers).
 __device__ __forceinline__ void decode8(const ScaledTable& s, uint32_t w, uint32_t out[4]) {
     const uint32_t ev = w & 0x0F0F0F0Fu;           // elements 0,2,4,6
     const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;    // elements 1,3,5,7
+    // bit 3 of element 2k sits at bit 8k+3 of w, of element 2k+1 at bit 8k+7
+    const uint32_t ev_hi8 = __builtin_amdgcn_perm(w << 12, w << 4, SIGN_SPREAD);
+    const uint32_t od_hi8 = __builtin_amdgcn_perm(w << 8, w, SIGN_SPREAD);
     uint32_t elo, ehi, olo, ohi;
-    lookup4(s, ev, elo, ehi);
-    lookup4(s, od, olo, ohi);
+    lookup4(s, ev, ev_hi8, elo, ehi);
+    lookup4(s, od, od_hi8, olo, ohi);
     // bf16 pairs (e0,e2),(e4,e6) and (o1,o3),(o5,o7)
     const uint32_t e01 = __builtin_amdgcn_perm(ehi, elo, 0x05010400u);
     const uint32_t e23 = __builtin_amdgcn_perm(ehi, elo, 0x07030602u);

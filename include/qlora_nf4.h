@@ -112,7 +112,7 @@ nf4_status nf4_dequantize(const nf4_weight* W, void* out, nf4_dtype out_dtype, v
 /* [PT]+[E2E]+[RW]: QLoRA linear forward.
  *   Y = X W'^T + s (X A^T) B^T,  s = alpha / r,  W' = dequant(W) rounded to bf16
  * with the dequantization fused into the matrix multiply.
- *   W       N x K weight, K a multiple of 64, N a multiple of 8
+ *   W       N x K weight, K a multiple of 64, N a multiple of 8, N*K < 2^32
  *   X       bf16 M x K;  M >= 0 (M == 0 enqueues nothing)
  *   A       bf16 r x K;  B  bf16 N x r;  1 <= r <= 128, r a multiple of 8
  *   Y       out: bf16 M x N
