@@ -116,9 +116,19 @@ nf4_status check_lora(const void* A, const void* B, int32_t r, float alpha) {
 
 size_t rank_buffer_bytes(int64_t M, int32_t r) { return align256((size_t)M * (size_t)r * 2); }
 
+// Token counts up to this use the dequantize-GEMV forward; larger ones the fused MFMA product.
+constexpr int64_t GEMV_MAX_M = 16;
+
+// Decoded first-level constants c1' (fp32, one per 64-block) that the fused MFMA products
+// read; the GEMV forward decodes them itself.
+size_t c1_buffer_bytes(int32_t op, int64_t M, int64_t N, int64_t K) {
+    const bool fused = op == NF4_OP_LINEAR_FWD ? M > GEMV_MAX_M : M > 0;
+    return fused ? align256((size_t)(N * (K / 64)) * 4) : 0;
+}
+
 // Workspace layouts (256-byte aligned pieces):
-//   forward : [s*T bf16 M x r][T bf16 M x r, when T_out is NULL][fp32 split-contraction slices]
-//   backward: [s*U bf16 M x r][T bf16 M x r, when T is NULL][fp32 split-contraction slices]
+//   forward : [s*T bf16 M x r][T bf16 M x r, when T_out is NULL][c1' fp32][fp32 split-contraction slices]
+//   backward: [s*U bf16 M x r][T bf16 M x r, when T is NULL][c1' fp32][fp32 split-contraction slices]
 size_t fwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
     (void)N;
     return nf4::skinny_partial_bytes(M, r, K);
@@ -161,12 +171,13 @@ void nf4_storage_bytes(int64_t n, int32_t blocksize, int32_t blocksize2, size_t*
 }
 
 size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r) {
-    (void)K;
-    if (M < 0 || N < 0 || r < 0) return 0;
+    if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
     switch (op) {
         case NF4_OP_DOUBLE_QUANTIZE: return nf4::double_quantize_ws_bytes(N);
-        case NF4_OP_LINEAR_FWD: return 2 * rank_buffer_bytes(M, r) + fwd_partial_bytes(M, N, K, r);
-        case NF4_OP_LINEAR_BWD: return 2 * rank_buffer_bytes(M, r) + bwd_partial_bytes(M, N, K, r);
+        case NF4_OP_LINEAR_FWD:
+            return 2 * rank_buffer_bytes(M, r) + c1_buffer_bytes(op, M, N, K) + fwd_partial_bytes(M, N, K, r);
+        case NF4_OP_LINEAR_BWD:
+            return 2 * rank_buffer_bytes(M, r) + c1_buffer_bytes(op, M, N, K) + bwd_partial_bytes(M, N, K, r);
         default: return 0;
     }
 }
@@ -240,18 +251,20 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(T_out, 16))
         return fail(NF4_ERR_ARG, "X, Y and T_out must be 16-byte aligned");
     const size_t rb = rank_buffer_bytes(M, r);
-    const size_t need = 2 * rb + fwd_partial_bytes(M, v.rows, v.cols, r);
+    const size_t cb = c1_buffer_bytes(NF4_OP_LINEAR_FWD, M, v.rows, v.cols);
+    const size_t need = 2 * rb + cb + fwd_partial_bytes(M, v.rows, v.cols, r);
     if (!workspace || workspace_bytes < need)
         return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LINEAR_FWD)");
     if (!aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
     uint16_t* Ts = (uint16_t*)workspace;
     uint16_t* Tb = T_out ? (uint16_t*)T_out : (uint16_t*)((char*)workspace + rb);
-    float* part = (float*)((char*)workspace + 2 * rb);
+    float* c1 = (float*)((char*)workspace + 2 * rb);
+    float* part = (float*)((char*)workspace + 2 * rb + cb);
     const float s = alpha / (float)r;
     hipStream_t hs = (hipStream_t)stream;
     const uint16_t* x = (const uint16_t*)X;
     hipError_t e;
-    if (M <= 16) {
+    if (M <= GEMV_MAX_M) {
         e = nf4::launch_lora_t_small(x, (const uint16_t*)A, M, v.cols, r, Tb, Ts, s, hs);
         if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
         e = nf4::launch_fused_gemv(v, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, table(), hs);
@@ -261,7 +274,9 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     e = nf4::launch_lora_gemm(x, false, (const uint16_t*)A, false, M, r, v.cols, part, 1.0f, Tb,
                               false, false, Ts, s, hs);
     if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
-    e = nf4::launch_fused_fwd(v, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, table(), hs);
+    e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (constants)");
+    e = nf4::launch_fused_fwd(v, c1, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, table(), hs);
     return hip_status(e, "qlora_linear_fwd (gemm)");
 }
 
@@ -281,7 +296,8 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(T, 16) || !aligned(dX, 16))
         return fail(NF4_ERR_ARG, "X, dY, T and dX must be 16-byte aligned");
     const size_t rb = rank_buffer_bytes(M, r);
-    const size_t need = 2 * rb + bwd_partial_bytes(M, v.rows, v.cols, r);
+    const size_t cb = c1_buffer_bytes(NF4_OP_LINEAR_BWD, M, v.rows, v.cols);
+    const size_t need = 2 * rb + cb + bwd_partial_bytes(M, v.rows, v.cols, r);
     if (!workspace || workspace_bytes < need)
         return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LINEAR_BWD)");
     if (!aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
@@ -293,7 +309,8 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     const uint16_t* bl = (const uint16_t*)B;
     uint16_t* Us = (uint16_t*)workspace;       // s * dY B
     const uint16_t* Tb = (const uint16_t*)T;
-    float* part = (float*)((char*)workspace + 2 * rb);
+    float* c1 = (float*)((char*)workspace + 2 * rb);
+    float* part = (float*)((char*)workspace + 2 * rb + cb);
     hipError_t e;
     if (M > 0) {
         // Us = s dY B   (B stored N x r: contraction-strided)
@@ -308,7 +325,9 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
             Tb = Tw;
         }
         if (dX) {
-            e = nf4::launch_fused_bwd_dx(v, g, M, Us, al, r, (uint16_t*)dX, table(), hs);
+            e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
+            if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (constants)");
+            e = nf4::launch_fused_bwd_dx(v, c1, g, M, Us, al, r, (uint16_t*)dX, table(), hs);
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dX)");
         }
     }

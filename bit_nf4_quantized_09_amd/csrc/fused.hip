@@ -57,16 +57,17 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* p) {
 }
 
 // Raw buffer access: a 128-bit descriptor in SGPRs, a per-lane 32-bit byte offset
-// and a wave-uniform byte offset.  Reads at or past `bytes` return zero.
+// and a wave-uniform byte offset.  The hardware range check sees the per-lane offset
+// (plus the instruction's immediate) only: a read whose per-lane offset reaches `bytes`
+// returns zero, while the wave-uniform offset is added after the check.  Every
+// wave-uniform offset below therefore stays inside the row it starts in, and offsets
+// that can leave the valid region go into the per-lane offset or the descriptor.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int64_t nrec = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
+    const int64_t nrec = bytes <= 0 ? 0 : (bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec, 0x00020000);
 }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
-}
-__device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 __device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
@@ -74,9 +75,7 @@ __device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, uint32_t vo
 
 struct FusedArgs {
     const uint8_t* codes;
-    const uint8_t* qc;
-    const float* c2;
-    const float* mean;
+    const float* c1;          // decoded first-level constant of every 64-block (N * K/64)
     int64_t N, K;             // frozen weight rows (out features) and columns (in features)
     const uint16_t* A;        // X [M x K] (forward) or dY [M x N] (backward)
     int64_t M;
@@ -91,12 +90,10 @@ struct XRegs {
     uint4 r0, r1, r2, r3, r4, r5, r6, r7;
 };
 
-// Packed codes of one (row, 64-block) plus its 8-bit constant and second-level constant.
+// Packed codes of one (row, 64-block) and its decoded constant (zero past the last row).
 struct BlockCodes {
     uint4 w0, w1;
-    uint32_t q;
-    float c2;
-    bool valid;
+    float c1;
 };
 
 template <bool BWD>
@@ -110,34 +107,40 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     const int64_t KB = a.K >> 6;
     const int64_t ldA = BWD ? a.N : a.K;                 // row length of the A operand
     const int64_t steps = BWD ? (a.N + 63) >> 6 : KB;   // 64-deep contraction steps
-    const float mean = *a.mean;
 
     // ---- this lane's share of the packed weight: one (row, 64-block) per step ----
     // forward: row c0 + tid, block = step; backward: row 64*step + tid/4, block c0/64 + tid%4.
-    // Rows past N read zero codes; the backward zeroes their block constant as well.
+    // Rows past N fall outside the buffers' range and read zero codes and a zero
+    // constant, so their dequantized values are zero.  The forward advances by a
+    // wave-uniform offset inside the row; the backward moves the descriptors down by
+    // 64 rows per step.
     const int nl = tid >> 2, jb = tid & 3;
     const int64_t kblk_b = (c0 >> 6) + jb < KB ? (c0 >> 6) + jb : KB - 1;
-    const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes, a.N * (a.K >> 1));
-    const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(a.qc, a.N * KB);
-    const __amdgpu_buffer_rsrc_t rs_c2 = make_rsrc(a.c2, ((a.N * KB + 255) >> 8) * 4);
     const int64_t my_row0 = BWD ? nl : c0 + tid;          // row at step 0
     const uint32_t code_voff = (uint32_t)(my_row0 * (a.K >> 1) + (BWD ? kblk_b * 32 : 0));
-    const uint32_t q_voff = (uint32_t)(my_row0 * KB + (BWD ? kblk_b : 0));
+    const uint32_t c1_voff = (uint32_t)((my_row0 * KB + (BWD ? kblk_b : 0)) * 4);
+    // The constant is requested first: it is needed first (scaled table), then the
+    // codes, then the A tile (LDS write at the end of the step).
     auto load_codes = [&](int64_t step) {
-        // per-step advance: forward one block (32 bytes), backward 64 rows
-        const uint32_t cs = (uint32_t)(BWD ? step * 64 * (a.K >> 1) : step * 32);
-        const uint32_t qs = (uint32_t)(BWD ? step * 64 * KB : step);
-        const int64_t cidx = (int64_t)q_voff + qs;           // global index of the constant
         BlockCodes bc;
-        bc.w0 = buf_load16(rs_codes, code_voff, cs);
-        bc.w1 = buf_load16(rs_codes, code_voff + 16, cs);
-        bc.q = buf_load1(rs_q, q_voff, qs);
-        bc.c2 = buf_loadf(rs_c2, (uint32_t)((cidx >> 8) * 4), 0);
-        bc.valid = (my_row0 + (BWD ? step * 64 : 0)) < a.N;
+        if constexpr (BWD) {
+            const int64_t r0 = step * 64;                  // first weight row of the step
+            const __amdgpu_buffer_rsrc_t rs_c1 = make_rsrc(a.c1 + r0 * KB, (a.N - r0) * KB * 4);
+            const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes + r0 * (a.K >> 1), (a.N - r0) * (a.K >> 1));
+            bc.c1 = buf_loadf(rs_c1, c1_voff, 0);
+            bc.w0 = buf_load16(rs_codes, code_voff, 0);
+            bc.w1 = buf_load16(rs_codes, code_voff + 16, 0);
+        } else {
+            const __amdgpu_buffer_rsrc_t rs_c1 = make_rsrc(a.c1, a.N * KB * 4);
+            const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes, a.N * (a.K >> 1));
+            bc.c1 = buf_loadf(rs_c1, c1_voff, (uint32_t)(step * 4));
+            bc.w0 = buf_load16(rs_codes, code_voff, (uint32_t)(step * 32));
+            bc.w1 = buf_load16(rs_codes, code_voff + 16, (uint32_t)(step * 32));
+        }
         return bc;
     };
     auto dequant_store = [&](uint8_t* sW, const BlockCodes& bc) {
-        const float c1p = bc.valid ? decode_c1(bc.q, c2_step(bc.c2), mean) : 0.0f;
+        const float c1p = bc.c1;
         const ScaledTable st = make_scaled_table(tab, c1p);
         const uint32_t words[8] = {bc.w0.x, bc.w0.y, bc.w0.z, bc.w0.w, bc.w1.x, bc.w1.y, bc.w1.z, bc.w1.w};
 #pragma unroll
@@ -152,28 +155,33 @@ void k_fused(FusedArgs a, Nf4Table tab) {
 
     // ---- A operand tile: 256 tokens x 64 contraction values, 8 chunks per lane ----
     // chunk i of this lane: tile row (tid >> 3) + 32 i, contraction chunk (tid & 7).  The
-    // buffer spans this block's rows only, so rows past M read zero.  Backward columns
-    // past N read finite data of the next row (or zero) and meet zeroed W' rows.
+    // descriptor of a step starts at the step's first contraction value of the tile's
+    // first row and ends with the tile's last row, so rows past M, and columns of the
+    // last row past its end, read zero.  Backward columns past N of the other rows read
+    // finite data of the next row and meet zeroed W' rows.
     const int achunk = tid & 7;
     const int64_t arows = a.M - m0 < FT ? a.M - m0 : FT;
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A + m0 * ldA, arows * ldA * 2);
-    const uint32_t a_voff = (uint32_t)(((tid >> 3) * ldA + achunk * 8) * 2);
+    const uint32_t a_voff0 = (uint32_t)(((tid >> 3) * ldA + achunk * 8) * 2);
     const uint32_t a_rstride = (uint32_t)(32 * ldA * 2);    // bytes between chunk i and i+1
+    const uint32_t a_voff1 = a_voff0 + a_rstride, a_voff2 = a_voff1 + a_rstride;
+    const uint32_t a_voff3 = a_voff2 + a_rstride, a_voff4 = a_voff3 + a_rstride;
+    const uint32_t a_voff5 = a_voff4 + a_rstride, a_voff6 = a_voff5 + a_rstride;
+    const uint32_t a_voff7 = a_voff6 + a_rstride;
 
     // Two register sets of the A tile: a set holds one step's 8 chunks from their
     // load until their LDS write one step later (named members, not an array, so
     // that they stay in registers).
     XRegs xa, xb;
     auto load_a = [&](XRegs& X, int64_t step) {
-        const uint32_t s0 = (uint32_t)(step * 128);
-        X.r0 = buf_load16(rs_a, a_voff, s0);
-        X.r1 = buf_load16(rs_a, a_voff, s0 + a_rstride);
-        X.r2 = buf_load16(rs_a, a_voff, s0 + 2 * a_rstride);
-        X.r3 = buf_load16(rs_a, a_voff, s0 + 3 * a_rstride);
-        X.r4 = buf_load16(rs_a, a_voff, s0 + 4 * a_rstride);
-        X.r5 = buf_load16(rs_a, a_voff, s0 + 5 * a_rstride);
-        X.r6 = buf_load16(rs_a, a_voff, s0 + 6 * a_rstride);
-        X.r7 = buf_load16(rs_a, a_voff, s0 + 7 * a_rstride);
+        const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A + m0 * ldA + step * 64, arows * ldA * 2 - step * 128);
+        X.r0 = buf_load16(rs_a, a_voff0, 0);
+        X.r1 = buf_load16(rs_a, a_voff1, 0);
+        X.r2 = buf_load16(rs_a, a_voff2, 0);
+        X.r3 = buf_load16(rs_a, a_voff3, 0);
+        X.r4 = buf_load16(rs_a, a_voff4, 0);
+        X.r5 = buf_load16(rs_a, a_voff5, 0);
+        X.r6 = buf_load16(rs_a, a_voff6, 0);
+        X.r7 = buf_load16(rs_a, a_voff7, 0);
     };
     auto store_a = [&](const XRegs& X, uint8_t* sA) {
         auto one = [&](const uint4& xi, int i) {
@@ -249,8 +257,8 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         const uint8_t* cur = lds + st * FSTAGE;
         uint8_t* nxt = lds + (st ^ 1) * FSTAGE;
         const int64_t n2 = it + 2 < steps ? it + 2 : steps - 1;
-        load_a(xn, n2);
         const BlockCodes wnxt = load_codes(n2);
+        load_a(xn, n2);
         const uint32_t words[8] = {wcur.w0.x, wcur.w0.y, wcur.w0.z, wcur.w0.w,
                                    wcur.w1.x, wcur.w1.y, wcur.w1.z, wcur.w1.w};
         uint8_t* sWn = nxt + FA_BYTES;
@@ -287,7 +295,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fc][i], fb[fc][j], acc[i][j], 0, 0, 0);
             }
             if (rg == 0) {
-                tbl = make_scaled_table(tab, wcur.valid ? decode_c1(wcur.q, c2_step(wcur.c2), mean) : 0.0f);
+                tbl = make_scaled_table(tab, wcur.c1);
             } else {
                 const int c = rg - 1;
                 uint32_t o[4];
@@ -414,19 +422,19 @@ static hipError_t launch_fused(const FusedArgs& fa, int64_t ncols, const Nf4Tabl
     });
 }
 
-hipError_t launch_fused_fwd(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Ts,
+hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* X, int64_t M, const uint16_t* Ts,
                             const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
                             hipStream_t st) {
     if (M == 0 || W.rows == 0) return hipSuccess;
-    FusedArgs fa{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, X, M, Ts, Bl, r, Y};
+    FusedArgs fa{W.codes, c1, W.rows, W.cols, X, M, Ts, Bl, r, Y};
     return launch_fused<false>(fa, W.rows, tab, st);
 }
 
-hipError_t launch_fused_bwd_dx(const WeightView& W, const uint16_t* dY, int64_t M, const uint16_t* Us,
+hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint16_t* dY, int64_t M, const uint16_t* Us,
                                const uint16_t* Al, int r, uint16_t* dX, const Nf4Table& tab,
                                hipStream_t st) {
     if (M == 0 || W.cols == 0) return hipSuccess;
-    FusedArgs fa{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, dY, M, Us, Al, r, dX};
+    FusedArgs fa{W.codes, c1, W.rows, W.cols, dY, M, Us, Al, r, dX};
     return launch_fused<true>(fa, W.cols, tab, st);
 }
 

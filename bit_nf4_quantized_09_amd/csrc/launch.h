@@ -54,8 +54,9 @@ struct FusedEvents {
 FusedEvents& fused_events();
 
 // ---- fused dequant products -------------------------------------------------
-// Y = X W'^T + Ts B^T, Ts = s T   (MFMA GEMM, dequantization fused into the W operand load)
-hipError_t launch_fused_fwd(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Ts,
+// Y = X W'^T + Ts B^T, Ts = s T   (MFMA GEMM, dequantization fused into the W operand load).
+// c1: the decoded first-level constants of W (launch_double_dequantize), one per 64-block.
+hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* X, int64_t M, const uint16_t* Ts,
                             const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
                             hipStream_t st);
 // Same product for M <= 16 tokens (HBM-bound dequant-GEMV).
@@ -63,7 +64,7 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
                              const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
                              hipStream_t st);
 // dX = dY W' + Us A, Us = s U   (contraction over N, W' used transposed)
-hipError_t launch_fused_bwd_dx(const WeightView& W, const uint16_t* dY, int64_t M, const uint16_t* Us,
+hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint16_t* dY, int64_t M, const uint16_t* Us,
                                const uint16_t* Al, int r, uint16_t* dX, const Nf4Table& tab,
                                hipStream_t st);
 

@@ -137,7 +137,13 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
                             size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace an operation needs (0 = none).  For
- * NF4_OP_DOUBLE_QUANTIZE pass n1 as N. */
+ * NF4_OP_DOUBLE_QUANTIZE pass n1 as N.  The linear products keep their
+ * intermediates there: the rank-r activations (s*T, T, s*U), the decoded
+ * first-level constants c1' of W (4 bytes per 64-block, written before the
+ * fused MFMA product; not needed by the M <= 16 forward) and fp32 partial sums
+ * of the split-contraction adapter products.  Contents are scratch: nothing
+ * survives between calls, and two calls that overlap in time on one device
+ * need separate workspaces. */
 size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r);
 
 /* [DQ] storage accounting for n values: codes ceil(n/2) bytes, q ceil(n/64)
