@@ -130,7 +130,7 @@ size_t c1_buffer_bytes(int32_t op, int64_t M, int64_t N, int64_t K) {
 //   forward : [s*T bf16 M x r][T bf16 M x r, when T_out is NULL][c1' fp32][fp32 split-contraction slices]
 //   backward: [s*U bf16 M x r][T bf16 M x r, when T is NULL][c1' fp32][fp32 split-contraction slices]
 size_t fwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
-    (void)N;
+    if (M <= GEMV_MAX_M) return align256(nf4::gemv_partial_bytes(M, N, K, r));
     return nf4::skinny_partial_bytes(M, r, K);
 }
 size_t bwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
@@ -265,9 +265,8 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     const uint16_t* x = (const uint16_t*)X;
     hipError_t e;
     if (M <= GEMV_MAX_M) {
-        e = nf4::launch_lora_t_small(x, (const uint16_t*)A, M, v.cols, r, Tb, Ts, s, hs);
-        if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
-        e = nf4::launch_fused_gemv(v, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, table(), hs);
+        e = nf4::launch_fused_gemv(v, x, M, (const uint16_t*)A, (const uint16_t*)B, r, s, (uint16_t*)Y,
+                                   Tb, part, table(), hs);
         return hip_status(e, "qlora_linear_fwd (gemv)");
     }
     // T = X A^T (kept for the backward) and s*T for the epilogue of the fused product

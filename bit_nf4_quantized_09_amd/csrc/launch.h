@@ -41,10 +41,6 @@ size_t skinny_partial_bytes(int64_t Mc, int64_t Nc, int64_t P);
 hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, bool b_trans,
                             int64_t Mc, int64_t Nc, int64_t P, float* part, float scale, void* C,
                             bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s);
-// T = X A^T for few tokens (M <= 16): X [M x K], A [r x K] -> T bf16 [M x r] and
-// Ts = bf16(s * X A^T).
-hipError_t launch_lora_t_small(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int r,
-                               uint16_t* T, uint16_t* Ts, float s, hipStream_t st);
 
 // ---- profiling hook: events around the next fused launch on this thread ----
 struct FusedEvents {
@@ -59,10 +55,13 @@ FusedEvents& fused_events();
 hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* X, int64_t M, const uint16_t* Ts,
                             const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
                             hipStream_t st);
-// Same product for M <= 16 tokens (HBM-bound dequant-GEMV).
-hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Ts,
-                             const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
-                             hipStream_t st);
+// Whole forward for M <= 16 tokens (HBM-bound dequant-GEMV): Y = X W'^T + s (X A^T) B^T and
+// T = X A^T, through fp32 partial sums per contraction slice (part: gemv_partial_bytes).
+int64_t gemv_slices(int64_t M, int64_t K);
+size_t gemv_partial_bytes(int64_t M, int64_t N, int64_t K, int r);
+hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Al,
+                             const uint16_t* Bl, int r, float s, uint16_t* Y, uint16_t* T, float* part,
+                             const Nf4Table& tab, hipStream_t st);
 // dX = dY W' + Us A, Us = s U   (contraction over N, W' used transposed)
 hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint16_t* dY, int64_t M, const uint16_t* Us,
                                const uint16_t* Al, int r, uint16_t* dX, const Nf4Table& tab,

@@ -235,60 +235,4 @@ hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, 
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// T = X A^T for M <= 16 tokens: one workgroup per adapter row j; lanes stride
-// over K in 8-element chunks, then a fixed-order reduction across the block.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_lora_t_small(const uint16_t* __restrict__ X,
-                                                      const uint16_t* __restrict__ A, int M,
-                                                      int64_t K, int r, uint16_t* __restrict__ T,
-                                                      uint16_t* __restrict__ Ts, float s) {
-    const int j = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    float acc[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) acc[m] = 0.0f;
-    const uint16_t* arow = A + (int64_t)j * K;
-    for (int64_t k = (int64_t)tid * 8; k < K; k += 256 * 8) {
-        const uint4 av = *reinterpret_cast<const uint4*>(arow + k);
-        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            if (m < M) {
-                const uint4 xv = *reinterpret_cast<const uint4*>(X + (int64_t)m * K + k);
-                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-                float s = acc[m];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    s += bf16_lo(xw[e]) * bf16_lo(aw[e]);
-                    s += bf16_hi(xw[e]) * bf16_hi(aw[e]);
-                }
-                acc[m] = s;
-            }
-        }
-    }
-    __shared__ float red[4][16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        float v = acc[m];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-        if (lane == 0) red[wave][m] = v;
-    }
-    __syncthreads();
-    if (tid < M) {
-        const float v = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
-        T[(int64_t)tid * r + j] = f32_to_bf16(v);
-        Ts[(int64_t)tid * r + j] = f32_to_bf16(v * s);
-    }
-}
-
-hipError_t launch_lora_t_small(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int r,
-                               uint16_t* T, uint16_t* Ts, float s, hipStream_t st) {
-    if (M == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_lora_t_small, dim3((unsigned)r), dim3(256), 0, st, X, A, (int)M, K, r, T,
-                       Ts, s);
-    return hipGetLastError();
-}
-
 }  // namespace nf4

@@ -66,6 +66,15 @@ def test_gemv_path(M, N, K):
     _run(W, X, A, B, dY, alpha=16.0)
 
 
+@pytest.mark.parametrize("M,N,K,r", [(3, 72, 576, 24), (1, 16, 65600, 8), (16, 48, 65600, 40),
+                                     (7, 24, 1088, 120)])
+def test_gemv_ranks_and_long_rows(M, N, K, r):
+    # adapter ranks that are not a multiple of 32, rows whose 256-blocks of second-level
+    # constants outnumber the per-workgroup cache (K > 64512), odd block counts per row
+    W, X, A, B, dY = (t.to(DEV) for t in linear_inputs(N, K, M, r, seed=seed_of(13, N, K, M, r)))
+    _run(W, X, A, B, dY, alpha=16.0)
+
+
 def test_gemv_and_gemm_paths_agree():
     # 16 tokens run through the dequant-GEMV; the same 16 plus one more run through the GEMM
     N, K, r = 520, 1024, 64
