@@ -40,8 +40,123 @@ def _args():
                    choices=["llama65b_layer", "llama7b_layer", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-paths", action="store_true", help="skip the codec and GEMV path figures")
-    p.add_argument("--cpu-tokens", type=int, default=32, help="tokens in the CPU-oracle sample")
+    p.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the CPU-oracle sample")
+    p.add_argument("--pmc-workload", action="store_true",
+                   help="one step of the workload, then a plain 512 MiB device copy (for counter runs)")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn two rocprofv3 counter CSVs (FETCH_SIZE, WRITE_SIZE) into the traffic summary")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "COMMAND"),
+                   help="turn a rocprofv3 kernel-stats CSV into a short summary naming its command")
     return p.parse_args()
+
+
+# ---- HBM traffic of the dominant kernel, from hardware counters -------------------
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are read in two rocprofv3 --pmc runs
+# of `bench.py --pmc-workload`; each counter is scaled by the factor that makes it
+# match the known bytes of a plain device copy measured in the same run.  The
+# summary records the hash of the kernel sources it was measured on; the traffic is
+# reported only while the sources still hash to that value.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_fused_fwd_llama65b_layer_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_09_amd", "csrc", f) for f in ("fused.hip", "nf4_common.h")]
+COPY_BYTES = 512 << 20
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _read_counters(path, counter):
+    import csv
+    per = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            if row.get("Counter_Name") != counter:
+                continue
+            key = (row.get("Dispatch_Id"), row.get("Kernel_Name"))
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    return per
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    fetch = _read_counters(fetch_csv, "FETCH_SIZE")
+    write = _read_counters(write_csv, "WRITE_SIZE")
+
+    def pick(table, pred):
+        return [v for (d, k), v in sorted(table.items()) if pred(k or "")]
+
+    is_fused = lambda k: "k_fused<false>" in k or "k_fusedILb0E" in k
+    is_copy = lambda k: "copy" in k.lower()
+    fc, wc = pick(fetch, is_copy), pick(write, is_copy)
+    ff, wf = pick(fetch, is_fused), pick(write, is_fused)
+    if not (fc and wc and ff and wf):
+        raise SystemExit("counter files lack the copy or the fused kernel")
+    # the copy of COPY_BYTES: largest dispatch of each kind
+    kf = (COPY_BYTES / 1024.0) / max(fc)
+    kw = (COPY_BYTES / 1024.0) / max(wc)
+    fetch_b = sum(ff) / len(ff) * 1024.0 * kf
+    write_b = sum(wf) / len(wf) * 1024.0 * kw
+    lines = [
+        "# k_fused<false> (forward fused dequant GEMM): HBM traffic per launch, LLaMA-65B layer",
+        "",
+        "Commands (GPU, from the repository root; one counter per run):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- python bench.py --pmc-workload",
+        "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- python bench.py --pmc-workload",
+        "    python bench.py --summarize-pmc <pmc_fetch>/run_counter_collection.csv <pmc_write>/run_counter_collection.csv",
+        "",
+        "Calibration: a plain device copy of %d MiB in the same run reads %.1f KiB by FETCH_SIZE and writes "
+        "%.1f KiB by WRITE_SIZE; the factors that map them to %d KiB are %.4f (fetch) and %.4f (write)."
+        % (COPY_BYTES >> 20, max(fc), max(wc), COPY_BYTES >> 10, kf, kw),
+        "",
+        "| launches | FETCH_SIZE KiB (avg) | WRITE_SIZE KiB (avg) | fetch bytes | write bytes |",
+        "|---|---|---|---|---|",
+        "| %d | %.1f | %.1f | %.4g | %.4g |" % (len(ff), sum(ff) / len(ff), sum(wf) / len(wf), fetch_b, write_b),
+        "",
+        "traffic_bytes_per_launch = %.6g" % (fetch_b + write_b),
+        "kernel_source_sha256 = %s" % kernel_source_hash(),
+    ]
+    print("\n".join(lines))
+
+
+def summarize_trace(stats_csv, command):
+    import csv
+
+    rows = list(csv.DictReader(open(stats_csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = ["# Kernel trace: rocprofv3 --kernel-trace --stats", "", "Command (GPU, repository root):", "",
+           "    " + command, "",
+           "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("|", "/")
+        if len(name) > 90:
+            name = name[:87] + "..."
+        out.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
+            name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            100.0 * float(r["TotalDurationNs"]) / total))
+    print("\n".join(out))
+
+
+def traffic_per_launch():
+    """HBM bytes per fused forward launch from the committed counter summary, or None
+    when there is none or the kernel sources changed since it was measured."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = dict(l.split(" = ", 1) for l in text.splitlines() if " = " in l and not l.startswith(" "))
+    if vals.get("kernel_source_sha256", "").strip() != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def layer_flops(M, projs, r):
@@ -181,8 +296,12 @@ def codec_paths(layer, dev, reps=3):
 
 
 def gemv_paths(layer, dev, r, alpha, reps=5):
-    """Few-token dequant-GEMV: GB/s over the layer's weights (rotating > 256 MB so the
-    Infinity Cache cannot hold them), M in {1, 4, 16}."""
+    """Few-token forward (dequant-GEMV): GB/s over the layer's weights, M in {1, 4, 16}.
+
+    The calls are queued behind a sleeping kernel and timed with one event pair
+    around the whole batch, so the figure is GPU time per call (both launches of the
+    path included) and neither host overhead nor event overhead enters it.  The
+    seven projections rotate through > 256 MB, more than the Infinity Cache holds."""
     import torch
     import bit_nf4_quantized_09_amd as nf4
     from workloads import Draw, seed_of
@@ -194,28 +313,25 @@ def gemv_paths(layer, dev, r, alpha, reps=5):
         for p in layer:
             nf4.qlora_linear_fwd(p["Wq"], xs[p["name"]], p["A"], p["B"], alpha)
         torch.cuda.synchronize()
-        evs = []
-        pool = event_pool(reps * len(layer))
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(5e7))           # holds the queue while the calls are submitted
         t0.record()
+        h0 = time.perf_counter()
         for _ in range(reps):
             for p in layer:
-                ev = next(pool)
-                nf4.nf4_profile_next_fused(*ev)
                 nf4.qlora_linear_fwd(p["Wq"], xs[p["name"]], p["A"], p["B"], alpha)
-                evs.append((ev, p))
+        h1 = time.perf_counter()
         t1.record()
         torch.cuda.synchronize()
-        call_s = t0.elapsed_time(t1) / 1e3 / len(evs)
-        kern_s = sum(a.elapsed_time(b) for (a, b), _ in evs) / 1e3 / len(evs)
-        # algorithmic bytes of the fused GEMV launch: packed weight + B + X + Ts + Y
-        kbytes = sum(NF4_BYTES_PER_PARAM * p["N"] * p["K"] + 2 * r * p["N"] + 2 * M * p["K"]
-                     + 2 * M * r + 2 * M * p["N"] for _, p in evs) / len(evs)
-        out["M%d" % M] = dict(kernel_GBps=kbytes / kern_s / 1e9,
-                              kernel_frac_hbm=kbytes / kern_s / 1e9 / PEAK_HBM_GBS,
-                              kernel_avg_us=kern_s * 1e6, call_avg_us=call_s * 1e6,
-                              launches=len(evs))
+        n = reps * len(layer)
+        gpu_s = t0.elapsed_time(t1) / 1e3 / n
+        # algorithmic bytes of one call: packed weight + A + B + X + Y (+ T)
+        nbytes = sum(NF4_BYTES_PER_PARAM * p["N"] * p["K"] + 2 * r * (p["N"] + p["K"]) + 2 * M * p["K"]
+                     + 2 * M * p["N"] + 2 * M * r for p in layer) / len(layer)
+        out["M%d" % M] = dict(GBps=nbytes / gpu_s / 1e9, frac_hbm=nbytes / gpu_s / 1e9 / PEAK_HBM_GBS,
+                              gpu_us_per_call=gpu_s * 1e6, host_us_per_call=(h1 - h0) * 1e6 / n,
+                              bytes_per_call=nbytes, calls=n)
     return out
 
 
@@ -247,8 +363,29 @@ def cpu_baseline(layer, alpha, r, tokens):
                        "float64 oracle)" % (tokens, len(layer)))
 
 
+def pmc_workload(args):
+    """One untimed step of the workload, then a plain device copy of COPY_BYTES."""
+    import torch
+
+    layer, projs, M, r, alpha = build_layer(args.workload, "cuda:0")
+    run_step(layer, alpha)
+    torch.cuda.synchronize()
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("pmc workload done", flush=True)
+
+
 def main():
     args = _args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -257,6 +394,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.pmc_workload:
+        pmc_workload(args)
+        return
     layer, projs, M, r, alpha = build_layer(args.workload, dev)
     fwd_flops, bwd_flops = layer_flops(M, projs, r)
 
@@ -288,7 +428,7 @@ def main():
                    "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "kernel": kf["kernel"], "achieved": round(kf["achieved"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(kf["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(kf["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic_per_launch(),
                      "avg_us": round(kf["avg_us"], 2), "launches": kf["launches"],
                      "bwd_dx_kernel": {"kernel": kb["kernel"], "achieved": round(kb["achieved"], 2),
                                        "frac": round(kb["achieved"] / PEAK_BF16_TFLOPS, 4),

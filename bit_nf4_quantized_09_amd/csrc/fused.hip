@@ -96,6 +96,28 @@ struct BlockCodes {
     float c1;
 };
 
+// Output tile of workgroup `wg` of `tiles_m x tiles_n` (returns m-tile, n-tile).
+//
+// Workgroups are handed to the 8 XCDs (each with its own L2) in turn: workgroup i runs
+// on XCD i % 8.  The map gives XCD x a contiguous range of the tile order, and walks
+// that order in groups of 4 token tiles, so the ~32 workgroups an XCD holds at once
+// cover a compact 4 x 8 block of output tiles and share their A tiles and W' tiles in
+// that XCD's L2 instead of fetching them again.  It is a bijection for any tile count.
+constexpr int XCDS = 8;
+constexpr int GROUP_M = 4;
+__device__ __forceinline__ void tile_of(int64_t wg, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+    const int64_t T = tiles_m * tiles_n;
+    const int64_t q = T / XCDS, rem = T % XCDS;
+    const int64_t x = wg % XCDS, local = wg / XCDS;
+    const int64_t p = x * q + (x < rem ? x : rem) + local;
+    const int64_t per_group = GROUP_M * tiles_n;
+    const int64_t first_m = (p / per_group) * GROUP_M;
+    const int64_t gm = tiles_m - first_m < GROUP_M ? tiles_m - first_m : GROUP_M;
+    const int64_t in_group = p % per_group;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
 template <bool BWD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fused(FusedArgs a, Nf4Table tab) {
@@ -103,7 +125,9 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     // forward tiles (tokens, out features); backward tiles (tokens, in features)
-    const int64_t c0 = (int64_t)blockIdx.x * FT, m0 = (int64_t)blockIdx.y * FT;
+    int64_t tm, tn;
+    tile_of(blockIdx.x, (a.M + FT - 1) / FT, ((BWD ? a.K : a.N) + FT - 1) / FT, tm, tn);
+    const int64_t c0 = tn * FT, m0 = tm * FT;
     const int64_t KB = a.K >> 6;
     const int64_t ldA = BWD ? a.N : a.K;                 // row length of the A operand
     const int64_t steps = BWD ? (a.N + 63) >> 6 : KB;   // 64-deep contraction steps
@@ -246,8 +270,9 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     // The body is laid out by hand as 8 regions fenced by sched_barrier: region r
     // issues MFMAs 8r..8r+7 of this step (substep r/2), one slice of the
     // dequantization of the next step (region 0: block constant and scaled table;
-    // region r > 0: codes 8(r-1)..8r-1 and their LDS write) and half of the
-    // fragment reads of the following substep.  Inside a region, each MFMA is
+    // region r > 0: codes 8(r-1)..8r-1 and their LDS write), half of the
+    // fragment reads of the following substep and one chunk of the A tile of step
+    // it+2 (8 chunks per lane per step).  Inside a region, each MFMA is
     // followed by a few VALU instructions, so the VALU work executes while the
     // matrix core is busy.
     // step `it` (stage it & 1): xn receives the A tile of step it+2, xw holds that of
@@ -258,7 +283,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         uint8_t* nxt = lds + (st ^ 1) * FSTAGE;
         const int64_t n2 = it + 2 < steps ? it + 2 : steps - 1;
         const BlockCodes wnxt = load_codes(n2);
-        load_a(xn, n2);
+        const __amdgpu_buffer_rsrc_t rs_an = make_rsrc(a.A + m0 * ldA + n2 * 64, arows * ldA * 2 - n2 * 128);
         const uint32_t words[8] = {wcur.w0.x, wcur.w0.y, wcur.w0.z, wcur.w0.w,
                                    wcur.w1.x, wcur.w1.y, wcur.w1.z, wcur.w1.w};
         uint8_t* sWn = nxt + FA_BYTES;
@@ -294,6 +319,18 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 const int i = (half * 8 + t) >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fc][i], fb[fc][j], acc[i][j], 0, 0, 0);
             }
+            // one 16-byte chunk of the A tile of step it+2 per region: a burst of wide
+            // loads at the top of the step would stall the wave at the texture unit
+            switch (rg) {
+                case 0: xn.r0 = buf_load16(rs_an, a_voff0, 0); break;
+                case 1: xn.r1 = buf_load16(rs_an, a_voff1, 0); break;
+                case 2: xn.r2 = buf_load16(rs_an, a_voff2, 0); break;
+                case 3: xn.r3 = buf_load16(rs_an, a_voff3, 0); break;
+                case 4: xn.r4 = buf_load16(rs_an, a_voff4, 0); break;
+                case 5: xn.r5 = buf_load16(rs_an, a_voff5, 0); break;
+                case 6: xn.r6 = buf_load16(rs_an, a_voff6, 0); break;
+                default: xn.r7 = buf_load16(rs_an, a_voff7, 0); break;
+            }
             if (rg == 0) {
                 tbl = make_scaled_table(tab, wcur.c1);
             } else {
@@ -310,6 +347,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);     // VALU
                 if (t < (BWD && half ? 8 : 4) && sub < 3)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+                if (t == 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -415,7 +453,7 @@ static hipError_t launch_fused(const FusedArgs& fa, int64_t ncols, const Nf4Tabl
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    dim3 grid((unsigned)((ncols + FT - 1) / FT), (unsigned)((fa.M + FT - 1) / FT));
+    dim3 grid((unsigned)(((ncols + FT - 1) / FT) * ((fa.M + FT - 1) / FT)));
     return with_events(st, [&] {
         hipLaunchKernelGGL(k_fused<BWD>, grid, dim3(256), FLDS, st, fa, tab);
         return hipGetLastError();
