@@ -10,31 +10,43 @@
 namespace nf4 {
 
 // ---------------------------------------------------------------------------
-// Quantize.  One lane owns 16 bytes of input: 4 fp32 or 8 bf16 values.  The
-// lanes of one 64-value block (16 or 8 of them) reduce the absmax with xor
-// shuffles, then each lane encodes its values and writes its 2 or 4 code bytes.
+// Quantize.  One lane owns 8 consecutive values (32 bytes of fp32 or 16 of bf16);
+// the 8 lanes of one 64-value block reduce the absmax with xor shuffles, then each
+// lane encodes its values and writes one 32-bit word of codes.
+//
+// Division: x = fp32(w / absmax) is formed from the correctly rounded reciprocal
+// y = RN(1/absmax) (one IEEE division per lane) as q = RN(w y), r = w - absmax q
+// (exact, fma), x = RN(q + r y).  By Markstein's theorem (y within half an ulp of
+// 1/absmax, q within one ulp of the quotient) this is the IEEE quotient whenever it
+// is a normal number.  A quotient small enough to be subnormal lies far inside
+// (-t, t) for the smallest encode threshold t ~ 0.04, so its code is the zero
+// level whichever way it rounds: the codes equal those of the IEEE division.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ w, int64_t n,
                                                   uint8_t* __restrict__ codes,
                                                   float* __restrict__ absmax, Nf4Table tab) {
-    constexpr int EPL = 16 / sizeof(T);
-    constexpr int LPB = 64 / EPL;
+    constexpr int EPL = 8;                 // values per lane
+    constexpr int LPB = 64 / EPL;          // lanes per 64-value block
     const int64_t nblk = (n + 63) / 64;
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t b = g / LPB;
-    if (b >= nblk) return;               // whole 64-value groups leave together
+    if (b >= nblk) return;                 // whole 64-value groups leave together
     const int sub = (int)(g % LPB);
     const int64_t base = b * 64 + (int64_t)sub * EPL;
     const bool full = (b * 64 + 64 <= n);
 
     float v[EPL];
     if (full) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(w + base);
         if constexpr (sizeof(T) == 4) {
-            v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
-            v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
+            const uint4 r0 = *reinterpret_cast<const uint4*>(w + base);
+            const uint4 r1 = *reinterpret_cast<const uint4*>(w + base + 4);
+            v[0] = __uint_as_float(r0.x); v[1] = __uint_as_float(r0.y);
+            v[2] = __uint_as_float(r0.z); v[3] = __uint_as_float(r0.w);
+            v[4] = __uint_as_float(r1.x); v[5] = __uint_as_float(r1.y);
+            v[6] = __uint_as_float(r1.z); v[7] = __uint_as_float(r1.w);
         } else {
+            const uint4 raw = *reinterpret_cast<const uint4*>(w + base);
             const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(r4[j]); v[2 * j + 1] = bf16_hi(r4[j]); }
@@ -58,17 +70,20 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ w, int64
     for (int o = LPB / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, LPB));
     if (sub == 0) absmax[b] = m;
 
+    const float y = __fdiv_rn(1.0f, m);
     uint32_t packed = 0;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-        uint32_t code = (m == 0.0f) ? 7u : nf4_encode(__fdiv_rn(v[e], m), tab);
+        const float q = v[e] * y;
+        const float r = __fmaf_rn(-m, q, v[e]);
+        const float x = __fmaf_rn(r, y, q);
+        uint32_t code = (m == 0.0f) ? 7u : nf4_encode(x, tab);
         if (!full && base + e >= n) code = 0u;
         packed |= code << (4 * e);
     }
     uint8_t* dst = codes + base / 2;
     if (full) {
-        if constexpr (EPL == 4) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
-        else *reinterpret_cast<uint32_t*>(dst) = packed;
+        *reinterpret_cast<uint32_t*>(dst) = packed;
     } else {
         const int64_t nbytes = (n + 1) / 2;
 #pragma unroll
@@ -81,8 +96,7 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, uint8_t* codes
                            const Nf4Table& tab, hipStream_t s) {
     if (n == 0) return hipSuccess;
     const int64_t nblk = (n + 63) / 64;
-    const int lpb = w_bf16 ? 8 : 16;
-    const int64_t lanes = nblk * lpb;
+    const int64_t lanes = nblk * 8;
     const unsigned grid = (unsigned)((lanes + 255) / 256);
     if (w_bf16)
         hipLaunchKernelGGL(k_quantize<uint16_t>, dim3(grid), dim3(256), 0, s,
@@ -228,7 +242,11 @@ hipError_t launch_double_dequantize(const uint8_t* q, const float* c2, const flo
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize: one lane per 8 values (one 32-bit word of codes).
+// Dequantize.  A workgroup handles chunks of 256 x 8 groups of E values (E = 4
+// for fp32 output, 8 for bf16, so one group is 16 bytes of output) in a
+// grid-stride loop.  Store j of lane l in wave w covers group (8w + j) * 64 + l
+// of the chunk, so every store (and every code load) of a wave is one contiguous
+// run.  The decoded constants of the chunk's blocks are formed once into LDS.
 // ---------------------------------------------------------------------------
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
@@ -236,48 +254,70 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
                                                     const float* __restrict__ c2,
                                                     const float* __restrict__ mean_p, int64_t n,
                                                     void* __restrict__ out, Nf4Table tab) {
+    constexpr int E = OUT_BF16 ? 8 : 4;            // values per group (16 bytes of output)
+    constexpr int CHUNK = 256 * 8 * E;             // values per chunk
+    constexpr int CBLK = CHUNK / 64;               // NF4 blocks per chunk (128 or 256)
     __shared__ float s_lv[16];
+    __shared__ float s_c1[CBLK];
+    if (threadIdx.x < 16) {
+        float l = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-        if (threadIdx.x == j) s_lv[j] = tab.lv[j];
-    __syncthreads();
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t i0 = t * 8;
-    if (i0 >= n) return;
-    const int64_t b = i0 >> 6;
-    const float c1p = decode_c1(q[b], c2_step(c2[b >> 8]), *mean_p);
-    const bool full = (i0 + 8 <= n);
-    uint32_t word;
-    if (full) {
-        word = *reinterpret_cast<const uint32_t*>(codes + i0 / 2);
-    } else {
-        word = 0;
-        const int64_t nbytes = (n + 1) / 2;
-        for (int j = 0; j < 4; ++j)
-            if (i0 / 2 + j < nbytes) word |= (uint32_t)codes[i0 / 2 + j] << (8 * j);
+        for (int j = 0; j < 16; ++j) l = threadIdx.x == j ? tab.lv[j] : l;
+        s_lv[threadIdx.x] = l;
     }
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = s_lv[(word >> (4 * e)) & 0xFu] * c1p;
-    if (OUT_BF16) {
-        uint16_t* o = reinterpret_cast<uint16_t*>(out) + i0;
-        if (full) {
-            uint4 pk;
-            pk.x = pack_bf16x2(v[0], v[1]); pk.y = pack_bf16x2(v[2], v[3]);
-            pk.z = pack_bf16x2(v[4], v[5]); pk.w = pack_bf16x2(v[6], v[7]);
-            *reinterpret_cast<uint4*>(o) = pk;
-        } else {
-            for (int e = 0; e < 8; ++e)
-                if (i0 + e < n) o[e] = f32_to_bf16(v[e]);
+    const float mean = *mean_p;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nblk = (n + 63) / 64;
+    const int64_t nbytes = (n + 1) / 2;
+    for (int64_t c0 = (int64_t)blockIdx.x * CHUNK; c0 < n; c0 += (int64_t)gridDim.x * CHUNK) {
+        __syncthreads();                           // previous chunk's constants are consumed
+        if (threadIdx.x < CBLK) {
+            const int64_t b = c0 / 64 + threadIdx.x;
+            s_c1[threadIdx.x] = b < nblk ? decode_c1(q[b], c2_step(c2[b >> 8]), mean) : 0.0f;
         }
-    } else {
-        float* o = reinterpret_cast<float*>(out) + i0;
-        if (full) {
-            *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-            *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
-        } else {
-            for (int e = 0; e < 8; ++e)
-                if (i0 + e < n) o[e] = v[e];
+        __syncthreads();
+        uint32_t cw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i0 = c0 + ((int64_t)(8 * wave + j) * 64 + lane) * E;
+            if (i0 + E <= n) {
+                if constexpr (E == 4) cw[j] = *reinterpret_cast<const uint16_t*>(codes + i0 / 2);
+                else cw[j] = *reinterpret_cast<const uint32_t*>(codes + i0 / 2);
+            } else {
+                uint32_t x = 0;
+                for (int t = 0; t < E / 2; ++t)
+                    if (i0 / 2 + t < nbytes) x |= (uint32_t)codes[i0 / 2 + t] << (8 * t);
+                cw[j] = x;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i0 = c0 + ((int64_t)(8 * wave + j) * 64 + lane) * E;
+            if (i0 >= n) continue;
+            const float c1p = s_c1[(i0 - c0) >> 6];
+            float v[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = s_lv[(cw[j] >> (4 * e)) & 0xFu] * c1p;
+            if constexpr (OUT_BF16) {
+                uint16_t* o = reinterpret_cast<uint16_t*>(out) + i0;
+                if (i0 + E <= n) {
+                    uint4 pk;
+                    pk.x = pack_bf16x2(v[0], v[1]); pk.y = pack_bf16x2(v[2], v[3]);
+                    pk.z = pack_bf16x2(v[4], v[5]); pk.w = pack_bf16x2(v[6], v[7]);
+                    *reinterpret_cast<uint4*>(o) = pk;
+                } else {
+                    for (int e = 0; e < E; ++e)
+                        if (i0 + e < n) o[e] = f32_to_bf16(v[e]);
+                }
+            } else {
+                float* o = reinterpret_cast<float*>(out) + i0;
+                if (i0 + E <= n) {
+                    *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+                    for (int e = 0; e < E; ++e)
+                        if (i0 + e < n) o[e] = v[e];
+                }
+            }
         }
     }
 }
@@ -286,7 +326,9 @@ hipError_t launch_dequantize(const WeightView& W, void* out, bool out_bf16, cons
                              hipStream_t s) {
     const int64_t n = W.rows * W.cols;
     if (n == 0) return hipSuccess;
-    const unsigned grid = (unsigned)ceil_div(ceil_div(n, 8), 256);
+    const int64_t chunk = out_bf16 ? 256 * 8 * 8 : 256 * 8 * 4;
+    const int64_t need = ceil_div(n, chunk);
+    const unsigned grid = (unsigned)(need < 2048 ? need : 2048);
     if (out_bf16)
         hipLaunchKernelGGL(k_dequantize<true>, dim3(grid), dim3(256), 0, s, W.codes, W.q, W.c2,
                            W.mean, n, out, tab);
