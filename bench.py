@@ -142,9 +142,12 @@ def summarize_trace(stats_csv, command):
     print("\n".join(out))
 
 
-def traffic_per_launch():
+def traffic_per_launch(workload):
     """HBM bytes per fused forward launch from the committed counter summary, or None
-    when there is none or the kernel sources changed since it was measured."""
+    when there is none, it covers another workload, or the kernel sources changed
+    since it was measured."""
+    if workload != "llama65b_layer":
+        return None
     try:
         with open(TRAFFIC_SUMMARY) as fh:
             text = fh.read()
@@ -428,7 +431,7 @@ def main():
                    "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "kernel": kf["kernel"], "achieved": round(kf["achieved"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(kf["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic_per_launch(),
+                     "frac": round(kf["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic_per_launch(args.workload),
                      "avg_us": round(kf["avg_us"], 2), "launches": kf["launches"],
                      "bwd_dx_kernel": {"kernel": kb["kernel"], "achieved": round(kb["achieved"], 2),
                                        "frac": round(kb["achieved"] / PEAK_BF16_TFLOPS, 4),

@@ -10,7 +10,7 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
-    config.addinivalue_line("markers", "slow: long-running CPU check")
+    config.addinivalue_line("markers", "slow: long-running check (minutes)")
 
 
 @pytest.fixture(scope="session")
