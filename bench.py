@@ -12,8 +12,10 @@ reported under "paths".  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `roofline` covers the dominant kernel (the fused
 dequant GEMM of the forward), timed with HIP events that the library records
-around each of its launches on the launch stream; `cpu_baseline` times the
-CPU oracle on a bounded sample of the same workload.
+around each fused product on the launch stream (the kernel, plus the small
+kernel that sums the contraction pieces of split tail tiles where a launch
+has them); `cpu_baseline` times the CPU oracle on a bounded sample of the
+same workload.
 """
 import argparse
 import json
@@ -57,7 +59,8 @@ def _args():
 # summary records the hash of the kernel sources it was measured on; the traffic is
 # reported only while the sources still hash to that value.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_fused_fwd_llama65b_layer_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_09_amd", "csrc", f) for f in ("fused.hip", "nf4_common.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_09_amd", "csrc", f)
+                  for f in ("fused.hip", "nf4_common.h", "tile_map.h")]
 COPY_BYTES = 512 << 20
 
 

@@ -127,14 +127,19 @@ size_t c1_buffer_bytes(int32_t op, int64_t M, int64_t N, int64_t K) {
 }
 
 // Workspace layouts (256-byte aligned pieces):
-//   forward : [s*T bf16 M x r][T bf16 M x r, when T_out is NULL][c1' fp32][fp32 split-contraction slices]
-//   backward: [s*U bf16 M x r][T bf16 M x r, when T is NULL][c1' fp32][fp32 split-contraction slices]
+//   forward : [s*T bf16 M x r][T bf16 M x r, when T_out is NULL][c1' fp32][fp32 partials]
+//   backward: [s*U bf16 M x r][T bf16 M x r, when T is NULL][c1' fp32][fp32 partials]
+// The partials region serves, one after the other in stream order, the split-contraction
+// slices of the rank-r products and the fp32 partial tiles of the fused product's split
+// tail tiles.
 size_t fwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
     if (M <= GEMV_MAX_M) return align256(nf4::gemv_partial_bytes(M, N, K, r));
-    return nf4::skinny_partial_bytes(M, r, K);
+    const size_t a = nf4::skinny_partial_bytes(M, r, K), b = align256(nf4::fused_fwd_plan(M, N, K).bytes);
+    return a > b ? a : b;
 }
 size_t bwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
-    size_t b = nf4::skinny_partial_bytes(M, r, N);
+    size_t b = align256(nf4::fused_bwd_plan(M, N, K).bytes);
+    b = nf4::skinny_partial_bytes(M, r, N) > b ? nf4::skinny_partial_bytes(M, r, N) : b;
     const size_t c[3] = {nf4::skinny_partial_bytes(M, r, K), nf4::skinny_partial_bytes(K, r, M),
                          nf4::skinny_partial_bytes(N, r, M)};
     for (size_t x : c) b = x > b ? x : b;
@@ -275,7 +280,7 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
     e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
     if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (constants)");
-    e = nf4::launch_fused_fwd(v, c1, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, table(), hs);
+    e = nf4::launch_fused_fwd(v, c1, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, part, table(), hs);
     return hip_status(e, "qlora_linear_fwd (gemm)");
 }
 
@@ -326,7 +331,7 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
         if (dX) {
             e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (constants)");
-            e = nf4::launch_fused_bwd_dx(v, c1, g, M, Us, al, r, (uint16_t*)dX, table(), hs);
+            e = nf4::launch_fused_bwd_dx(v, c1, g, M, Us, al, r, (uint16_t*)dX, part, table(), hs);
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dX)");
         }
     }

@@ -22,7 +22,6 @@
 
 namespace nf4 {
 
-constexpr int FT = 256;                 // output tile edge (tokens x features)
 constexpr int FA_BYTES = 32768;         // A tile: 256 tokens x 64 contraction values (bf16)
 constexpr int FW_BYTES = 32768;         // W' tile: 256 x 64 (forward) or 64 x 256 (backward)
 constexpr int FSTAGE = FA_BYTES + FW_BYTES;
@@ -83,6 +82,10 @@ struct FusedArgs {
     const uint16_t* Lr;       // forward: B [N x r];   backward: A [r x K]
     int r;
     uint16_t* out;            // forward: Y [M x N];   backward: dX [M x K]
+    // split contraction of the tail tiles (S == 1: none)
+    int S;                    // pieces per tail tile
+    int64_t chunk;            // contraction steps per piece
+    float* spart;             // fp32 partial tiles, 65536 floats per (tail tile, piece)
 };
 
 // One lane's eight 16-byte chunks of an A tile.
@@ -96,28 +99,6 @@ struct BlockCodes {
     float c1;
 };
 
-// Output tile of workgroup `wg` of `tiles_m x tiles_n` (returns m-tile, n-tile).
-//
-// Workgroups are handed to the 8 XCDs (each with its own L2) in turn: workgroup i runs
-// on XCD i % 8.  The map gives XCD x a contiguous range of the tile order, and walks
-// that order in groups of 4 token tiles, so the ~32 workgroups an XCD holds at once
-// cover a compact 4 x 8 block of output tiles and share their A tiles and W' tiles in
-// that XCD's L2 instead of fetching them again.  It is a bijection for any tile count.
-constexpr int XCDS = 8;
-constexpr int GROUP_M = 4;
-__device__ __forceinline__ void tile_of(int64_t wg, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
-    const int64_t T = tiles_m * tiles_n;
-    const int64_t q = T / XCDS, rem = T % XCDS;
-    const int64_t x = wg % XCDS, local = wg / XCDS;
-    const int64_t p = x * q + (x < rem ? x : rem) + local;
-    const int64_t per_group = GROUP_M * tiles_n;
-    const int64_t first_m = (p / per_group) * GROUP_M;
-    const int64_t gm = tiles_m - first_m < GROUP_M ? tiles_m - first_m : GROUP_M;
-    const int64_t in_group = p % per_group;
-    tm = first_m + in_group % gm;
-    tn = in_group / gm;
-}
-
 template <bool BWD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fused(FusedArgs a, Nf4Table tab) {
@@ -125,12 +106,14 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     // forward tiles (tokens, out features); backward tiles (tokens, in features)
-    int64_t tm, tn;
-    tile_of(blockIdx.x, (a.M + FT - 1) / FT, ((BWD ? a.K : a.N) + FT - 1) / FT, tm, tn);
-    const int64_t c0 = tn * FT, m0 = tm * FT;
+    Unit u;
+    if (!unit_of(blockIdx.x, (a.M + FT - 1) / FT, ((BWD ? a.K : a.N) + FT - 1) / FT, a.S, u)) return;
+    const int64_t c0 = u.tn * FT, m0 = u.tm * FT;
     const int64_t KB = a.K >> 6;
     const int64_t ldA = BWD ? a.N : a.K;                 // row length of the A operand
-    const int64_t steps = BWD ? (a.N + 63) >> 6 : KB;   // 64-deep contraction steps
+    const int64_t all_steps = BWD ? (a.N + 63) >> 6 : KB;   // 64-deep contraction steps
+    int64_t sb, steps;                                    // this unit's steps sb .. sb + steps - 1
+    unit_steps(all_steps, a.chunk, u.split, sb, steps);
 
     // ---- this lane's share of the packed weight: one (row, 64-block) per step ----
     // forward: row c0 + tid, block = step; backward: row 64*step + tid/4, block c0/64 + tid%4.
@@ -145,7 +128,8 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     const uint32_t c1_voff = (uint32_t)((my_row0 * KB + (BWD ? kblk_b : 0)) * 4);
     // The constant is requested first: it is needed first (scaled table), then the
     // codes, then the A tile (LDS write at the end of the step).
-    auto load_codes = [&](int64_t step) {
+    auto load_codes = [&](int64_t lstep) {
+        const int64_t step = sb + lstep;
         BlockCodes bc;
         if constexpr (BWD) {
             const int64_t r0 = step * 64;                  // first weight row of the step
@@ -196,7 +180,8 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     // load until their LDS write one step later (named members, not an array, so
     // that they stay in registers).
     XRegs xa, xb;
-    auto load_a = [&](XRegs& X, int64_t step) {
+    auto load_a = [&](XRegs& X, int64_t lstep) {
+        const int64_t step = sb + lstep;
         const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A + m0 * ldA + step * 64, arows * ldA * 2 - step * 128);
         X.r0 = buf_load16(rs_a, a_voff0, 0);
         X.r1 = buf_load16(rs_a, a_voff1, 0);
@@ -283,7 +268,8 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         uint8_t* nxt = lds + (st ^ 1) * FSTAGE;
         const int64_t n2 = it + 2 < steps ? it + 2 : steps - 1;
         const BlockCodes wnxt = load_codes(n2);
-        const __amdgpu_buffer_rsrc_t rs_an = make_rsrc(a.A + m0 * ldA + n2 * 64, arows * ldA * 2 - n2 * 128);
+        const int64_t g2 = sb + n2;
+        const __amdgpu_buffer_rsrc_t rs_an = make_rsrc(a.A + m0 * ldA + g2 * 64, arows * ldA * 2 - g2 * 128);
         const uint32_t words[8] = {wcur.w0.x, wcur.w0.y, wcur.w0.z, wcur.w0.w,
                                    wcur.w1.x, wcur.w1.y, wcur.w1.z, wcur.w1.w};
         uint8_t* sWn = nxt + FA_BYTES;
@@ -373,7 +359,9 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     // ---- rank-r adapter term, staged through stage 0 in rank chunks of 64 ----
     //   forward : acc += (s T) B^T   (A operand s*T [M x r], B operand rows of B [N x r])
     //   backward: acc += (s U) A     (A operand s*U [M x r], B operand A [r x K], transposed read)
-    for (int rc = 0; rc < a.r; rc += 64) {
+    // (piece 0 only, for a split tile)
+    const int rr = u.split <= 0 ? a.r : 0;
+    for (int rc = 0; rc < rr; rc += 64) {
         uint8_t* sR = lds;
         uint8_t* sL = lds + FA_BYTES;
 #pragma unroll
@@ -406,6 +394,23 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         const int left = a.r - rc;
         mfma_step(sR, sL, left >= 64 ? 4 : (left + 15) / 16);
         __syncthreads();
+    }
+
+    // ---- piece of a split tile: fp32 partial tile, row-major 256 x 256, summed later ----
+    if (u.split >= 0) {
+        float* slot = a.spart + (u.tail * a.S + u.split) * (int64_t)TILE_FLOATS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+                for (int reg = 0; reg < 16; ++reg) {
+                    const int row = wm * 128 + i * 32 + 8 * (reg >> 2) + 4 * (lane >> 5) + (reg & 3);
+                    slot[row * FT + col] = acc[i][j][reg];
+                }
+            }
+        return;
     }
 
     // ---- store bf16 ----
@@ -444,8 +449,43 @@ static hipError_t with_events(hipStream_t st, F&& fn) {
     return hipSuccess;
 }
 
+// Sum of the S fp32 partial tiles of every split tail tile, in piece order, to bf16.
+// Workgroup (slot t, band b): rows 8b..8b+7 of the tile, 8 columns per lane.
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ spart, int S, int64_t M,
+                                                      int64_t ncols, int64_t tiles_m, int64_t tiles_n,
+                                                      uint16_t* __restrict__ out) {
+    const int64_t t = blockIdx.x >> 5;
+    int64_t tm, tn;
+    if (!tail_tile(t, tiles_m, tiles_n, tm, tn)) return;
+    const int row = ((blockIdx.x & 31) << 3) + (threadIdx.x >> 5);
+    const int col = (threadIdx.x & 31) << 3;
+    const float* p = spart + t * S * (int64_t)TILE_FLOATS + row * FT + col;
+    float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
+    for (int pc = 1; pc < S; ++pc) {
+        const float4 l2 = *reinterpret_cast<const float4*>(p + pc * (int64_t)TILE_FLOATS);
+        const float4 h2 = *reinterpret_cast<const float4*>(p + pc * (int64_t)TILE_FLOATS + 4);
+        lo.x += l2.x; lo.y += l2.y; lo.z += l2.z; lo.w += l2.w;
+        hi.x += h2.x; hi.y += h2.y; hi.z += h2.z; hi.w += h2.w;
+    }
+    const int64_t grow = tm * FT + row, gcol = tn * FT + col;
+    if (grow >= M || gcol >= ncols) return;
+    const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint16_t* o = out + grow * ncols + gcol;
+    if ((ncols & 7) == 0) {
+        uint4 w;
+        w.x = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        w.y = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        w.z = f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+        w.w = f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+        *reinterpret_cast<uint4*>(o) = w;
+    } else {
+        for (int e = 0; e < 8 && gcol + e < ncols; ++e) o[e] = f32_to_bf16(v[e]);
+    }
+}
+
 template <bool BWD>
-static hipError_t launch_fused(const FusedArgs& fa, int64_t ncols, const Nf4Table& tab, hipStream_t st) {
+static hipError_t launch_fused(FusedArgs fa, int64_t ncols, int64_t steps, void* split_ws,
+                               const Nf4Table& tab, hipStream_t st) {
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)k_fused<BWD>,
@@ -453,27 +493,36 @@ static hipError_t launch_fused(const FusedArgs& fa, int64_t ncols, const Nf4Tabl
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    dim3 grid((unsigned)(((ncols + FT - 1) / FT) * ((fa.M + FT - 1) / FT)));
+    const FusedPlan p = fused_plan(fa.M, ncols, steps);
+    fa.S = p.S;
+    fa.chunk = p.chunk;
+    fa.spart = (float*)split_ws;
+    if (p.S > 1 && !split_ws) return hipErrorInvalidValue;
+    // the profiling events cover the product and, for split tail tiles, their sum
     return with_events(st, [&] {
-        hipLaunchKernelGGL(k_fused<BWD>, grid, dim3(256), FLDS, st, fa, tab);
+        hipLaunchKernelGGL(k_fused<BWD>, dim3((unsigned)p.grid), dim3(256), FLDS, st, fa, tab);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || p.S == 1) return e;
+        hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)(p.tails * 32)), dim3(256), 0, st, fa.spart, p.S,
+                           fa.M, ncols, (fa.M + FT - 1) / FT, (ncols + FT - 1) / FT, fa.out);
         return hipGetLastError();
     });
 }
 
 hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* X, int64_t M, const uint16_t* Ts,
-                            const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
+                            const uint16_t* Bl, int r, uint16_t* Y, void* split_ws, const Nf4Table& tab,
                             hipStream_t st) {
     if (M == 0 || W.rows == 0) return hipSuccess;
-    FusedArgs fa{W.codes, c1, W.rows, W.cols, X, M, Ts, Bl, r, Y};
-    return launch_fused<false>(fa, W.rows, tab, st);
+    FusedArgs fa{W.codes, c1, W.rows, W.cols, X, M, Ts, Bl, r, Y, 1, 0, nullptr};
+    return launch_fused<false>(fa, W.rows, W.cols >> 6, split_ws, tab, st);
 }
 
 hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint16_t* dY, int64_t M, const uint16_t* Us,
-                               const uint16_t* Al, int r, uint16_t* dX, const Nf4Table& tab,
+                               const uint16_t* Al, int r, uint16_t* dX, void* split_ws, const Nf4Table& tab,
                                hipStream_t st) {
     if (M == 0 || W.cols == 0) return hipSuccess;
-    FusedArgs fa{W.codes, c1, W.rows, W.cols, dY, M, Us, Al, r, dX};
-    return launch_fused<true>(fa, W.cols, tab, st);
+    FusedArgs fa{W.codes, c1, W.rows, W.cols, dY, M, Us, Al, r, dX, 1, 0, nullptr};
+    return launch_fused<true>(fa, W.cols, (W.rows + 63) >> 6, split_ws, tab, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "nf4_common.h"
+#include "tile_map.h"
 
 namespace nf4 {
 
@@ -53,7 +54,7 @@ FusedEvents& fused_events();
 // Y = X W'^T + Ts B^T, Ts = s T   (MFMA GEMM, dequantization fused into the W operand load).
 // c1: the decoded first-level constants of W (launch_double_dequantize), one per 64-block.
 hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* X, int64_t M, const uint16_t* Ts,
-                            const uint16_t* Bl, int r, uint16_t* Y, const Nf4Table& tab,
+                            const uint16_t* Bl, int r, uint16_t* Y, void* split_ws, const Nf4Table& tab,
                             hipStream_t st);
 // Whole forward for M <= 16 tokens (HBM-bound dequant-GEMV): Y = X W'^T + s (X A^T) B^T and
 // T = X A^T, through fp32 partial sums per contraction slice (part: gemv_partial_bytes).
@@ -64,7 +65,7 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
                              const Nf4Table& tab, hipStream_t st);
 // dX = dY W' + Us A, Us = s U   (contraction over N, W' used transposed)
 hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint16_t* dY, int64_t M, const uint16_t* Us,
-                               const uint16_t* Al, int r, uint16_t* dX, const Nf4Table& tab,
+                               const uint16_t* Al, int r, uint16_t* dX, void* split_ws, const Nf4Table& tab,
                                hipStream_t st);
 
 }  // namespace nf4

@@ -141,7 +141,10 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
  * intermediates there: the rank-r activations (s*T, T, s*U), the decoded
  * first-level constants c1' of W (4 bytes per 64-block, written before the
  * fused MFMA product; not needed by the M <= 16 forward) and fp32 partial sums
- * of the split-contraction adapter products.  Contents are scratch: nothing
+ * of the split-contraction adapter products and of the fused product's tail
+ * tiles (when the last wave of 256 x 256 output tiles would leave most compute
+ * units idle, those tiles are computed in up to 4 contraction pieces: at most
+ * 64 MiB).  Contents are scratch: nothing
  * survives between calls, and two calls that overlap in time on one device
  * need separate workspaces. */
 size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r);

@@ -52,8 +52,11 @@ def test_tiny_layer():
     _run(W, X, A, B, dY, alpha=16.0)
 
 
+# Launches of a few tiles cut every tile into contraction pieces; (8, 64, 33, 8) has a
+# single step (no pieces) and the 136-tile forward of (2048, 128, 4352, 16) runs whole
+# tiles only, while its 17-tile dX runs pieces.
 @pytest.mark.parametrize("N,K,M,r", [(328, 320, 300, 8), (256, 512, 257, 64), (520, 192, 513, 128),
-                                     (264, 256, 40, 24), (8, 64, 33, 8)])
+                                     (264, 256, 40, 24), (8, 64, 33, 8), (2048, 128, 4352, 16)])
 def test_ragged_gemm_path(N, K, M, r):
     W, X, A, B, dY = (t.to(DEV) for t in linear_inputs(N, K, M, r, seed=seed_of(10, N, K, M, r)))
     _run(W, X, A, B, dY, alpha=16.0)
