@@ -49,7 +49,94 @@ def _args():
                    help="turn two rocprofv3 counter CSVs (FETCH_SIZE, WRITE_SIZE) into the traffic summary")
     p.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "COMMAND"),
                    help="turn a rocprofv3 kernel-stats CSV into a short summary naming its command")
+    p.add_argument("--gemv-sweep", action="store_true",
+                   help="few-token forward only: 10 queued calls for each LLaMA-65B shape and M in "
+                        "{1, 4, 16} (for a kernel trace; see --summarize-gemv-trace)")
+    p.add_argument("--summarize-gemv-trace", metavar="KERNEL_TRACE_CSV",
+                   help="per-shape kernel durations of a --gemv-sweep kernel trace, as a markdown table")
+    p.add_argument("--plain-gemm", action="store_true",
+                   help="time the vendor library's plain bf16 GEMM (torch.matmul) at the layer shapes, "
+                        "for context, and print a markdown table")
     return p.parse_args()
+
+
+GEMV_SWEEP_SHAPES = ((8192, 8192), (22016, 8192), (8192, 22016))
+GEMV_SWEEP_M = (1, 4, 16)
+GEMV_SWEEP_CALLS = 10
+
+
+def gemv_sweep():
+    """The few-token forward alone: for each shape and token count, GEMV_SWEEP_CALLS calls
+    queued behind a sleeping kernel, so that they run back to back."""
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+    from workloads import linear_inputs, seed_of
+
+    for (N, K) in GEMV_SWEEP_SHAPES:
+        W, X, A, B, _ = linear_inputs(N, K, 16, 64, seed=seed_of(3, N, K), device="cuda", with_dy=False)
+        Wq = nf4.quantize_weight(W)
+        del W
+        for M in GEMV_SWEEP_M:
+            x = X[:M].contiguous()
+            torch.cuda.synchronize()
+            torch.cuda._sleep(int(2e7))
+            for _ in range(GEMV_SWEEP_CALLS):
+                nf4.qlora_linear_fwd(Wq, x, A, B, 16.0)
+            torch.cuda.synchronize()
+            print("gemv sweep N=%d K=%d M=%d done" % (N, K, M), file=sys.stderr, flush=True)
+
+
+def summarize_gemv_trace(trace_csv):
+    import csv
+
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "k_gemv_" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out = ["| N x K | M | k_gemv_part us | k_gemv_reduce us | call us | codes+constants GB/s (part) | "
+           "algorithmic GB/s (call) |", "|---|---|---|---|---|---|---|"]
+    i = 0
+    for (N, K) in GEMV_SWEEP_SHAPES:
+        for M in GEMV_SWEEP_M:
+            grp = rows[i:i + 2 * GEMV_SWEEP_CALLS]
+            i += 2 * GEMV_SWEEP_CALLS
+            dur = lambda key: sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                                     for r in grp if key in r["Kernel_Name"])
+            part, red = dur("k_gemv_part"), dur("k_gemv_reduce")
+            pm, rm = part[len(part) // 2], red[len(red) // 2]
+            wbytes = NF4_BYTES_PER_PARAM * N * K
+            cbytes = wbytes + 2 * 64 * (N + K) + 2 * M * K + 2 * M * N + 2 * M * 64
+            out.append("| %d x %d | %d | %.2f | %.2f | %.2f | %.0f | %.0f |" % (
+                N, K, M, pm, rm, pm + rm, wbytes / pm / 1e3, cbytes / (pm + rm) / 1e3))
+    print("\n".join(out))
+
+
+def plain_gemm_table():
+    """torch.matmul (hipBLASLt) bf16 products of the forward's (NT) and the dX product's (NN)
+    layouts at the LLaMA shapes: a library GEMM with no dequantization, for context."""
+    import torch
+
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    rows = ["| M x N x K | NT (Y = X W^T, the forward's layout) | NN (the dX product's layout) |",
+            "|---|---|---|"]
+    for (M, N, K) in ((4096, 8192, 8192), (4096, 22016, 8192), (4096, 8192, 22016), (2048, 4096, 4096),
+                      (2048, 11008, 4096), (2048, 4096, 11008)):
+        X = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=gen)
+        W = torch.randn(N, K, device="cuda", dtype=torch.bfloat16, generator=gen) * 0.02
+        cells = []
+        for op in (W.t(), W.t().contiguous()):
+            for _ in range(3):
+                X @ op
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                X @ op
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 20 * 1e3
+            cells.append("%.1f us, %.0f TFLOP/s" % (us, 2.0 * M * N * K / us / 1e6))
+        rows.append("| %d x %d x %d | %s | %s |" % (M, N, K, cells[0], cells[1]))
+        print(rows[-1], file=sys.stderr, flush=True)
+        del X, W
+    print("\n".join(rows))
 
 
 # ---- HBM traffic of the dominant kernel, from hardware counters -------------------
@@ -60,7 +147,7 @@ def _args():
 # reported only while the sources still hash to that value.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_fused_fwd_llama65b_layer_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_09_amd", "csrc", f)
-                  for f in ("fused.hip", "nf4_common.h", "tile_map.h")]
+                  for f in ("fused.hip", "nf4_common.h", "tile_map.h", "bufio.h")]
 COPY_BYTES = 512 << 20
 
 
@@ -392,6 +479,9 @@ def main():
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
         return
+    if args.summarize_gemv_trace:
+        summarize_gemv_trace(args.summarize_gemv_trace)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -400,6 +490,12 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.plain_gemm:
+        plain_gemm_table()
+        return
+    if args.gemv_sweep:
+        gemv_sweep()
+        return
     if args.pmc_workload:
         pmc_workload(args)
         return

@@ -18,6 +18,7 @@
 // constant and expands its 64 codes with byte permutes before writing them to
 // LDS; every dequantized value is therefore computed once per workgroup and
 // reused by 256 rows of the other operand.
+#include "bufio.h"
 #include "launch.h"
 
 namespace nf4 {
@@ -53,23 +54,6 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* p) {
     const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_i16x4*)(const __attribute__((address_space(3))) uint8_t*)(p));
     return __builtin_bit_cast(uint2, v);
-}
-
-// Raw buffer access: a 128-bit descriptor in SGPRs, a per-lane 32-bit byte offset
-// and a wave-uniform byte offset.  The hardware range check sees the per-lane offset
-// (plus the instruction's immediate) only: a read whose per-lane offset reaches `bytes`
-// returns zero, while the wave-uniform offset is added after the check.  Every
-// wave-uniform offset below therefore stays inside the row it starts in, and offsets
-// that can leave the valid region go into the per-lane offset or the descriptor.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int64_t nrec = bytes <= 0 ? 0 : (bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
-}
-__device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
 }
 
 struct FusedArgs {
@@ -433,22 +417,6 @@ FusedEvents& fused_events() {
     return ev;
 }
 
-// Launch `fn` between the armed profiling events (if any), then disarm.
-template <typename F>
-static hipError_t with_events(hipStream_t st, F&& fn) {
-    FusedEvents& ev = fused_events();
-    const FusedEvents armed = ev;
-    ev = FusedEvents{};
-    if (armed.start) {
-        hipError_t e = hipEventRecord(armed.start, st);
-        if (e != hipSuccess) return e;
-    }
-    hipError_t e = fn();
-    if (e != hipSuccess) return e;
-    if (armed.stop) return hipEventRecord(armed.stop, st);
-    return hipSuccess;
-}
-
 // Sum of the S fp32 partial tiles of every split tail tile, in piece order, to bf16.
 // Workgroup (slot t, band b): rows 8b..8b+7 of the tile, 8 columns per lane.
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ spart, int S, int64_t M,
@@ -523,328 +491,6 @@ hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint1
     if (M == 0 || W.cols == 0) return hipSuccess;
     FusedArgs fa{W.codes, c1, W.rows, W.cols, dY, M, Us, Al, r, dX, 1, 0, nullptr};
     return launch_fused<true>(fa, W.cols, (W.rows + 63) >> 6, split_ws, tab, st);
-}
-
-// ---------------------------------------------------------------------------
-// Few-token forward (M <= 16): an HBM-bound stream over the packed weight, in two
-// launches.
-//
-// k_gemv_part<RB>: workgroup (row group, contraction slice) = 64 rows x RB NF4
-// blocks; wave w owns rows 16w..16w+15.  The slice's token inputs X[0:M, slice] are
-// staged once into LDS (rows padded by 16 bytes so that the 16 tokens of one MFMA
-// operand read hit distinct banks); then every wave requests all RB blocks of its
-// codes at once, so the whole slice is in flight and no later request waits behind
-// an earlier one (the vector-memory counter retires in order).  Per block, lane
-// (n = lane % 16, g = lane / 16) holds the 16 codes k = 16g..16g+15 of row n (8
-// bytes); two v_mfma_f32_16x16x32_bf16 on the unscaled bf16 levels, against the same
-// inputs of token n from LDS, give the block's partial dot products, which the
-// block's decoded constant c1' scales into the fp32 accumulator.  Levels come from a
-// 256-entry LDS table that maps one code byte to its two bf16 levels; c1' from an
-// E4M3 table, the row's 8-bit constants (one aligned window) and at most two
-// second-level steps per row and slice.  Row groups past the weight run the adapter
-// rows A (bf16, no scale): partial sums of T = X A^T from the same pass.  Partial
-// sums go to part[slice][token][row] (rows N.. hold T).
-//
-// k_gemv_reduce: per 64 weight rows, sums the slices in a fixed order, forms
-// T = sum of its slices, s T (bf16), and Y = sum + (s T) B^T (bf16).
-// ---------------------------------------------------------------------------
-typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-constexpr int GV_GROUP = 64;                         // rows per workgroup (16 per wave)
-
-__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
-}
-__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
-}
-
-// NF4 blocks per contraction slice: 16 for up to 4 tokens, 32 above (fewer slices,
-// less partial-sum traffic, at most 64 KB of staged inputs)
-static int gemv_rb(int64_t M) { return M <= 4 ? 16 : 32; }
-int64_t gemv_slices(int64_t M, int64_t K) { return ((K >> 6) + gemv_rb(M) - 1) / gemv_rb(M); }
-size_t gemv_partial_bytes(int64_t M, int64_t N, int64_t K, int r) {
-    return (size_t)gemv_slices(M, K) * (size_t)M * (size_t)(N + r) * 4;
-}
-
-struct GvArgs {
-    const uint8_t* codes;
-    const uint8_t* qc;
-    const float* c2;
-    const float* mean;
-    int64_t N, K;
-    const uint16_t* X;
-    int M;
-    const uint16_t* Al;      // adapter A [r x K]
-    const uint16_t* Bl;      // adapter B [N x r]
-    int r;
-    float s;
-    float* part;             // [slices][M][N + r]
-    uint16_t* Y;             // [M x N]
-    uint16_t* T;             // [M x r]
-};
-
-// One workgroup of k_gemv_part: weight rows (ADAPTER false) or adapter rows A.
-// Straight-line code from the first request to the last wait, so that every wait
-// names exactly the requests it needs.
-template <int RB, bool ADAPTER>
-__device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& tab, int64_t group) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t gv_lds[];
-    constexpr int XSTRIDE = RB * 128 + 16;             // bytes per staged token row
-    uint32_t* s_pair = reinterpret_cast<uint32_t*>(gv_lds);        // code byte -> two bf16 levels
-    float* s_e4m3 = reinterpret_cast<float*>(gv_lds + 1024);       // 8-bit constant -> E4M3 value
-    uint8_t* s_x = gv_lds + 2048;                                  // [16][XSTRIDE] token inputs
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t KB = a.K >> 6;
-    const int64_t n0 = group * GV_GROUP + 16 * wave;
-    const int64_t slice = blockIdx.x;
-    const int64_t b0 = slice * RB;                      // first block of the slice
-    const int nb = KB - b0 < RB ? (int)(KB - b0) : RB;  // blocks of the slice inside the row
-    const int nl = lane & 15, g = lane >> 4;
-    const int64_t n = n0 + nl;                          // row of this lane
-    auto bcl = [&](int j) { return (uint32_t)(b0 + j < KB ? b0 + j : KB - 1); };
-
-    // ---- requests: token inputs of the slice first, then this wave's rows ----
-    // The inputs (16 token rows x RB*8 chunks of 16 bytes; tokens past M and chunks
-    // past the row lie outside the range and read zero) pass through registers into
-    // LDS.  Being requested first, the wait for them leaves the later requests in flight.
-    const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(a.X + b0 * 64, (int64_t)a.M * a.K * 2 - b0 * 128);
-    constexpr int XCH = 16 * RB * 8 / 256;              // chunks per thread
-    uint4 xs[XCH];
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-        const int q = tid + 256 * i, m = q / (RB * 8), c = q % (RB * 8);
-        const uint32_t vo = (m < a.M && c < nb * 8) ? (uint32_t)((int64_t)m * a.K * 2 + c * 16) : 0x80000000u;
-        xs[i] = buf_load16(rs_x, vo, 0);
-    }
-    uint2 cw[RB];
-    uint32_t qw[RB / 4 + 1];
-    float mean = 0.0f, c2f = 0.0f, c2l = 0.0f;
-    int64_t g_first = 0;
-    if constexpr (!ADAPTER) {
-        mean = *a.mean;
-        // second-level constants: a row's slice meets at most two 256-blocks
-        const int64_t n2 = (a.N * KB + 255) >> 8;
-        const int64_t ci0 = n * KB + b0;
-        g_first = ci0 >> 8;
-        const int64_t gl = (ci0 + nb - 1) >> 8;
-        c2f = a.c2[g_first < n2 ? g_first : n2 - 1];
-        c2l = a.c2[gl < n2 ? gl : n2 - 1];
-        // 8-bit constants of the slice (aligned window), then the codes in block order
-        const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(a.qc, a.N * KB);
-        const uint32_t qa = (uint32_t)ci0 & ~3u;
-#pragma unroll
-        for (int i = 0; i < RB / 4 + 1; ++i) qw[i] = buf_load4(rs_q, qa + 4 * i, 0);
-        const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes, a.N * (a.K >> 1));
-        const uint32_t c_voff = (uint32_t)(n * (a.K >> 1) + 8 * g);
-#pragma unroll
-        for (int j = 0; j < RB; ++j) cw[j] = buf_load8(rs_codes, c_voff, bcl(j) * 32);
-    }
-
-    // ---- tables and staged inputs ----
-    {
-        float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            lo = (tid & 15) == j ? tab.lv[j] : lo;
-            hi = (tid >> 4) == j ? tab.lv[j] : hi;
-        }
-        s_pair[tid] = pack_bf16x2(lo, hi);
-        s_e4m3[tid] = e4m3_to_f32((uint32_t)tid);
-    }
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-        const int q = tid + 256 * i, m = q / (RB * 8), c = q % (RB * 8);
-        *reinterpret_cast<uint4*>(s_x + m * XSTRIDE + c * 16) = xs[i];
-    }
-    __syncthreads();
-
-    // MFMA A operand: token m, inputs 16g.. of a block
-    const uint8_t* xrow = s_x + (lane & 15) * XSTRIDE + 32 * g;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (!ADAPTER) {
-        const float st_first = c2_step(c2f);
-        const float st_last = c2_step(c2l);
-        const uint32_t sh = ((uint32_t)(n * KB + b0) & 3u) * 8;
-#pragma unroll
-        for (int j = 0; j < RB; ++j) {
-            uint32_t w[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                w[e] = s_pair[(cw[j].x >> (8 * e)) & 0xFFu];
-                w[4 + e] = s_pair[(cw[j].y >> (8 * e)) & 0xFFu];
-            }
-            const bf16x8v x0 = *reinterpret_cast<const bf16x8v*>(xrow + j * 128);
-            const bf16x8v x1 = *reinterpret_cast<const bf16x8v*>(xrow + j * 128 + 16);
-            f32x4 part = {0.0f, 0.0f, 0.0f, 0.0f};
-            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                x0, __builtin_bit_cast(bf16x8v, make_uint4(w[0], w[1], w[2], w[3])), part, 0, 0, 0);
-            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                x1, __builtin_bit_cast(bf16x8v, make_uint4(w[4], w[5], w[6], w[7])), part, 0, 0, 0);
-            const uint32_t qword = (uint32_t)__builtin_amdgcn_alignbit(qw[j / 4 + 1], qw[j / 4], sh);
-            const uint32_t qbyte = (qword >> (8 * (j & 3))) & 0xFFu;
-            const float stp = ((n * KB + b0 + j) >> 8) == g_first ? st_first : st_last;
-            // blocks past the row contribute zero
-            const float c1p = j < nb ? __fmaf_rn(s_e4m3[qbyte], stp, mean) : 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = __fmaf_rn(c1p, part[i], acc[i]);
-        }
-    } else {
-        // adapter rows (bf16), four blocks at a time, the next four in flight
-        const __amdgpu_buffer_rsrc_t rs_al = make_rsrc(a.Al, (int64_t)a.r * a.K * 2);
-        const uint32_t a_voff = n < a.r ? (uint32_t)(n * a.K * 2 + 32 * g) : 0x80000000u;
-        auto load4 = [&](uint4 (&al)[4][2], int j0) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                al[u][0] = buf_load16(rs_al, a_voff, bcl(j0 + u) * 128);
-                al[u][1] = buf_load16(rs_al, a_voff + 16, bcl(j0 + u) * 128);
-            }
-        };
-        auto mfma4 = [&](const uint4 (&al)[4][2], int j0) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (j0 + u < nb) {
-                    const bf16x8v x0 = *reinterpret_cast<const bf16x8v*>(xrow + (j0 + u) * 128);
-                    const bf16x8v x1 = *reinterpret_cast<const bf16x8v*>(xrow + (j0 + u) * 128 + 16);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, __builtin_bit_cast(bf16x8v, al[u][0]), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, __builtin_bit_cast(bf16x8v, al[u][1]), acc, 0, 0, 0);
-                }
-            }
-        };
-        uint4 la[4][2], lb[4][2];
-        load4(la, 0);
-#pragma unroll
-        for (int j0 = 0; j0 < RB; j0 += 8) {
-            load4(lb, j0 + 4);
-            mfma4(la, j0);
-            if (j0 + 8 < RB) load4(la, j0 + 8);
-            mfma4(lb, j0 + 4);
-        }
-    }
-    // lane holds tokens 4g..4g+3 of row n
-    const int64_t nrows = ADAPTER ? a.r : a.N;
-    if (n < nrows) {
-        const int64_t col = ADAPTER ? a.N + n : n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * g + i < a.M) a.part[(slice * a.M + 4 * g + i) * (a.N + a.r) + col] = acc[i];
-    }
-}
-
-// grid (slice, row group): the slices of one row group are dispatched together, so the
-// workgroups in flight read whole rows of codes (long runs within one DRAM page);
-// the adapter row groups come first.
-template <int RB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 16 ? 4 : 2, 8)))
-void k_gemv_part(GvArgs a, Nf4Table tab) {
-    const int64_t nag = (a.r + GV_GROUP - 1) / GV_GROUP;
-    if ((int64_t)blockIdx.y < nag) gemv_part_body<RB, true>(a, tab, blockIdx.y);
-    else gemv_part_body<RB, false>(a, tab, (int64_t)blockIdx.y - nag);
-}
-
-constexpr int GR_ROWS = 64;
-
-// Sum of `slices` values spaced `stride` apart: eight independent running sums (so the
-// loads are in flight together), combined in a fixed order.
-__device__ __forceinline__ float sum_slices(const float* p, int64_t stride, int64_t slices) {
-    float t[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    int64_t sl = 0;
-    for (; sl + 8 <= slices; sl += 8) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) t[u] += p[(sl + u) * stride];
-    }
-#pragma unroll
-    for (int u = 0; u < 7; ++u)
-        if (sl + u < slices) t[u] += p[(sl + u) * stride];
-    return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
-}
-
-__global__ __launch_bounds__(256) void k_gemv_reduce(GvArgs a, int64_t slices) {
-    __shared__ float s_ts[16][129];       // s T (rounded to bf16), tokens x rank
-    const int tid = threadIdx.x;
-    const int64_t ld = a.N + a.r;
-    const int64_t sstride = (int64_t)a.M * ld;        // one slice of partial sums
-    const int64_t n0 = (int64_t)blockIdx.x * GR_ROWS;
-    // This thread's first output (token m, row n): its row of B and its sum over the
-    // slices are requested together with the sums that form T, so the workgroup makes
-    // one round trip to memory before the last step.
-    const int m_first = tid / GR_ROWS;
-    const int64_t n_first = n0 + tid % GR_ROWS;
-    const bool first_ok = m_first < a.M && n_first < a.N;
-    uint4 bv[16];
-#pragma unroll
-    for (int q8 = 0; q8 < 16; ++q8)
-        bv[q8] = (first_ok && q8 < a.r / 8) ? reinterpret_cast<const uint4*>(a.Bl + n_first * a.r)[q8]
-                                            : make_uint4(0, 0, 0, 0);
-    const float y_first = first_ok ? sum_slices(a.part + (int64_t)m_first * ld + n_first, sstride, slices) : 0.0f;
-    for (int i = tid; i < a.M * a.r; i += 256) {
-        const int m = i / a.r, q = i % a.r;
-        const float t = sum_slices(a.part + (int64_t)m * ld + a.N + q, sstride, slices);
-        s_ts[m][q] = bf16_to_f32(f32_to_bf16(a.s * t));
-        if (blockIdx.x == 0) a.T[(int64_t)m * a.r + q] = f32_to_bf16(t);
-    }
-    __syncthreads();
-    auto lora = [&](int m, const uint4 (&b)[16]) {
-        float l = 0.0f;
-#pragma unroll
-        for (int q8 = 0; q8 < 16; ++q8) {
-            if (q8 < a.r / 8) {
-                const uint32_t bw[4] = {b[q8].x, b[q8].y, b[q8].z, b[q8].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    l = __fmaf_rn(s_ts[m][8 * q8 + 2 * e], bf16_lo(bw[e]), l);
-                    l = __fmaf_rn(s_ts[m][8 * q8 + 2 * e + 1], bf16_hi(bw[e]), l);
-                }
-            }
-        }
-        return l;
-    };
-    if (first_ok) a.Y[(int64_t)m_first * a.N + n_first] = f32_to_bf16(y_first + lora(m_first, bv));
-    // remaining outputs (more than 4 tokens)
-    for (int i = tid + 256; i < a.M * GR_ROWS; i += 256) {
-        const int m = i / GR_ROWS;
-        const int64_t n = n0 + i % GR_ROWS;
-        if (n >= a.N) continue;
-        uint4 b2[16];
-#pragma unroll
-        for (int q8 = 0; q8 < 16; ++q8)
-            b2[q8] = q8 < a.r / 8 ? reinterpret_cast<const uint4*>(a.Bl + n * a.r)[q8] : make_uint4(0, 0, 0, 0);
-        const float y = sum_slices(a.part + (int64_t)m * ld + n, sstride, slices);
-        a.Y[(int64_t)m * a.N + n] = f32_to_bf16(y + lora(m, b2));
-    }
-}
-
-template <int RB>
-static hipError_t launch_gemv_part(dim3 grid, const GvArgs& ga, const Nf4Table& tab, hipStream_t st) {
-    const int lds = 2048 + 16 * (RB * 128 + 16);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_gemv_part<RB>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(k_gemv_part<RB>, grid, dim3(256), lds, st, ga, tab);
-    return hipGetLastError();
-}
-
-hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Al,
-                             const uint16_t* Bl, int r, float s, uint16_t* Y, uint16_t* T, float* part,
-                             const Nf4Table& tab, hipStream_t st) {
-    if (M == 0) return hipSuccess;
-    const int64_t slices = gemv_slices(M, W.cols);
-    GvArgs ga{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, X, (int)M, Al, Bl, r, s, part, Y, T};
-    dim3 g1((unsigned)slices, (unsigned)((r + GV_GROUP - 1) / GV_GROUP + (W.rows + GV_GROUP - 1) / GV_GROUP));
-    dim3 g2((unsigned)((W.rows + GR_ROWS - 1) / GR_ROWS > 0 ? (W.rows + GR_ROWS - 1) / GR_ROWS : 1));
-    return with_events(st, [&] {
-        if (g1.x > 0 && g1.y > 0) {
-            hipError_t e = gemv_rb(M) == 16 ? launch_gemv_part<16>(g1, ga, tab, st)
-                                            : launch_gemv_part<32>(g1, ga, tab, st);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(k_gemv_reduce, g2, dim3(256), 0, st, ga, slices);
-        return hipGetLastError();
-    });
 }
 
 }  // namespace nf4

@@ -1,0 +1,402 @@
+// gemv.hip -- few-token forward of the QLoRA NF4 linear layer (gfx950).
+//
+// "Paged optimizers, and QLoRA end to end" (zerotofrontier.app "sft/peft"): every
+// frozen matrix is dequantized block by block and multiplied in 16-bit precision,
+// with the bf16 LoRA output added.  Layer formula: "Putting it together"
+// (prism.theerrors.in QLoRA explainer).  For a handful of tokens the product is a
+// stream over the packed weight, bound by HBM.
+#include "bufio.h"
+#include "launch.h"
+
+namespace nf4 {
+
+// ---------------------------------------------------------------------------
+// Few-token forward (M <= 16): an HBM-bound stream over the packed weight, in two
+// launches.
+//
+// k_gemv_part<RB, MT>: workgroup (contraction slice, row group) = 64 rows x RB NF4
+// blocks; wave w owns rows 16w..16w+15.  The slice's token inputs X[0:MT, slice]
+// (MT = 4 or 16 staged token rows, rows past M reading zero) are staged once into
+// LDS, rows padded by 16 bytes for the banks.  Every wave then requests all of its
+// codes at once, so the whole slice is in flight and no later request waits behind an
+// earlier one (the vector-memory counter retires in order).
+//
+// Codes move as 16 bytes per lane: lane (n = lane % 16, g = lane / 16) reads bytes
+// 16g..16g+15 of the 64-byte block pair (2p, 2p+1) of row n, so one request covers
+// 64 contiguous bytes of each of 16 rows (the 8-byte-per-lane form, 32 bytes per row,
+// streams at about three quarters of the rate).  Lanes 0-31 then hold block 2p and
+// lanes 32-63 block 2p+1; one v_permlane32_swap per register pair trades the second
+// half of the first with the first half of the second, after which every lane holds
+// 16 codes of each block: codes kA(g)..kA(g)+15, kA = 0, 32, 16, 48 for g = 0..3.
+// Two v_mfma_f32_16x16x32_bf16 per block on the unscaled bf16 levels, against the
+// inputs of the same contraction indices from LDS, give the block's partial dot
+// products, which the block's decoded constant c1' scales into the fp32 accumulator.
+// Levels come from a 256-entry LDS table that maps one code byte to its two bf16
+// levels; c1' from an E4M3 table, the row's 8-bit constants (one aligned window) and
+// at most two second-level steps per row and slice.  Row groups past the weight run
+// the adapter rows A (bf16, no scale): partial sums of T = X A^T from the same pass.
+// Partial sums go to part[slice][token][row] (rows N.. hold T).
+//
+// k_gemv_reduce: per 32 or 64 weight rows, sums the slices in slice order, forms T
+// (the sum of its slices) and s T (bf16), and Y = sum + (s T) B^T (bf16), with every
+// load of a thread requested before the first is used.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+
+// NF4 blocks per contraction slice (16: more, smaller workgroups measured faster than
+// 32 even at 16 tokens, where the slices double the partial-sum traffic)
+constexpr int GV_RB = 16;
+int64_t gemv_slices(int64_t M, int64_t K) {
+    (void)M;
+    return ((K >> 6) + GV_RB - 1) / GV_RB;
+}
+size_t gemv_partial_bytes(int64_t M, int64_t N, int64_t K, int r) {
+    return (size_t)gemv_slices(M, K) * (size_t)M * (size_t)(N + r) * 4;
+}
+
+struct GvArgs {
+    const uint8_t* codes;
+    const uint8_t* qc;
+    const float* c2;
+    const float* mean;
+    int64_t N, K;
+    const uint16_t* X;
+    int M;
+    const uint16_t* Al;      // adapter A [r x K]
+    const uint16_t* Bl;      // adapter B [N x r]
+    int r;
+    float s;
+    float* part;             // [slices][M][N + r]
+    uint16_t* Y;             // [M x N]
+    uint16_t* T;             // [M x r]
+};
+
+// Four code bytes (8 codes) -> the MFMA operand of their 8 unscaled bf16 levels.
+__device__ __forceinline__ bf16x8v lookup8(const uint32_t* s_pair, uint32_t w) {
+    return __builtin_bit_cast(bf16x8v, make_uint4(s_pair[w & 0xFFu], s_pair[(w >> 8) & 0xFFu],
+                                                  s_pair[(w >> 16) & 0xFFu], s_pair[w >> 24]));
+}
+
+constexpr int GV_WV = 4;                   // waves per workgroup of k_gemv_part
+constexpr int GV_ROWS = 16 * GV_WV;        // weight rows per workgroup (16 per wave)
+constexpr int GV_AROWS = 16;               // adapter rows per workgroup
+
+// Dynamic LDS of k_gemv_part: staged inputs, adapter partial sums (the level and E4M3
+// tables are static, at fixed addresses, so that a lookup is one shift of a code byte).
+constexpr int gv_lds_bytes(int MT) { return MT * (GV_RB * 128 + 16) + GV_WV * 64 * 16; }
+
+// One workgroup of k_gemv_part: GV_ROWS weight rows (ADAPTER false), or GV_AROWS adapter
+// rows A (bf16, no scale) whose slice is split among the waves (wave w: blocks
+// w RB/WV ..) and summed across the waves in LDS, so that an adapter workgroup moves
+// about as many bytes as a weight workgroup.  Straight-line code from the first
+// request to the last wait, so that every wait names exactly the requests it needs.
+template <int RB, int MT, bool ADAPTER>
+__device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& tab, int64_t group) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t gv_lds[];
+    __shared__ uint32_t s_pair[256];                   // code byte -> two bf16 levels
+    __shared__ float s_e4m3[256];                      // 8-bit constant -> E4M3 value
+    constexpr int NT = 64 * GV_WV;                     // threads
+    constexpr int XSTRIDE = RB * 128 + 16;             // bytes per staged token row
+    constexpr int RBW = RB / GV_WV;                    // adapter blocks per wave
+    uint8_t* s_x = gv_lds;                                         // [MT][XSTRIDE] token inputs
+    f32x4* s_red = reinterpret_cast<f32x4*>(s_x + MT * XSTRIDE);   // [WV][64] adapter partials
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t KB = a.K >> 6;
+    const int64_t slice = blockIdx.x;
+    const int64_t b0 = slice * RB;                      // first block of the slice
+    const int nb = KB - b0 < RB ? (int)(KB - b0) : RB;  // blocks of the slice inside the row
+    const int nl = lane & 15, g = lane >> 4;
+    // row of this lane
+    const int64_t n = ADAPTER ? group * GV_AROWS + nl : group * GV_ROWS + 16 * wave + nl;
+
+    // ---- requests: token inputs of the slice first, then this wave's rows ----
+    // The inputs (MT token rows x RB*8 chunks of 16 bytes; tokens past M and chunks
+    // past the row lie outside the range and read zero) pass through registers into
+    // LDS.  Being requested first, the wait for them leaves the later requests in flight.
+    const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(a.X + b0 * 64, (int64_t)a.M * a.K * 2 - b0 * 128);
+    constexpr int XCH = MT * RB * 8 / NT;               // chunks per thread
+    uint4 xs[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int q = tid + NT * i, m = q / (RB * 8), c = q % (RB * 8);
+        const uint32_t vo = (m < a.M && c < nb * 8) ? (uint32_t)((int64_t)m * a.K * 2 + c * 16) : 0x80000000u;
+        xs[i] = buf_load16(rs_x, vo, 0);
+    }
+    uint4 cw[RB / 2];
+    uint32_t qw[RB / 4 + 1];
+    uint4 al[RBW][2];
+    float mean = 0.0f, c2f = 0.0f, c2l = 0.0f;
+    int64_t g_first = 0;
+    if constexpr (!ADAPTER) {
+        mean = *a.mean;
+        // second-level constants: a row's slice meets at most two 256-blocks
+        const int64_t n2 = (a.N * KB + 255) >> 8;
+        const int64_t ci0 = n * KB + b0;
+        g_first = ci0 >> 8;
+        const int64_t gl = (ci0 + nb - 1) >> 8;
+        c2f = a.c2[g_first < n2 ? g_first : n2 - 1];
+        c2l = a.c2[gl < n2 ? gl : n2 - 1];
+        // 8-bit constants of the slice (aligned window), then the codes in block order.
+        // The pair offset goes in the range-checked part of the address: a pair past
+        // the row reads the next row (finite codes, given a zero constant below) or,
+        // past the last row, zero.
+        const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(a.qc, a.N * KB);
+        const uint32_t qa = (uint32_t)ci0 & ~3u;
+#pragma unroll
+        for (int i = 0; i < RB / 4 + 1; ++i) qw[i] = buf_load4(rs_q, qa + 4 * i, 0);
+        const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes, a.N * (a.K >> 1));
+        const uint32_t c_voff = (uint32_t)(n * (a.K >> 1) + b0 * 32 + 16 * g);
+#pragma unroll
+        for (int p = 0; p < RB / 2; ++p) cw[p] = buf_load16(rs_codes, c_voff + 64 * p, 0);
+    } else {
+        // this wave's blocks of the adapter rows; lane (n, g) takes contraction indices
+        // 16g..16g+15 of each block (block index clamped into the row: the wave-uniform
+        // offset is not range-checked; blocks past the row are skipped below)
+        const __amdgpu_buffer_rsrc_t rs_al = make_rsrc(a.Al, (int64_t)a.r * a.K * 2);
+        const uint32_t a_voff = n < a.r ? (uint32_t)(n * a.K * 2 + 32 * g) : 0x80000000u;
+#pragma unroll
+        for (int u = 0; u < RBW; ++u) {
+            const int64_t j = b0 + wave * RBW + u;
+            const uint32_t so = (uint32_t)((j < KB ? j : KB - 1) * 128);
+            al[u][0] = buf_load16(rs_al, a_voff, so);
+            al[u][1] = buf_load16(rs_al, a_voff + 16, so);
+        }
+    }
+
+    // ---- tables and staged inputs ----
+    {
+        float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            lo = (tid & 15) == j ? tab.lv[j] : lo;
+            hi = (tid >> 4) == j ? tab.lv[j] : hi;
+        }
+        s_pair[tid] = pack_bf16x2(lo, hi);
+        s_e4m3[tid] = e4m3_to_f32((uint32_t)tid);
+    }
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int q = tid + NT * i, m = q / (RB * 8), c = q % (RB * 8);
+        *reinterpret_cast<uint4*>(s_x + m * XSTRIDE + c * 16) = xs[i];
+    }
+    __syncthreads();
+
+    // MFMA A operand rows: token m = lane % 16 (rows past MT repeat rows below MT; their
+    // outputs are never stored)
+    const uint8_t* xtok = s_x + (lane & (MT - 1)) * XSTRIDE;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!ADAPTER) {
+        const float st_first = c2_step(c2f);
+        const float st_last = c2_step(c2l);
+        const int64_t ci0 = n * KB + b0;                 // constant index of the slice's first block
+        // blocks j >= jsplit of this row's slice belong to the next second-level block
+        const int jsplit = 256 - (int)(ci0 & 255);
+        // the slice's 8-bit constants, realigned: byte j of q4[] is block j's
+        const uint32_t sh = ((uint32_t)ci0 & 3u) * 8;
+        uint32_t q4[RB / 4];
+#pragma unroll
+        for (int i = 0; i < RB / 4; ++i) q4[i] = (uint32_t)__builtin_amdgcn_alignbit(qw[i + 1], qw[i], sh);
+        const int kA = 32 * (g & 1) + 16 * (g >> 1);     // first contraction index of the lane
+        // valid: blocks past the row contribute zero (a factor, not a branch: the decoded
+        // constant of any byte is finite)
+        auto c1_of = [&](int j, bool all_valid) {
+            const uint32_t qbyte = (q4[j / 4] >> (8 * (j & 3))) & 0xFFu;
+            const float c = __fmaf_rn(s_e4m3[qbyte], j < jsplit ? st_first : st_last, mean);
+            return all_valid ? c : c * (float)(j < nb);
+        };
+        auto run = [&](bool all_valid) {
+#pragma unroll
+            for (int p = 0; p < RB / 2; ++p) {
+                // lanes 0-31: bytes of block 2p, lanes 32-63: block 2p+1 -> both blocks per lane
+                uint32_t x = cw[p].x, y = cw[p].y, z = cw[p].z, w = cw[p].w;
+                const auto xz = __builtin_amdgcn_permlane32_swap(x, z, false, false);
+                const auto yw = __builtin_amdgcn_permlane32_swap(y, w, false, false);
+                x = xz[0]; z = xz[1]; y = yw[0]; w = yw[1];
+                const uint8_t* xa = xtok + (2 * p) * 128 + kA * 2;
+                const uint8_t* xb = xa + 128;
+                f32x4 pa = {0.0f, 0.0f, 0.0f, 0.0f}, pb = {0.0f, 0.0f, 0.0f, 0.0f};
+                pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8v*>(xa),
+                                                             lookup8(s_pair, x), pa, 0, 0, 0);
+                pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8v*>(xa + 16),
+                                                             lookup8(s_pair, y), pa, 0, 0, 0);
+                pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8v*>(xb),
+                                                             lookup8(s_pair, z), pb, 0, 0, 0);
+                pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8v*>(xb + 16),
+                                                             lookup8(s_pair, w), pb, 0, 0, 0);
+                const float ca = c1_of(2 * p, all_valid), cb = c1_of(2 * p + 1, all_valid);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __fmaf_rn(cb, pb[i], __fmaf_rn(ca, pa[i], acc[i]));
+            }
+        };
+        // a whole slice (all but a row's last), or the last, with blocks past the row
+        if (nb == RB) run(true);
+        else run(false);
+    } else {
+        const uint8_t* xrow = xtok + 32 * g;
+#pragma unroll
+        for (int u = 0; u < RBW; ++u) {
+            const int j = wave * RBW + u;
+            if (j < nb) {
+                const bf16x8v x0 = *reinterpret_cast<const bf16x8v*>(xrow + j * 128);
+                const bf16x8v x1 = *reinterpret_cast<const bf16x8v*>(xrow + j * 128 + 16);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, __builtin_bit_cast(bf16x8v, al[u][0]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, __builtin_bit_cast(bf16x8v, al[u][1]), acc, 0, 0, 0);
+            }
+        }
+        // sum over the waves, in wave order
+        s_red[wave * 64 + lane] = acc;
+        __syncthreads();
+        if (wave != 0) return;
+        acc = s_red[lane];
+#pragma unroll
+        for (int w = 1; w < GV_WV; ++w) {
+            const f32x4 v = s_red[w * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += v[i];
+        }
+    }
+    // lane holds tokens 4g..4g+3 of row n
+    const int64_t nrows = ADAPTER ? a.r : a.N;
+    if (n < nrows) {
+        const int64_t col = ADAPTER ? a.N + n : n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * g + i < a.M) a.part[(slice * a.M + 4 * g + i) * (a.N + a.r) + col] = acc[i];
+    }
+}
+
+// grid (slice, row group): the slices of one row group are dispatched together, so the
+// workgroups in flight read whole rows of codes (long runs within one DRAM page);
+// the adapter row groups come first.
+template <int RB, int MT>
+__global__ __launch_bounds__(64 * GV_WV) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void k_gemv_part(GvArgs a, Nf4Table tab) {
+    const int64_t nag = (a.r + GV_AROWS - 1) / GV_AROWS;
+    if ((int64_t)blockIdx.y < nag) gemv_part_body<RB, MT, true>(a, tab, blockIdx.y);
+    else gemv_part_body<RB, MT, false>(a, tab, (int64_t)blockIdx.y - nag);
+}
+
+// k_gemv_reduce<ROWS, NO, NT>: workgroup of ROWS weight rows; thread (row n = n0 + tid %
+// ROWS, token group tg = tid / ROWS) owns outputs (tg + (256/ROWS) i, n), i < NO, and T
+// entries tid + 256 t, t < NT (all M x r of them, in every workgroup: they are few and
+// L2-resident).  Slices are added in slice order, 8 at a time with every load of the
+// eight requested before the first add.
+template <int ROWS, int NO, int NT>
+__global__ __launch_bounds__(256) void k_gemv_reduce(GvArgs a, int64_t slices) {
+    constexpr int TG = 256 / ROWS;
+    constexpr int NE = NO + NT;
+    __shared__ float s_ts[16][129];       // s T (rounded to bf16), tokens x rank
+    const int tid = threadIdx.x;
+    const int64_t ld = a.N + a.r;
+    const int64_t sstride = (int64_t)a.M * ld;        // one slice of partial sums
+    const int64_t n = (int64_t)blockIdx.x * ROWS + tid % ROWS;
+    const int tg = tid / ROWS;
+    // this thread's row of B, requested first
+    uint4 bv[16];
+    const bool row_ok = n < a.N;
+#pragma unroll
+    for (int q8 = 0; q8 < 16; ++q8)
+        bv[q8] = (row_ok && q8 < a.r / 8) ? reinterpret_cast<const uint4*>(a.Bl + n * a.r)[q8] : make_uint4(0, 0, 0, 0);
+    // partial-sum offsets of the outputs and T entries; an entry that does not exist
+    // reads offset 0 and adds zero
+    int64_t off[NE];
+    bool ok[NE];
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+        const int m = tg + TG * i;
+        ok[i] = row_ok && m < a.M;
+        off[i] = ok[i] ? (int64_t)m * ld + n : 0;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int e = tid + 256 * t;
+        ok[NO + t] = e < a.M * a.r;
+        off[NO + t] = ok[NO + t] ? (int64_t)(e / a.r) * ld + a.N + e % a.r : 0;
+    }
+    float sum[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) sum[i] = 0.0f;
+    for (int64_t s0 = 0; s0 < slices; s0 += 8) {
+        float v[8][NE];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float* ps = a.part + (s0 + u < slices ? (s0 + u) * sstride : 0);
+#pragma unroll
+            for (int i = 0; i < NE; ++i) v[u][i] = ps[off[i]];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool su = s0 + u < slices;
+#pragma unroll
+            for (int i = 0; i < NE; ++i) sum[i] += (su && ok[i]) ? v[u][i] : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (ok[NO + t]) {
+            const int e = tid + 256 * t, m = e / a.r, q = e % a.r;
+            s_ts[m][q] = bf16_to_f32(f32_to_bf16(a.s * sum[NO + t]));
+            if (blockIdx.x == 0) a.T[(int64_t)m * a.r + q] = f32_to_bf16(sum[NO + t]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+        if (!ok[i]) continue;
+        const int m = tg + TG * i;
+        float l = 0.0f;
+#pragma unroll
+        for (int q8 = 0; q8 < 16; ++q8) {
+            if (q8 < a.r / 8) {
+                const uint32_t bw[4] = {bv[q8].x, bv[q8].y, bv[q8].z, bv[q8].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    l = __fmaf_rn(s_ts[m][8 * q8 + 2 * e], bf16_lo(bw[e]), l);
+                    l = __fmaf_rn(s_ts[m][8 * q8 + 2 * e + 1], bf16_hi(bw[e]), l);
+                }
+            }
+        }
+        a.Y[(int64_t)m * a.N + n] = f32_to_bf16(sum[i] + l);
+    }
+}
+
+template <int MT>
+static hipError_t launch_gemv_part(dim3 grid, const GvArgs& ga, const Nf4Table& tab, hipStream_t st) {
+    const int lds = gv_lds_bytes(MT);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_gemv_part<GV_RB, MT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_gemv_part<GV_RB, MT>), grid, dim3(64 * GV_WV), lds, st, ga, tab);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, const uint16_t* Al,
+                             const uint16_t* Bl, int r, float s, uint16_t* Y, uint16_t* T, float* part,
+                             const Nf4Table& tab, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    const int64_t slices = gemv_slices(M, W.cols);
+    GvArgs ga{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, X, (int)M, Al, Bl, r, s, part, Y, T};
+    dim3 g1((unsigned)slices, (unsigned)((r + GV_AROWS - 1) / GV_AROWS + (W.rows + GV_ROWS - 1) / GV_ROWS));
+    // reduce: 32 rows x 8 token groups (one output per thread) for up to 4 tokens,
+    // 64 rows x 4 token groups (four outputs) above
+    const bool small = M <= 4;
+    const int64_t rrows = small ? 32 : 64;
+    dim3 g2((unsigned)((W.rows + rrows - 1) / rrows > 0 ? (W.rows + rrows - 1) / rrows : 1));
+    return with_events(st, [&] {
+        if (g1.x > 0 && g1.y > 0) {
+            hipError_t e = small ? launch_gemv_part<4>(g1, ga, tab, st) : launch_gemv_part<16>(g1, ga, tab, st);
+            if (e != hipSuccess) return e;
+        }
+        if (small) hipLaunchKernelGGL((k_gemv_reduce<32, 1, 2>), g2, dim3(256), 0, st, ga, slices);
+        else hipLaunchKernelGGL((k_gemv_reduce<64, 4, 8>), g2, dim3(256), 0, st, ga, slices);
+        return hipGetLastError();
+    });
+}
+
+}  // namespace nf4

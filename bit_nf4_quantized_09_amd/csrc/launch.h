@@ -50,6 +50,22 @@ struct FusedEvents {
 };
 FusedEvents& fused_events();
 
+// Launch `fn` between the armed profiling events (if any), then disarm.
+template <typename F>
+inline hipError_t with_events(hipStream_t st, F&& fn) {
+    FusedEvents& ev = fused_events();
+    const FusedEvents armed = ev;
+    ev = FusedEvents{};
+    if (armed.start) {
+        hipError_t e = hipEventRecord(armed.start, st);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = fn();
+    if (e != hipSuccess) return e;
+    if (armed.stop) return hipEventRecord(armed.stop, st);
+    return hipSuccess;
+}
+
 // ---- fused dequant products -------------------------------------------------
 // Y = X W'^T + Ts B^T, Ts = s T   (MFMA GEMM, dequantization fused into the W operand load).
 // c1: the decoded first-level constants of W (launch_double_dequantize), one per 64-block.
