@@ -12,7 +12,8 @@ namespace nf4 {
 // ---------------------------------------------------------------------------
 // Quantize.  One lane owns 8 consecutive values (32 bytes of fp32 or 16 of bf16);
 // the 8 lanes of one 64-value block reduce the absmax with xor shuffles, then each
-// lane encodes its values and writes one 32-bit word of codes.
+// lane encodes its values and writes one 32-bit word of codes.  A workgroup takes
+// 32 blocks per step and strides over the tensor.
 //
 // Division: x = fp32(w / absmax) is formed from the correctly rounded reciprocal
 // y = RN(1/absmax) (one IEEE division per lane) as q = RN(w y), r = w - absmax q
@@ -21,74 +22,111 @@ namespace nf4 {
 // is a normal number.  A quotient small enough to be subnormal lies far inside
 // (-t, t) for the smallest encode threshold t ~ 0.04, so its code is the zero
 // level whichever way it rounds: the codes equal those of the IEEE division.
+//
+// Encode: the code is the number of thresholds below x (nearest level, a value
+// exactly between two levels taking the lower code).  |x| <= 1, so bucket
+// b = floor(32 x) + 32 (exact: 32 x is exact) is in [0, 64]; bucket b covers
+// [(b-32)/32, (b-31)/32).  The thresholds lie more than 1/32 apart, so a bucket
+// holds at most one: code = (thresholds below the bucket) + (x > the bucket's
+// threshold, +inf if none).  The same fp32 thresholds and strict comparisons as a
+// search through all fifteen, in one LDS read, one compare and one add.
 // ---------------------------------------------------------------------------
+constexpr int QB_BLOCKS = 32;          // 64-value blocks per workgroup step (8 lanes each)
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ w, int64_t n,
                                                   uint8_t* __restrict__ codes,
                                                   float* __restrict__ absmax, Nf4Table tab) {
     constexpr int EPL = 8;                 // values per lane
     constexpr int LPB = 64 / EPL;          // lanes per 64-value block
-    const int64_t nblk = (n + 63) / 64;
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t b = g / LPB;
-    if (b >= nblk) return;                 // whole 64-value groups leave together
-    const int sub = (int)(g % LPB);
-    const int64_t base = b * 64 + (int64_t)sub * EPL;
-    const bool full = (b * 64 + 64 <= n);
-
-    float v[EPL];
-    if (full) {
-        if constexpr (sizeof(T) == 4) {
-            const uint4 r0 = *reinterpret_cast<const uint4*>(w + base);
-            const uint4 r1 = *reinterpret_cast<const uint4*>(w + base + 4);
-            v[0] = __uint_as_float(r0.x); v[1] = __uint_as_float(r0.y);
-            v[2] = __uint_as_float(r0.z); v[3] = __uint_as_float(r0.w);
-            v[4] = __uint_as_float(r1.x); v[5] = __uint_as_float(r1.y);
-            v[6] = __uint_as_float(r1.z); v[7] = __uint_as_float(r1.w);
-        } else {
-            const uint4 raw = *reinterpret_cast<const uint4*>(w + base);
-            const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+    __shared__ uint2 s_bucket[65];         // {thresholds below, threshold bits}
+    if (threadIdx.x < 65) {
+        const float lo = (float)((int)threadIdx.x - 32) * (1.0f / 32.0f);
+        const float hi = lo + 1.0f / 32.0f;
+        uint32_t below = 0;
+        float th = __builtin_inff();
 #pragma unroll
-            for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(r4[j]); v[2 * j + 1] = bf16_hi(r4[j]); }
+        for (int j = 0; j < 15; ++j) {
+            below += tab.th[j] < lo ? 1u : 0u;
+            th = (tab.th[j] >= lo && tab.th[j] < hi) ? tab.th[j] : th;
         }
-    } else {
+        s_bucket[threadIdx.x] = make_uint2(below, __float_as_uint(th));
+    }
+    __syncthreads();
+
+    const int64_t nblk = (n + 63) / 64;
+    const int64_t steps = (nblk + QB_BLOCKS - 1) / QB_BLOCKS;
+    const int sub = (int)(threadIdx.x % LPB);
+    for (int64_t st = blockIdx.x; st < steps; st += gridDim.x) {
+        const int64_t b = st * QB_BLOCKS + threadIdx.x / LPB;
+        if (b >= nblk) continue;           // whole 64-value groups leave together
+        const int64_t base = b * 64 + (int64_t)sub * EPL;
+        const bool full = (b * 64 + 64 <= n);
+
+        float v[EPL];
+        if (full) {
+            if constexpr (sizeof(T) == 4) {
+                const uint4 r0 = *reinterpret_cast<const uint4*>(w + base);
+                const uint4 r1 = *reinterpret_cast<const uint4*>(w + base + 4);
+                v[0] = __uint_as_float(r0.x); v[1] = __uint_as_float(r0.y);
+                v[2] = __uint_as_float(r0.z); v[3] = __uint_as_float(r0.w);
+                v[4] = __uint_as_float(r1.x); v[5] = __uint_as_float(r1.y);
+                v[6] = __uint_as_float(r1.z); v[7] = __uint_as_float(r1.w);
+            } else {
+                const uint4 raw = *reinterpret_cast<const uint4*>(w + base);
+                const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(r4[j]); v[2 * j + 1] = bf16_hi(r4[j]); }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int64_t idx = base + e;
+                float x = 0.0f;
+                if (idx < n) {
+                    if constexpr (sizeof(T) == 4) x = __uint_as_float(w[idx]);
+                    else x = bf16_to_f32(w[idx]);
+                }
+                v[e] = x;
+            }
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) m = fmaxf(m, fabsf(v[e]));
+#pragma unroll
+        for (int o = LPB / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, LPB));
+        if (sub == 0) absmax[b] = m;
+
+        const float y = __fdiv_rn(1.0f, m);
+        uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            const int64_t idx = base + e;
-            float x = 0.0f;
-            if (idx < n) {
-                if constexpr (sizeof(T) == 4) x = __uint_as_float(w[idx]);
-                else x = bf16_to_f32(w[idx]);
-            }
-            v[e] = x;
+            const float q = v[e] * y;
+            const float r = __fmaf_rn(-m, q, v[e]);
+            const float x = __fmaf_rn(r, y, q);
+            // bucket index, clamped (a zero block gives NaN here; its codes are replaced below)
+            const int bi = min(max((int)floorf(x * 32.0f) + 32, 0), 64);
+            const uint2 bk = s_bucket[bi];
+            const uint32_t code = bk.x + (x > __uint_as_float(bk.y) ? 1u : 0u);
+            packed |= code << (4 * e);
         }
-    }
-    float m = 0.0f;
+        if (m == 0.0f) packed = 0x77777777u;   // an all-zero block: the exact-zero level
+        uint8_t* dst = codes + base / 2;
+        if (full) {
+            *reinterpret_cast<uint32_t*>(dst) = packed;
+        } else {
+            const int64_t nbytes = (n + 1) / 2;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) m = fmaxf(m, fabsf(v[e]));
-#pragma unroll
-    for (int o = LPB / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, LPB));
-    if (sub == 0) absmax[b] = m;
-
-    const float y = __fdiv_rn(1.0f, m);
-    uint32_t packed = 0;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const float q = v[e] * y;
-        const float r = __fmaf_rn(-m, q, v[e]);
-        const float x = __fmaf_rn(r, y, q);
-        uint32_t code = (m == 0.0f) ? 7u : nf4_encode(x, tab);
-        if (!full && base + e >= n) code = 0u;
-        packed |= code << (4 * e);
-    }
-    uint8_t* dst = codes + base / 2;
-    if (full) {
-        *reinterpret_cast<uint32_t*>(dst) = packed;
-    } else {
-        const int64_t nbytes = (n + 1) / 2;
-#pragma unroll
-        for (int j = 0; j < EPL / 2; ++j)
-            if (base / 2 + j < nbytes) dst[j] = (uint8_t)(packed >> (8 * j));
+            for (int j = 0; j < EPL / 2; ++j) {
+                if (base / 2 + j < nbytes) {
+                    // codes past n are zero
+                    uint32_t byte = (packed >> (8 * j)) & 0xFFu;
+                    if (base + 2 * j + 1 >= n) byte &= 0x0Fu;
+                    if (base + 2 * j >= n) byte = 0u;
+                    dst[j] = (uint8_t)byte;
+                }
+            }
+        }
     }
 }
 
@@ -96,8 +134,9 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, uint8_t* codes
                            const Nf4Table& tab, hipStream_t s) {
     if (n == 0) return hipSuccess;
     const int64_t nblk = (n + 63) / 64;
-    const int64_t lanes = nblk * 8;
-    const unsigned grid = (unsigned)((lanes + 255) / 256);
+    const int64_t steps = (nblk + QB_BLOCKS - 1) / QB_BLOCKS;
+    // enough workgroups to fill the chip several times over; each strides over the rest
+    const unsigned grid = (unsigned)(steps < 8192 ? steps : 8192);
     if (w_bf16)
         hipLaunchKernelGGL(k_quantize<uint16_t>, dim3(grid), dim3(256), 0, s,
                            (const uint16_t*)w, n, codes, absmax, tab);
