@@ -5,6 +5,8 @@
 // levels), "Double quantization" (mean-subtracted 8-bit constants in blocks of
 // 256 with fp32 second-level constants), "The real way" (two codes per byte).
 // All of these kernels are HBM-bound streams.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace nf4 {
@@ -285,7 +287,11 @@ hipError_t launch_double_dequantize(const uint8_t* q, const float* c2, const flo
 // for fp32 output, 8 for bf16, so one group is 16 bytes of output) in a
 // grid-stride loop.  Store j of lane l in wave w covers group (8w + j) * 64 + l
 // of the chunk, so every store (and every code load) of a wave is one contiguous
-// run.  The decoded constants of the chunk's blocks are formed once into LDS.
+// run.  Each lane decodes the constant of its group's block itself (the 8-bit
+// constants and second-level constants are L1-resident, 16 / E lanes read the same
+// byte), so a chunk needs no barrier, and every request of a chunk is made before
+// its first store.  Levels come from a 256-entry LDS table of code byte -> the two
+// fp32 levels.
 // ---------------------------------------------------------------------------
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
@@ -295,31 +301,33 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
                                                     void* __restrict__ out, Nf4Table tab) {
     constexpr int E = OUT_BF16 ? 8 : 4;            // values per group (16 bytes of output)
     constexpr int CHUNK = 256 * 8 * E;             // values per chunk
-    constexpr int CBLK = CHUNK / 64;               // NF4 blocks per chunk (128 or 256)
-    __shared__ float s_lv[16];
-    __shared__ float s_c1[CBLK];
-    if (threadIdx.x < 16) {
-        float l = 0.0f;
+    __shared__ float2 s_pair[256];                 // code byte -> (level of low nibble, of high nibble)
+    {
+        float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) l = threadIdx.x == j ? tab.lv[j] : l;
-        s_lv[threadIdx.x] = l;
+        for (int j = 0; j < 16; ++j) {
+            lo = (threadIdx.x & 15) == j ? tab.lv[j] : lo;
+            hi = (threadIdx.x >> 4) == j ? tab.lv[j] : hi;
+        }
+        s_pair[threadIdx.x] = make_float2(lo, hi);
     }
+    __syncthreads();
     const float mean = *mean_p;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t nblk = (n + 63) / 64;
     const int64_t nbytes = (n + 1) / 2;
-    for (int64_t c0 = (int64_t)blockIdx.x * CHUNK; c0 < n; c0 += (int64_t)gridDim.x * CHUNK) {
-        __syncthreads();                           // previous chunk's constants are consumed
-        if (threadIdx.x < CBLK) {
-            const int64_t b = c0 / 64 + threadIdx.x;
-            s_c1[threadIdx.x] = b < nblk ? decode_c1(q[b], c2_step(c2[b >> 8]), mean) : 0.0f;
-        }
-        __syncthreads();
+    const int64_t n2 = (nblk + 255) / 256;
+    // one chunk; WHOLE: every group of the chunk lies inside the tensor (no checks, no
+    // branches, so the requests of all eight groups are in flight together)
+    auto chunk = [&](int64_t c0, auto whole_tag) {
+        constexpr bool WHOLE = decltype(whole_tag)::value;
         uint32_t cw[8];
+        uint32_t qb[8];
+        float cs[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int64_t i0 = c0 + ((int64_t)(8 * wave + j) * 64 + lane) * E;
-            if (i0 + E <= n) {
+            if (WHOLE || i0 + E <= n) {
                 if constexpr (E == 4) cw[j] = *reinterpret_cast<const uint16_t*>(codes + i0 / 2);
                 else cw[j] = *reinterpret_cast<const uint32_t*>(codes + i0 / 2);
             } else {
@@ -328,18 +336,26 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
                     if (i0 / 2 + t < nbytes) x |= (uint32_t)codes[i0 / 2 + t] << (8 * t);
                 cw[j] = x;
             }
+            // the group's block, clamped into the arrays (a group past n stores nothing)
+            const int64_t blk = WHOLE ? i0 / 64 : (i0 / 64 < nblk ? i0 / 64 : nblk - 1);
+            qb[j] = q[blk];
+            cs[j] = c2[WHOLE ? (blk >> 8) : ((blk >> 8) < n2 ? (blk >> 8) : n2 - 1)];
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int64_t i0 = c0 + ((int64_t)(8 * wave + j) * 64 + lane) * E;
-            if (i0 >= n) continue;
-            const float c1p = s_c1[(i0 - c0) >> 6];
+            if (!WHOLE && i0 >= n) continue;
+            const float c1p = decode_c1(qb[j], c2_step(cs[j]), mean);
             float v[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[e] = s_lv[(cw[j] >> (4 * e)) & 0xFu] * c1p;
+            for (int e = 0; e < E / 2; ++e) {
+                const float2 l = s_pair[(cw[j] >> (8 * e)) & 0xFFu];
+                v[2 * e] = l.x * c1p;
+                v[2 * e + 1] = l.y * c1p;
+            }
             if constexpr (OUT_BF16) {
                 uint16_t* o = reinterpret_cast<uint16_t*>(out) + i0;
-                if (i0 + E <= n) {
+                if (WHOLE || i0 + E <= n) {
                     uint4 pk;
                     pk.x = pack_bf16x2(v[0], v[1]); pk.y = pack_bf16x2(v[2], v[3]);
                     pk.z = pack_bf16x2(v[4], v[5]); pk.w = pack_bf16x2(v[6], v[7]);
@@ -350,7 +366,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
                 }
             } else {
                 float* o = reinterpret_cast<float*>(out) + i0;
-                if (i0 + E <= n) {
+                if (WHOLE || i0 + E <= n) {
                     *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
                 } else {
                     for (int e = 0; e < E; ++e)
@@ -358,6 +374,10 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
                 }
             }
         }
+    };
+    for (int64_t c0 = (int64_t)blockIdx.x * CHUNK; c0 < n; c0 += (int64_t)gridDim.x * CHUNK) {
+        if (c0 + CHUNK <= n) chunk(c0, std::true_type{});
+        else chunk(c0, std::false_type{});
     }
 }
 
