@@ -10,23 +10,40 @@
 // Forward  Y  = X W'^T + s T B^T   (NT product, contraction over K)
 // Backward dX = dY W' + s U A      (NN product, contraction over N)
 //
-// Design for CDNA4: 256 x 256 output tile per workgroup of 4 waves (each wave
-// 128 x 128 = 4 x 4 tiles of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators
-// per lane), one NF4 block (64 values) of contraction per pipeline step, two
-// LDS stages of 64 KB.  The packed codes of one (row, 64-block) are owned by
-// one lane, which builds a 16-entry bf16 table scaled by the block's decoded
-// constant and expands its 64 codes with byte permutes before writing them to
-// LDS; every dequantized value is therefore computed once per workgroup and
-// reused by 256 rows of the other operand.
+// Design for CDNA4: a TM x TN output tile per workgroup of 4 waves (each wave
+// 128 x 128 = 4 x 4 tiles of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per
+// lane), one NF4 block (64 values) of contraction per pipeline step, two LDS
+// stages.  The packed codes of one (row, 64-block) are owned by 256/TN lanes, each
+// of which builds a 16-entry bf16 table scaled by the block's decoded constant and
+// expands its share of the codes with byte permutes before writing them to LDS;
+// every dequantized value is therefore computed once per workgroup and reused by TM
+// rows of the other operand.  The decode work per MFMA falls as TM grows: the
+// 512 x 128 tile (2 x 80 KB stages, the whole 160 KB LDS) decodes half as much per
+// MFMA as a 256 x 256 tile.
 #include "bufio.h"
 #include "launch.h"
 
 namespace nf4 {
 
-constexpr int FA_BYTES = 32768;         // A tile: 256 tokens x 64 contraction values (bf16)
-constexpr int FW_BYTES = 32768;         // W' tile: 256 x 64 (forward) or 64 x 256 (backward)
-constexpr int FSTAGE = FA_BYTES + FW_BYTES;
-constexpr int FLDS = 2 * FSTAGE;        // two pipeline stages: 128 KB of the 160 KB LDS
+// Tile geometry of k_fused<BWD, TM, TN>.
+template <int TM, int TN>
+struct FusedTile {
+    static_assert(TM * TN == TILE_FLOATS && TM % 128 == 0 && TN % 128 == 0, "tile");
+    static constexpr int WN = TN / 128;                  // waves across the tile (4 waves)
+    static constexpr int A_BYTES = TM * 128;             // A tile: TM tokens x 64 bf16
+    static constexpr int W_BYTES = TN * 128;             // W' tile: TN x 64 (fwd) or 64 x TN (bwd)
+    static constexpr int STAGE = A_BYTES + W_BYTES;
+    static constexpr int LDS = 2 * STAGE;
+    static constexpr int ACH = TM / 32;                  // A tile 16-byte chunks per lane per step
+    static constexpr int LPP = 256 / TN;                 // lanes per (row, 64-block) of W'
+    static constexpr int CPL = 64 / LPP;                 // codes per lane per step
+    static constexpr int NCH = CPL / 8;                  // 8-code chunks per lane per step
+    static constexpr int NW = CPL / 32;                  // 16-byte code words per lane
+    // A-tile register sets: two (8 chunks: loaded in step it for step it+2, written at the
+    // end of step it+1), or one (16 chunks: chunks 2r, 2r+1 written in region r of step
+    // it+1, reloaded for step it+2 two regions later)
+    static constexpr int DEPTH = ACH <= 8 ? 2 : 1;
+};
 
 // [rows][64 bf16] tile with 128-byte rows: 16-byte chunk c of row r sits at chunk
 // position c ^ g(r), g(r) = (r ^ (r >> 3)) & 7.  Any 16 consecutive rows reading the
@@ -36,11 +53,12 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
     return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
 }
 
-// Backward W' tile [64 n][256 k] with 512-byte rows, read by ds_read_b64_tr_b16:
+// Backward W' tile [64 n][TN k] with 2 TN-byte rows, read by ds_read_b64_tr_b16:
 // 32-byte segment u (16 k values) of row r sits at u ^ 2(r & 3), so the 4 rows x 2
 // segments that 32 lanes read in one pass land on distinct banks.
+template <int TN>
 __device__ __forceinline__ int wt_off(int row, int k) {
-    return row * 512 + (((k >> 4) ^ ((row & 3) << 1)) << 5) + ((k & 15) << 1);
+    return row * (2 * TN) + (((k >> 4) ^ ((row & 3) << 1)) << 5) + ((k & 15) << 1);
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -72,116 +90,115 @@ struct FusedArgs {
     float* spart;             // fp32 partial tiles, 65536 floats per (tail tile, piece)
 };
 
-// One lane's eight 16-byte chunks of an A tile.
+// One lane's 16-byte chunks of an A tile (indexed with constants only, so that they
+// stay in registers).
+template <int N>
 struct XRegs {
-    uint4 r0, r1, r2, r3, r4, r5, r6, r7;
+    uint4 r[N];
 };
 
-// Packed codes of one (row, 64-block) and its decoded constant (zero past the last row).
+// This lane's packed codes of one (row, 64-block) and its decoded constant (zero past
+// the last row).
+template <int NW>
 struct BlockCodes {
-    uint4 w0, w1;
+    uint4 w[NW];
     float c1;
 };
 
-template <bool BWD>
+template <bool BWD, int TM, int TN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fused(FusedArgs a, Nf4Table tab) {
+    using G = FusedTile<TM, TN>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / G::WN, wn = wave % G::WN;
     // forward tiles (tokens, out features); backward tiles (tokens, in features)
     Unit u;
-    if (!unit_of(blockIdx.x, (a.M + FT - 1) / FT, ((BWD ? a.K : a.N) + FT - 1) / FT, a.S, u)) return;
-    const int64_t c0 = u.tn * FT, m0 = u.tm * FT;
+    if (!unit_of(blockIdx.x, (a.M + TM - 1) / TM, ((BWD ? a.K : a.N) + TN - 1) / TN, a.S, u)) return;
+    const int64_t c0 = u.tn * TN, m0 = u.tm * TM;
     const int64_t KB = a.K >> 6;
     const int64_t ldA = BWD ? a.N : a.K;                 // row length of the A operand
     const int64_t all_steps = BWD ? (a.N + 63) >> 6 : KB;   // 64-deep contraction steps
     int64_t sb, steps;                                    // this unit's steps sb .. sb + steps - 1
     unit_steps(all_steps, a.chunk, u.split, sb, steps);
 
-    // ---- this lane's share of the packed weight: one (row, 64-block) per step ----
-    // forward: row c0 + tid, block = step; backward: row 64*step + tid/4, block c0/64 + tid%4.
-    // Rows past N fall outside the buffers' range and read zero codes and a zero
-    // constant, so their dequantized values are zero.  The forward advances by a
-    // wave-uniform offset inside the row; the backward moves the descriptors down by
-    // 64 rows per step.
-    const int nl = tid >> 2, jb = tid & 3;
+    // ---- this lane's share of the packed weight: CPL codes of one (row, 64-block) per step ----
+    // pair = tid / LPP, part = tid % LPP (codes part*CPL .. of the block).
+    // forward: row c0 + pair, block = step; backward: row 64*step + pair / (TN/64), block
+    // c0/64 + pair % (TN/64).  Rows past N fall outside the buffers' range and read zero
+    // codes and a zero constant, so their dequantized values are zero.  The forward
+    // advances by a wave-uniform offset inside the row; the backward moves the
+    // descriptors down by 64 rows per step.
+    const int pair = tid / G::LPP, part = tid % G::LPP;
+    const int nl = BWD ? pair / (TN / 64) : pair;         // row of the W' tile (bwd: of 64)
+    const int jb = BWD ? pair % (TN / 64) : 0;            // block of the tile (bwd)
     const int64_t kblk_b = (c0 >> 6) + jb < KB ? (c0 >> 6) + jb : KB - 1;
-    const int64_t my_row0 = BWD ? nl : c0 + tid;          // row at step 0
-    const uint32_t code_voff = (uint32_t)(my_row0 * (a.K >> 1) + (BWD ? kblk_b * 32 : 0));
+    const int64_t my_row0 = BWD ? nl : c0 + pair;         // row at step 0
+    const uint32_t code_voff = (uint32_t)(my_row0 * (a.K >> 1) + (BWD ? kblk_b * 32 : 0) + part * (G::CPL / 2));
     const uint32_t c1_voff = (uint32_t)((my_row0 * KB + (BWD ? kblk_b : 0)) * 4);
     // The constant is requested first: it is needed first (scaled table), then the
     // codes, then the A tile (LDS write at the end of the step).
     auto load_codes = [&](int64_t lstep) {
         const int64_t step = sb + lstep;
-        BlockCodes bc;
+        BlockCodes<G::NW> bc;
         if constexpr (BWD) {
             const int64_t r0 = step * 64;                  // first weight row of the step
             const __amdgpu_buffer_rsrc_t rs_c1 = make_rsrc(a.c1 + r0 * KB, (a.N - r0) * KB * 4);
             const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes + r0 * (a.K >> 1), (a.N - r0) * (a.K >> 1));
             bc.c1 = buf_loadf(rs_c1, c1_voff, 0);
-            bc.w0 = buf_load16(rs_codes, code_voff, 0);
-            bc.w1 = buf_load16(rs_codes, code_voff + 16, 0);
+#pragma unroll
+            for (int i = 0; i < G::NW; ++i) bc.w[i] = buf_load16(rs_codes, code_voff + 16 * i, 0);
         } else {
             const __amdgpu_buffer_rsrc_t rs_c1 = make_rsrc(a.c1, a.N * KB * 4);
             const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes, a.N * (a.K >> 1));
             bc.c1 = buf_loadf(rs_c1, c1_voff, (uint32_t)(step * 4));
-            bc.w0 = buf_load16(rs_codes, code_voff, (uint32_t)(step * 32));
-            bc.w1 = buf_load16(rs_codes, code_voff + 16, (uint32_t)(step * 32));
+#pragma unroll
+            for (int i = 0; i < G::NW; ++i) bc.w[i] = buf_load16(rs_codes, code_voff + 16 * i, (uint32_t)(step * 32));
         }
         return bc;
     };
-    auto dequant_store = [&](uint8_t* sW, const BlockCodes& bc) {
-        const float c1p = bc.c1;
-        const ScaledTable st = make_scaled_table(tab, c1p);
-        const uint32_t words[8] = {bc.w0.x, bc.w0.y, bc.w0.z, bc.w0.w, bc.w1.x, bc.w1.y, bc.w1.z, bc.w1.w};
+    // LDS position of this lane's decoded chunk c (8 codes)
+    auto w_off = [&](int c) {
+        if constexpr (BWD) return wt_off<TN>(nl, jb * 64 + part * G::CPL + c * 8);
+        else return tile_off(pair, part * G::NCH + c);
+    };
+    auto word = [&](const BlockCodes<G::NW>& bc, int c) {
+        const uint4 v = bc.w[c >> 2];
+        return (c & 3) == 0 ? v.x : (c & 3) == 1 ? v.y : (c & 3) == 2 ? v.z : v.w;
+    };
+    auto dequant_store = [&](uint8_t* sW, const BlockCodes<G::NW>& bc) {
+        const ScaledTable st = make_scaled_table(tab, bc.c1);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < G::NCH; ++c) {
             uint32_t o[4];
-            decode8(st, words[c], o);
-            const uint4 v = make_uint4(o[0], o[1], o[2], o[3]);
-            if constexpr (BWD) *reinterpret_cast<uint4*>(sW + wt_off(nl, jb * 64 + c * 8)) = v;
-            else *reinterpret_cast<uint4*>(sW + tile_off(tid, c)) = v;
+            decode8(st, word(bc, c), o);
+            *reinterpret_cast<uint4*>(sW + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     };
 
-    // ---- A operand tile: 256 tokens x 64 contraction values, 8 chunks per lane ----
+    // ---- A operand tile: TM tokens x 64 contraction values, ACH chunks per lane ----
     // chunk i of this lane: tile row (tid >> 3) + 32 i, contraction chunk (tid & 7).  The
     // descriptor of a step starts at the step's first contraction value of the tile's
     // first row and ends with the tile's last row, so rows past M, and columns of the
     // last row past its end, read zero.  Backward columns past N of the other rows read
     // finite data of the next row and meet zeroed W' rows.
     const int achunk = tid & 7;
-    const int64_t arows = a.M - m0 < FT ? a.M - m0 : FT;
+    const int64_t arows = a.M - m0 < TM ? a.M - m0 : TM;
     const uint32_t a_voff0 = (uint32_t)(((tid >> 3) * ldA + achunk * 8) * 2);
     const uint32_t a_rstride = (uint32_t)(32 * ldA * 2);    // bytes between chunk i and i+1
-    const uint32_t a_voff1 = a_voff0 + a_rstride, a_voff2 = a_voff1 + a_rstride;
-    const uint32_t a_voff3 = a_voff2 + a_rstride, a_voff4 = a_voff3 + a_rstride;
-    const uint32_t a_voff5 = a_voff4 + a_rstride, a_voff6 = a_voff5 + a_rstride;
-    const uint32_t a_voff7 = a_voff6 + a_rstride;
-
-    // Two register sets of the A tile: a set holds one step's 8 chunks from their
-    // load until their LDS write one step later (named members, not an array, so
-    // that they stay in registers).
-    XRegs xa, xb;
-    auto load_a = [&](XRegs& X, int64_t lstep) {
+    auto a_rsrc = [&](int64_t lstep) {
         const int64_t step = sb + lstep;
-        const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A + m0 * ldA + step * 64, arows * ldA * 2 - step * 128);
-        X.r0 = buf_load16(rs_a, a_voff0, 0);
-        X.r1 = buf_load16(rs_a, a_voff1, 0);
-        X.r2 = buf_load16(rs_a, a_voff2, 0);
-        X.r3 = buf_load16(rs_a, a_voff3, 0);
-        X.r4 = buf_load16(rs_a, a_voff4, 0);
-        X.r5 = buf_load16(rs_a, a_voff5, 0);
-        X.r6 = buf_load16(rs_a, a_voff6, 0);
-        X.r7 = buf_load16(rs_a, a_voff7, 0);
+        return make_rsrc(a.A + m0 * ldA + step * 64, arows * ldA * 2 - step * 128);
     };
-    auto store_a = [&](const XRegs& X, uint8_t* sA) {
-        auto one = [&](const uint4& xi, int i) {
-            *reinterpret_cast<uint4*>(sA + tile_off((tid + 256 * i) >> 3, achunk)) = xi;
-        };
-        one(X.r0, 0); one(X.r1, 1); one(X.r2, 2); one(X.r3, 3);
-        one(X.r4, 4); one(X.r5, 5); one(X.r6, 6); one(X.r7, 7);
+    auto load_a = [&](XRegs<G::ACH>& X, int64_t lstep) {
+        const __amdgpu_buffer_rsrc_t rs_a = a_rsrc(lstep);
+#pragma unroll
+        for (int i = 0; i < G::ACH; ++i) X.r[i] = buf_load16(rs_a, a_voff0 + i * a_rstride, 0);
+    };
+    auto store_a = [&](const XRegs<G::ACH>& X, uint8_t* sA) {
+#pragma unroll
+        for (int i = 0; i < G::ACH; ++i)
+            *reinterpret_cast<uint4*>(sA + tile_off((tid >> 3) + 32 * i, achunk)) = X.r[i];
     };
 
     f32x16 acc[4][4];
@@ -196,8 +213,8 @@ void k_fused(FusedArgs a, Nf4Table tab) {
             const int g = lane >> 4, jl = lane & 15;
             const int row = 16 * sub + 8 * (g >> 1) + (jl >> 2);
             const int k = wn * 128 + j * 32 + 16 * (g & 1) + 4 * (jl & 3);
-            const uint2 lo = ds_read_tr16(sB + wt_off(row, k));
-            const uint2 hi = ds_read_tr16(sB + wt_off(row + 4, k));
+            const uint2 lo = ds_read_tr16(sB + wt_off<TN>(row, k));
+            const uint2 hi = ds_read_tr16(sB + wt_off<TN>(row + 4, k));
             return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         } else {
             const int rb = wn * 128 + j * 32 + (lane & 31);
@@ -224,41 +241,31 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         }
     };
 
-    // ---- prologue: stage 0 <- step 0; A tile and codes of step 1 in registers ----
-    {
-        load_a(xa, 0);
-        const BlockCodes b0 = load_codes(0);
-        store_a(xa, lds);
-        dequant_store(lds + FA_BYTES, b0);
-    }
-    load_a(xb, steps > 1 ? 1 : 0);
-    BlockCodes wcur = load_codes(steps > 1 ? 1 : 0);
-    __syncthreads();
-
     // ---- main loop: the MFMAs of step `it` overlap the dequantization of step it+1 ----
     // The body is laid out by hand as 8 regions fenced by sched_barrier: region r
     // issues MFMAs 8r..8r+7 of this step (substep r/2), one slice of the
     // dequantization of the next step (region 0: block constant and scaled table;
-    // region r > 0: codes 8(r-1)..8r-1 and their LDS write), half of the
-    // fragment reads of the following substep and one chunk of the A tile of step
-    // it+2 (8 chunks per lane per step).  Inside a region, each MFMA is
-    // followed by a few VALU instructions, so the VALU work executes while the
-    // matrix core is busy.
-    // step `it` (stage it & 1): xn receives the A tile of step it+2, xw holds that of
-    // step it+1 and is written to the other stage at the end.
-    auto step_body = [&](int64_t it, XRegs& xn, const XRegs& xw) {
+    // region r > 0: chunk r-1 of this lane's codes and its LDS write), half of the
+    // fragment reads of the following substep and a share of the A tile traffic.  Inside
+    // a region, each MFMA is followed by a few VALU instructions, so the VALU work
+    // executes while the matrix core is busy.
+    // step `it` (stage it & 1): xn receives the A tile of step it+2 and xw holds that of
+    // step it+1, to be written to the other stage.  Two sets: one chunk loaded per region,
+    // xw written at the end.  One set (xn == xw): region r writes chunks 2r, 2r+1 and
+    // reloads chunks 2r-4, 2r-3; chunks 12-15 are reloaded after the last region, so
+    // every chunk has six regions to arrive.  With one set the decode of the next W'
+    // tile runs in regions 3-7, away from the A-tile writes of the first regions.
+    BlockCodes<G::NW> wcur;
+    auto step_body = [&](int64_t it, XRegs<G::ACH>& xn, const XRegs<G::ACH>& xw) {
         const int st = (int)(it & 1);
-        const uint8_t* cur = lds + st * FSTAGE;
-        uint8_t* nxt = lds + (st ^ 1) * FSTAGE;
+        const uint8_t* cur = lds + st * G::STAGE;
+        uint8_t* nxt = lds + (st ^ 1) * G::STAGE;
         const int64_t n2 = it + 2 < steps ? it + 2 : steps - 1;
-        const BlockCodes wnxt = load_codes(n2);
-        const int64_t g2 = sb + n2;
-        const __amdgpu_buffer_rsrc_t rs_an = make_rsrc(a.A + m0 * ldA + g2 * 64, arows * ldA * 2 - g2 * 128);
-        const uint32_t words[8] = {wcur.w0.x, wcur.w0.y, wcur.w0.z, wcur.w0.w,
-                                   wcur.w1.x, wcur.w1.y, wcur.w1.z, wcur.w1.w};
-        uint8_t* sWn = nxt + FA_BYTES;
+        const BlockCodes<G::NW> wnxt = load_codes(n2);
+        const __amdgpu_buffer_rsrc_t rs_an = a_rsrc(n2);
+        uint8_t* sWn = nxt + G::A_BYTES;
         const uint8_t* sA = cur;
-        const uint8_t* sB = cur + FA_BYTES;
+        const uint8_t* sB = cur + G::A_BYTES;
 
         bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
@@ -289,27 +296,35 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 const int i = (half * 8 + t) >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fc][i], fb[fc][j], acc[i][j], 0, 0, 0);
             }
-            // one 16-byte chunk of the A tile of step it+2 per region: a burst of wide
-            // loads at the top of the step would stall the wave at the texture unit
-            switch (rg) {
-                case 0: xn.r0 = buf_load16(rs_an, a_voff0, 0); break;
-                case 1: xn.r1 = buf_load16(rs_an, a_voff1, 0); break;
-                case 2: xn.r2 = buf_load16(rs_an, a_voff2, 0); break;
-                case 3: xn.r3 = buf_load16(rs_an, a_voff3, 0); break;
-                case 4: xn.r4 = buf_load16(rs_an, a_voff4, 0); break;
-                case 5: xn.r5 = buf_load16(rs_an, a_voff5, 0); break;
-                case 6: xn.r6 = buf_load16(rs_an, a_voff6, 0); break;
-                default: xn.r7 = buf_load16(rs_an, a_voff7, 0); break;
-            }
-            if (rg == 0) {
-                tbl = make_scaled_table(tab, wcur.c1);
+            // A tile chunks, spread over the regions: a burst of wide loads at the top of
+            // the step would stall the wave at the texture unit
+            if constexpr (G::DEPTH == 2) {
+                xn.r[rg] = buf_load16(rs_an, a_voff0 + rg * a_rstride, 0);
             } else {
-                const int c = rg - 1;
+                // region r writes chunks 2r, 2r+1 and (r >= 2) reloads chunks 2r-4, 2r-3
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int i = 2 * rg + q;
+                    *reinterpret_cast<uint4*>(nxt + tile_off((tid >> 3) + 32 * i, achunk)) = xw.r[i];
+                }
+                if (rg >= 2) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int i = 2 * rg - 4 + q;
+                        xn.r[i] = buf_load16(rs_an, a_voff0 + i * a_rstride, 0);
+                    }
+                }
+            }
+            // decode window: regions 0.. (two register sets) or 3.. (one set: the first
+            // half carries the A tile writes)
+            constexpr int D0 = G::DEPTH == 2 ? 0 : 3;
+            if (rg == D0) {
+                tbl = make_scaled_table(tab, wcur.c1);
+            } else if (rg > D0 && rg - D0 - 1 < G::NCH && rg - D0 - 1 < 7 - D0) {
+                const int c = rg - D0 - 1;
                 uint32_t o[4];
-                decode8(tbl, words[c], o);
-                const uint4 v = make_uint4(o[0], o[1], o[2], o[3]);
-                if constexpr (BWD) *reinterpret_cast<uint4*>(sWn + wt_off(nl, jb * 64 + c * 8)) = v;
-                else *reinterpret_cast<uint4*>(sWn + tile_off(tid, c)) = v;
+                decode8(tbl, word(wcur, c), o);
+                *reinterpret_cast<uint4*>(sWn + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -317,28 +332,59 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);     // VALU
                 if (t < (BWD && half ? 8 : 4) && sub < 3)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
-                if (t == 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                if (G::DEPTH == 2 ? t == 2 : (rg >= 2 && (t == 2 || t == 6)))
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                if (G::DEPTH == 1 && (t == 4 || t == 7))
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        {
+#pragma unroll
+        for (int c = (G::DEPTH == 2 ? 7 : 4); c < G::NCH; ++c) {
             uint32_t o[4];
-            decode8(tbl, words[7], o);
-            const uint4 v = make_uint4(o[0], o[1], o[2], o[3]);
-            if constexpr (BWD) *reinterpret_cast<uint4*>(sWn + wt_off(nl, jb * 64 + 56)) = v;
-            else *reinterpret_cast<uint4*>(sWn + tile_off(tid, 7)) = v;
+            decode8(tbl, word(wcur, c), o);
+            *reinterpret_cast<uint4*>(sWn + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
         }
-        store_a(xw, nxt);
+        if constexpr (G::DEPTH == 2) {
+            store_a(xw, nxt);
+        } else {
+            // the last four chunks of the A tile of step it+2
+#pragma unroll
+            for (int i = 12; i < 16; ++i) xn.r[i] = buf_load16(rs_an, a_voff0 + i * a_rstride, 0);
+        }
         wcur = wnxt;
         __syncthreads();
     };
-    int64_t it = 0;
-    for (; it + 1 < steps; it += 2) {
-        step_body(it, xa, xb);
-        step_body(it + 1, xb, xa);
-    }
-    if (it < steps) step_body(it, xa, xb);
 
+    // ---- prologue: stage 0 <- step 0; codes of step 1 (and, DEPTH 2, the A tile of step 1) ----
+    XRegs<G::ACH> xa, xb;
+    {
+        load_a(xa, 0);
+        const BlockCodes<G::NW> b0 = load_codes(0);
+        store_a(xa, lds);
+        dequant_store(lds + G::A_BYTES, b0);
+    }
+    if constexpr (G::DEPTH == 2) {
+        load_a(xb, steps > 1 ? 1 : 0);
+        wcur = load_codes(steps > 1 ? 1 : 0);
+    } else {
+        // the loop's own request order (codes of a step, then the A tile of the step
+        // before it), so that its waits need no slack for a different order
+        wcur = load_codes(steps > 1 ? 1 : 0);
+        load_a(xa, steps > 1 ? 1 : 0);
+    }
+    __syncthreads();
+
+    if constexpr (G::DEPTH == 2) {
+        int64_t it = 0;
+        for (; it + 1 < steps; it += 2) {
+            step_body(it, xa, xb);
+            step_body(it + 1, xb, xa);
+        }
+        if (it < steps) step_body(it, xa, xb);
+    } else {
+        for (int64_t it = 0; it < steps; ++it) step_body(it, xa, xa);
+    }
 
     // ---- rank-r adapter term, staged through stage 0 in rank chunks of 64 ----
     //   forward : acc += (s T) B^T   (A operand s*T [M x r], B operand rows of B [N x r])
@@ -347,24 +393,26 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     const int rr = u.split <= 0 ? a.r : 0;
     for (int rc = 0; rc < rr; rc += 64) {
         uint8_t* sR = lds;
-        uint8_t* sL = lds + FA_BYTES;
+        uint8_t* sL = lds + G::A_BYTES;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < TM * 8 / 256; ++i) {
             const int qi = tid + 256 * i;
-            {
-                const int row = qi >> 3, c = qi & 7;
-                const int col = rc + 8 * c;
-                const int64_t gm = m0 + row;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (col < a.r && gm < a.M) v = *reinterpret_cast<const uint4*>(a.Rk + gm * a.r + col);
-                *reinterpret_cast<uint4*>(sR + tile_off(row, c)) = v;
-            }
+            const int row = qi >> 3, c = qi & 7;
+            const int col = rc + 8 * c;
+            const int64_t gm = m0 + row;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (col < a.r && gm < a.M) v = *reinterpret_cast<const uint4*>(a.Rk + gm * a.r + col);
+            *reinterpret_cast<uint4*>(sR + tile_off(row, c)) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < TN * 8 / 256; ++i) {
+            const int qi = tid + 256 * i;
             if constexpr (BWD) {
-                const int j = qi >> 5, c = qi & 31;          // rank row j, 8 features per chunk
+                const int j = qi / (TN / 8), c = qi % (TN / 8);   // rank row j, 8 features per chunk
                 const int64_t gk = c0 + 8 * c;
                 uint4 v = make_uint4(0, 0, 0, 0);
                 if (rc + j < a.r && gk < a.K) v = *reinterpret_cast<const uint4*>(a.Lr + (int64_t)(rc + j) * a.K + gk);
-                *reinterpret_cast<uint4*>(sL + wt_off(j, 8 * c)) = v;
+                *reinterpret_cast<uint4*>(sL + wt_off<TN>(j, 8 * c)) = v;
             } else {
                 const int row = qi >> 3, c = qi & 7;
                 const int col = rc + 8 * c;
@@ -380,7 +428,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         __syncthreads();
     }
 
-    // ---- piece of a split tile: fp32 partial tile, row-major 256 x 256, summed later ----
+    // ---- piece of a split tile: fp32 partial tile, row-major TM x TN, summed later ----
     if (u.split >= 0) {
         float* slot = a.spart + (u.tail * a.S + u.split) * (int64_t)TILE_FLOATS;
 #pragma unroll
@@ -391,7 +439,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
 #pragma unroll
                 for (int reg = 0; reg < 16; ++reg) {
                     const int row = wm * 128 + i * 32 + 8 * (reg >> 2) + 4 * (lane >> 5) + (reg & 3);
-                    slot[row * FT + col] = acc[i][j][reg];
+                    slot[row * TN + col] = acc[i][j][reg];
                 }
             }
         return;
@@ -418,16 +466,18 @@ FusedEvents& fused_events() {
 }
 
 // Sum of the S fp32 partial tiles of every split tail tile, in piece order, to bf16.
-// Workgroup (slot t, band b): rows 8b..8b+7 of the tile, 8 columns per lane.
+// Workgroup (slot t, part b) of a TM x TN tile: 256 runs of 8 columns, row-major.
+template <int TN>
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ spart, int S, int64_t M,
                                                       int64_t ncols, int64_t tiles_m, int64_t tiles_n,
                                                       uint16_t* __restrict__ out) {
+    constexpr int TM = TILE_FLOATS / TN;
     const int64_t t = blockIdx.x >> 5;
     int64_t tm, tn;
     if (!tail_tile(t, tiles_m, tiles_n, tm, tn)) return;
-    const int row = ((blockIdx.x & 31) << 3) + (threadIdx.x >> 5);
-    const int col = (threadIdx.x & 31) << 3;
-    const float* p = spart + t * S * (int64_t)TILE_FLOATS + row * FT + col;
+    const int q = ((blockIdx.x & 31) << 8) + threadIdx.x;      // run of 8 floats in the tile
+    const int row = q / (TN / 8), col = (q % (TN / 8)) * 8;
+    const float* p = spart + t * S * (int64_t)TILE_FLOATS + row * TN + col;
     float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
     for (int pc = 1; pc < S; ++pc) {
         const float4 l2 = *reinterpret_cast<const float4*>(p + pc * (int64_t)TILE_FLOATS);
@@ -435,7 +485,7 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
         lo.x += l2.x; lo.y += l2.y; lo.z += l2.z; lo.w += l2.w;
         hi.x += h2.x; hi.y += h2.y; hi.z += h2.z; hi.w += h2.w;
     }
-    const int64_t grow = tm * FT + row, gcol = tn * FT + col;
+    const int64_t grow = tm * TM + row, gcol = tn * TN + col;
     if (grow >= M || gcol >= ncols) return;
     const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     uint16_t* o = out + grow * ncols + gcol;
@@ -454,10 +504,12 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
 template <bool BWD>
 static hipError_t launch_fused(FusedArgs fa, int64_t ncols, int64_t steps, void* split_ws,
                                const Nf4Table& tab, hipStream_t st) {
+    constexpr int TM = FUSED_TM, TN = FUSED_TN;
+    using G = FusedTile<TM, TN>;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_fused<BWD>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, FLDS);
+        hipError_t e = hipFuncSetAttribute((const void*)k_fused<BWD, TM, TN>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
@@ -468,11 +520,11 @@ static hipError_t launch_fused(FusedArgs fa, int64_t ncols, int64_t steps, void*
     if (p.S > 1 && !split_ws) return hipErrorInvalidValue;
     // the profiling events cover the product and, for split tail tiles, their sum
     return with_events(st, [&] {
-        hipLaunchKernelGGL(k_fused<BWD>, dim3((unsigned)p.grid), dim3(256), FLDS, st, fa, tab);
+        hipLaunchKernelGGL((k_fused<BWD, TM, TN>), dim3((unsigned)p.grid), dim3(256), G::LDS, st, fa, tab);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.S == 1) return e;
-        hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)(p.tails * 32)), dim3(256), 0, st, fa.spart, p.S,
-                           fa.M, ncols, (fa.M + FT - 1) / FT, (ncols + FT - 1) / FT, fa.out);
+        hipLaunchKernelGGL(k_split_reduce<TN>, dim3((unsigned)(p.tails * 32)), dim3(256), 0, st, fa.spart, p.S,
+                           fa.M, ncols, (fa.M + TM - 1) / TM, (ncols + TN - 1) / TN, fa.out);
         return hipGetLastError();
     });
 }

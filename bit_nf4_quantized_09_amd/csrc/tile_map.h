@@ -13,8 +13,9 @@
 
 namespace nf4 {
 
-constexpr int FT = 256;                 // output tile edge (tokens x features)
-constexpr int TILE_FLOATS = FT * FT;
+constexpr int FUSED_TM = 512;           // output tile: tokens
+constexpr int FUSED_TN = 128;           //              x features
+constexpr int TILE_FLOATS = 65536;      // TM x TN of every tile shape
 constexpr int XCDS = 8;                 // accelerator complex dies, each with its own L2
 constexpr int XCD_CUS = 32;             // compute units per XCD (256 / 8)
 constexpr int GROUP_M = 4;              // token tiles per group of the tile order
@@ -30,13 +31,14 @@ struct FusedPlan {
     size_t bytes;             // split workspace (0 when S == 1)
 };
 
-// Launch over an M x ncols output in 256 x 256 tiles with `steps` 64-deep contraction
+// Launch over an M x ncols output in tm x tn tiles with `steps` 64-deep contraction
 // steps.  One workgroup fills a compute unit, so an XCD runs its tiles in waves of
 // XCD_CUS; when the last wave of the fuller XCDs is at most half full, each of its
 // tiles is cut into S = min(4, XCD_CUS / tail) pieces (every piece non-empty).
-__host__ __device__ __forceinline__ FusedPlan fused_plan(int64_t M, int64_t ncols, int64_t steps) {
+__host__ __device__ __forceinline__ FusedPlan fused_plan(int64_t M, int64_t ncols, int64_t steps,
+                                                         int tm = FUSED_TM, int tn = FUSED_TN) {
     FusedPlan p{1, steps, 0, 0, 0};
-    const int64_t T = ((ncols + FT - 1) / FT) * ((M + FT - 1) / FT);
+    const int64_t T = ((ncols + tn - 1) / tn) * ((M + tm - 1) / tm);
     p.grid = T;
     if (T == 0 || steps < 2) return p;
     const int64_t q = T / XCDS, rem = T % XCDS;

@@ -15,9 +15,9 @@
 
 using namespace nf4;
 
-static int check(int64_t M, int64_t ncols, int64_t steps) {
-    const FusedPlan p = fused_plan(M, ncols, steps);
-    const int64_t tm_n = (M + FT - 1) / FT, tn_n = (ncols + FT - 1) / FT, T = tm_n * tn_n;
+static int check(int64_t M, int64_t ncols, int64_t steps, int TM, int TN) {
+    const FusedPlan p = fused_plan(M, ncols, steps, TM, TN);
+    const int64_t tm_n = (M + TM - 1) / TM, tn_n = (ncols + TN - 1) / TN, T = tm_n * tn_n;
     if (p.S < 1 || p.S > MAX_SPLIT) return 1;
     if (p.S == 1 && (p.grid != T || p.bytes != 0)) return 2;
     if (p.S > 1 && p.bytes != (size_t)(p.tails * p.S) * TILE_FLOATS * 4) return 3;
@@ -92,19 +92,21 @@ int main() {
     for (int64_t M : Ms)
         for (int64_t N : Ns)
             for (int64_t S : Ss) {
-                ++shapes;
-                const int e = check(M, N, S);
-                if (e) {
-                    ++bad;
-                    if (bad < 10) std::printf("# M=%lld ncols=%lld steps=%lld code %d\n", (long long)M,
-                                              (long long)N, (long long)S, e);
+                for (int shape = 0; shape < 2; ++shape) {
+                    ++shapes;
+                    const int e = shape ? check(M, N, S, 512, 128) : check(M, N, S, 256, 256);
+                    if (e) {
+                        ++bad;
+                        if (bad < 10) std::printf("# M=%lld ncols=%lld steps=%lld shape %d code %d\n",
+                                                  (long long)M, (long long)N, (long long)S, shape, e);
+                    }
                 }
             }
     // every tile count up to 600 (one token tile), with a few step counts
     for (int64_t T = 1; T <= 600; ++T)
         for (int64_t S : {2, 3, 9, 128}) {
             ++shapes;
-            const int e = check(FT, T * FT, S);
+            const int e = check(FUSED_TM, T * FUSED_TN, S, FUSED_TM, FUSED_TN);
             if (e) {
                 ++bad;
                 if (bad < 10) std::printf("# tiles=%lld steps=%lld code %d\n", (long long)T, (long long)S, e);
