@@ -179,7 +179,7 @@ def summarize_pmc(fetch_csv, write_csv):
     def pick(table, pred):
         return [v for (d, k), v in sorted(table.items()) if pred(k or "")]
 
-    is_fused = lambda k: "k_fused<false>" in k or "k_fusedILb0E" in k
+    is_fused = lambda k: "k_fused<false" in k or "k_fusedILb0E" in k
     is_copy = lambda k: "copy" in k.lower()
     fc, wc = pick(fetch, is_copy), pick(write, is_copy)
     ff, wf = pick(fetch, is_fused), pick(write, is_fused)
