@@ -12,6 +12,7 @@
 // permutes).  The contraction is split across workgroups so that the grid
 // fills the chip; a second pass sums the fp32 slices in a fixed order, so the
 // result is deterministic.
+#include "bufio.h"
 #include "launch.h"
 
 namespace nf4 {
@@ -45,115 +46,166 @@ __device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8]) {
     }
 }
 
-// Operand staging into an LDS tile [ROWS][64 contraction] for one chunk.
-//   TRANS == false: element (i, p) at src[i * ld + p]   (16-byte chunks along p)
-//   TRANS == true : element (i, p) at src[p * ld + i]   (8 x 8 blocks, transposed in registers)
-// `slot` numbers this thread's share: slots [0, NSLOT) of a tile are spread over the
-// workgroup; a thread owns at most one transposed block or CPT contiguous chunks.
-template <int ROWS, bool TRANS>
-struct Stager {
-    static constexpr int NBLK = (ROWS / 8) * 8;          // 8x8 blocks per tile (transposed)
-    static constexpr int CPT = ROWS * 8 / 256;           // 16-byte chunks per thread (direct)
-    uint4 r[TRANS ? 8 : CPT];
+// Operand staging.  Each LDS stage holds the A tile [128 rows][64 contraction] and the
+// B tile [64 cols][64 contraction] of one contraction chunk:
+//   direct operand    : element (i, p) at src[i * ld + p]  (16-byte pieces along p)
+//   transposed operand: element (i, p) at src[p * ld + i]  (8 x 8 blocks, one contraction
+//                       row per piece, transposed in registers with byte permutes)
+// A thread stages up to 8 pieces of one chunk, all of one operand except in the
+// all-direct case; which pieces is fixed per wave:
+//   A T, B T : waves 0-1 one A block each, wave 2 one B block each, wave 3 none
+//   A D, B T : waves 0-2 A pieces tid + 192 t (t < 6), wave 3 one B block each
+//   A T, B D : waves 0-1 one A block each, waves 2-3 B pieces (tid - 128) + 128 t (t < 4)
+//   A D, B D : every thread A pieces tid + 256 t (t < 4) and B pieces tid + 256 (t - 4)
+// A piece's byte offset is the same for every chunk: the chunk moves the descriptor
+// instead (direct: src + r0 * ld + p0, transposed: src + p0 * ld + r0, with r0 the tile's
+// first row and p0 the chunk's first contraction index).  Pieces the thread does not own,
+// or whose rows lie past the operand, get an offset past any descriptor range and read
+// zero; so do pieces past the contraction end P, tested per chunk (direct pieces never
+// straddle P, which is a multiple of 8 for them).  The loads are straight-line code.
+constexpr uint32_t SK_OOB = 0x80000000u;
 
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t ld, int64_t rows,
-                                         int64_t P, int64_t i0, int64_t p0, int slot) {
-        if constexpr (TRANS) {
-            if (slot < NBLK) {
-                const int rb = slot >> 3, pb = slot & 7;
-                const int64_t gi = i0 + rb * 8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int64_t gp = p0 + pb * 8 + e;
-                    r[e] = (gp < P && gi < rows) ? *reinterpret_cast<const uint4*>(src + gp * ld + gi)
-                                                 : make_uint4(0, 0, 0, 0);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < CPT; ++t) {
-                const int q = slot + 256 * t;
-                const int a = q >> 3, c = q & 7;
-                const int64_t gi = i0 + a, gp = p0 + 8 * c;
-                r[t] = (gi < rows && gp < P) ? *reinterpret_cast<const uint4*>(src + gi * ld + gp)
-                                             : make_uint4(0, 0, 0, 0);
-            }
-        }
-    }
-    __device__ __forceinline__ void store(uint8_t* sm, int slot) {
-        if constexpr (TRANS) {
-            if (slot < NBLK) {
-                const int rb = slot >> 3, pb = slot & 7;
-                uint4 t[8];
-                transpose8x8(r, t);
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<uint4*>(sm + lds_off(rb * 8 + j, pb)) = t[j];
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < CPT; ++t) {
-                const int q = slot + 256 * t;
-                *reinterpret_cast<uint4*>(sm + lds_off(q >> 3, q & 7)) = r[t];
-            }
-        }
-    }
+template <bool ATR, bool BTR>
+struct SkStage {
+    static constexpr int NR = (!ATR && !BTR) ? 6 : 8;
+    uint4 r[NR];
 };
 
 // Partial C[i][j] = sum over this workgroup's contraction slice of Aop[i][p] * Bop[p][j],
 // written as fp32 to part[z][i][j].  Grid: (col tiles, row tiles, slices).
+//
+// Three register sets of staged chunks: chunk c+3 is requested during step c and
+// written to LDS at the start of step c+2, so every request has two steps to arrive.
 template <bool ATR, bool BTR>
 __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ A,
                                                 const uint16_t* __restrict__ B, int64_t Mc,
                                                 int64_t Nc, int64_t P, int64_t chunks_per_slice,
                                                 float* __restrict__ part) {
+    using St = SkStage<ATR, BTR>;
+    constexpr int NR = St::NR;
+    constexpr bool DD = !ATR && !BTR;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SK_STAGE];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t i0 = (int64_t)blockIdx.y * SK_BM, j0 = (int64_t)blockIdx.x * SK_BN;
     const int64_t nchunks = (P + SK_PC - 1) / SK_PC;
     const int64_t c0 = (int64_t)blockIdx.z * chunks_per_slice;
     const int64_t c1 = (c0 + chunks_per_slice < nchunks) ? c0 + chunks_per_slice : nchunks;
     const int64_t lda = ATR ? Mc : P;
     const int64_t ldb = BTR ? Nc : P;
-    // thread roles: transposed A uses slots 0..127, transposed B slots 128..191
-    const int aslot = tid;
-    const int bslot = ATR ? tid - 128 : tid;
 
-    Stager<SK_BM, ATR> sa;
-    Stager<SK_BN, BTR> sb;
-    f32x16 acc0 = {}, acc1 = {};
-
-    auto load = [&](int64_t c) {
-        sa.load(A, lda, Mc, P, i0, c * SK_PC, aslot);
-        if (!BTR || bslot >= 0) sb.load(B, ldb, Nc, P, j0, c * SK_PC, BTR ? bslot : tid);
+    // this wave's operand and layout (wave-uniform); B in the all-direct case is pieces 4-5
+    const bool a_wave = DD || (ATR ? wave < 2 : (BTR ? wave < 3 : true));
+    const bool b_wave = !DD && (ATR ? (wave >= 2 && (!BTR || wave == 2)) : wave == 3);
+    const bool w_trans = a_wave ? ATR : BTR;
+    // piece t: tile row (direct) or 8-row group start (transposed), contraction index in chunk
+    auto piece_row = [&](int t) -> int {
+        if constexpr (DD) return (tid >> 3) + 32 * (t & 3);
+        if (w_trans) return (((a_wave ? tid : tid - (ATR ? 128 : 192)) >> 3) & 15) * 8;
+        return a_wave ? (tid + 192 * t) >> 3 : ((tid - 128) + 128 * t) >> 3;
     };
-    auto store = [&](int stage) {
-        uint8_t* base = lds + stage * SK_STAGE;
-        sa.store(base, aslot);
-        if (!BTR || bslot >= 0) sb.store(base + SK_A_BYTES, BTR ? bslot : tid);
+    auto piece_pc = [&](int t) -> int { return 8 * (tid & 7) + ((!DD && w_trans) ? t : 0); };
+    auto piece_own = [&](int t) -> bool {
+        if constexpr (DD) return t < 4 || (tid >> 3) + 32 * (t - 4) < SK_BN;
+        if (!a_wave && !b_wave) return false;
+        if (w_trans) return true;
+        return a_wave ? (t < 6 && tid + 192 * t < SK_BM * 8) : t < 4;
     };
-
-    if (c0 < c1) {
-        load(c0);
-        store(0);
-        __syncthreads();
-        for (int64_t c = c0; c < c1; ++c) {
-            const int stage = (int)((c - c0) & 1);
-            if (c + 1 < c1) load(c + 1);
-            const uint8_t* sA = lds + stage * SK_STAGE;
-            const uint8_t* sB = sA + SK_A_BYTES;
+    uint32_t off[NR];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int ch = 2 * s + (lane >> 5);
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sA + lds_off(wave * 32 + (lane & 31), ch));
-                const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(sB + lds_off(lane & 31, ch));
-                const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(sB + lds_off(32 + (lane & 31), ch));
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
-            }
-            if (c + 1 < c1) store(stage ^ 1);
-            __syncthreads();
+    for (int t = 0; t < NR; ++t) {
+        const bool ob = DD ? t >= 4 : !a_wave;
+        const int64_t rows = ob ? Nc : Mc, r0 = ob ? j0 : i0, ld = ob ? ldb : lda;
+        const int row = piece_row(t), pc = piece_pc(t);
+        const bool tr = DD ? false : w_trans;
+        const bool ok = piece_own(t) && r0 + row < rows;
+        off[t] = ok ? (uint32_t)(tr ? ((int64_t)pc * ld + row) * 2 : ((int64_t)row * ld + pc) * 2) : SK_OOB;
+    }
+    auto rsrc_at = [&](const uint16_t* src, bool tr, int64_t ld, int64_t rows, int64_t r0, int64_t nmax,
+                       int64_t p0) {
+        if (tr) return make_rsrc(src + p0 * ld + r0, (P - p0) * ld * 2 - r0 * 2);
+        const int64_t nr = rows - r0 < nmax ? rows - r0 : nmax;
+        return make_rsrc(src + r0 * ld + p0, (nr * ld - p0) * 2);
+    };
+    auto load = [&](St& S, int64_t c) {
+        const int64_t cc = c < c1 ? c : c1 - 1;            // past the slice: a repeat, never used
+        const int64_t p0 = cc * SK_PC;
+        const int rem = (int)(P - p0 < SK_PC ? P - p0 : SK_PC);
+        const __amdgpu_buffer_rsrc_t ra = rsrc_at(A, ATR, lda, Mc, i0, SK_BM, p0);
+        const __amdgpu_buffer_rsrc_t rb = rsrc_at(B, BTR, ldb, Nc, j0, SK_BN, p0);
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            const bool ob = DD ? t >= 4 : !a_wave;
+            const uint32_t o = piece_pc(t) < rem ? off[t] : SK_OOB;
+            S.r[t] = buf_load16(ob ? rb : ra, o, 0);
         }
+    };
+    auto store = [&](const St& S, int stage) {
+        uint8_t* sA = lds + stage * SK_STAGE;
+        uint8_t* sB = sA + SK_A_BYTES;
+        if constexpr (DD) {
+#pragma unroll
+            for (int t = 0; t < NR; ++t) {
+                if (piece_own(t))
+                    *reinterpret_cast<uint4*>((t < 4 ? sA : sB) + lds_off(piece_row(t), tid & 7)) = S.r[t];
+            }
+        } else {
+            if (!a_wave && !b_wave) return;
+            uint8_t* dst = a_wave ? sA : sB;
+            if (w_trans) {
+                const int rb = piece_row(0);
+                uint4 tr[8];
+                transpose8x8(S.r, tr);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    *reinterpret_cast<uint4*>(dst + lds_off(rb + j, tid & 7)) = tr[j];
+            } else {
+#pragma unroll
+                for (int t = 0; t < 6; ++t)
+                    if (piece_own(t))
+                        *reinterpret_cast<uint4*>(dst + lds_off(piece_row(t), tid & 7)) = S.r[t];
+            }
+        }
+    };
+    f32x16 acc0 = {}, acc1 = {};
+    auto compute = [&](int stage) {
+        const uint8_t* sA = lds + stage * SK_STAGE;
+        const uint8_t* sB = sA + SK_A_BYTES;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int ch = 2 * s + (lane >> 5);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(sA + lds_off(wave * 32 + (lane & 31), ch));
+            const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(sB + lds_off(lane & 31, ch));
+            const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(sB + lds_off(32 + (lane & 31), ch));
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
+        }
+    };
+    St s0, s1, s2;
+    // step k (chunk c0 + k) with register sets cur (chunk k's, already in LDS) and nx (chunk
+    // k+1's): write nx to the free stage, request chunk k+3 into cur, multiply stage k & 1
+    auto step = [&](int64_t k, St& cur, const St& nx) {
+        store(nx, (int)((k + 1) & 1));
+        load(cur, c0 + k + 3);
+        compute((int)(k & 1));
+        __syncthreads();
+    };
+
+    const int64_t n = c1 - c0;
+    if (n > 0) {
+        load(s0, c0);
+        store(s0, 0);
+        load(s1, c0 + 1);
+        load(s2, c0 + 2);
+        __syncthreads();
+        int64_t k = 0;
+        for (; k + 3 <= n; k += 3) {
+            step(k, s0, s1);
+            step(k + 1, s1, s2);
+            step(k + 2, s2, s0);
+        }
+        if (k < n) step(k, s0, s1);
+        if (k + 1 < n) step(k + 1, s1, s2);
     }
     float* out = part + (int64_t)blockIdx.z * Mc * Nc;
 #pragma unroll
@@ -174,16 +226,29 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
                                                        void* __restrict__ C, bool c_f32,
                                                        bool c_trans, uint16_t* __restrict__ C2,
                                                        float scale2) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = Mc * Nc;
-    if (i >= total) return;
-    float v = 0.0f;
-    for (int z = 0; z < S; ++z) v += part[(int64_t)z * total + i];
-    const int64_t row = i / Nc, col = i - row * Nc;
-    const int64_t dst = c_trans ? col * Mc + row : i;
-    if (c_f32) reinterpret_cast<float*>(C)[dst] = v * scale;
-    else reinterpret_cast<uint16_t*>(C)[dst] = f32_to_bf16(v * scale);
-    if (C2) C2[dst] = f32_to_bf16(v * scale2);
+    const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i4 >= total) return;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (i4 + 4 <= total) {
+        for (int z = 0; z < S; ++z) {
+            const float4 p = *reinterpret_cast<const float4*>(part + (int64_t)z * total + i4);
+            v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+        }
+    } else {
+        for (int z = 0; z < S; ++z)
+            for (int e = 0; e < 4; ++e)
+                if (i4 + e < total) v[e] += part[(int64_t)z * total + i4 + e];
+    }
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = i4 + e;
+        if (i >= total) break;
+        const int64_t row = i / Nc, col = i - row * Nc;
+        const int64_t dst = c_trans ? col * Mc + row : i;
+        if (c_f32) reinterpret_cast<float*>(C)[dst] = v[e] * scale;
+        else reinterpret_cast<uint16_t*>(C)[dst] = f32_to_bf16(v[e] * scale);
+        if (C2) C2[dst] = f32_to_bf16(v[e] * scale2);
+    }
 }
 
 void skinny_plan(int64_t Mc, int64_t Nc, int64_t P, int* slices, int64_t* chunks_per_slice) {
@@ -194,7 +259,9 @@ void skinny_plan(int64_t Mc, int64_t Nc, int64_t P, int* slices, int64_t* chunks
         *chunks_per_slice = 0;
         return;
     }
-    int64_t S = (512 + tiles - 1) / tiles;
+    // about one workgroup per CU: more slices would add fp32 partial traffic (S times the
+    // output, written once and read once) faster than they add bandwidth
+    int64_t S = (256 + tiles - 1) / tiles;
     const int64_t smax = nchunks / 4 > 1 ? nchunks / 4 : 1;
     if (S > smax) S = smax;
     if (S < 1) S = 1;
@@ -215,6 +282,11 @@ hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, 
                             int64_t Mc, int64_t Nc, int64_t P, float* part, float scale, void* C,
                             bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s) {
     if (Mc == 0 || Nc == 0) return hipSuccess;
+    // per-lane buffer offsets are 32-bit: a direct operand spans 128 rows of its leading
+    // dimension P, a transposed one 64 contraction rows of its leading dimension
+    if ((!a_trans || !b_trans) && P >= ((int64_t)1 << 22)) return hipErrorInvalidValue;
+    if ((a_trans && Mc >= ((int64_t)1 << 23)) || (b_trans && Nc >= ((int64_t)1 << 23)))
+        return hipErrorInvalidValue;
     int S;
     int64_t cps;
     skinny_plan(Mc, Nc, P, &S, &cps);
@@ -230,7 +302,7 @@ hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = Mc * Nc;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, S,
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((total + 1023) / 1024)), dim3(256), 0, s, part, S,
                        Mc, Nc, scale, C, c_f32, c_trans, C2, scale2);
     return hipGetLastError();
 }
