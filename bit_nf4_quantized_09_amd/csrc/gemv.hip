@@ -14,8 +14,9 @@ namespace nf4 {
 // Few-token forward (M <= 16): an HBM-bound stream over the packed weight, in two
 // launches.
 //
-// k_gemv_part<RB, MT>: workgroup (contraction slice, row group) = 64 rows x RB NF4
-// blocks; wave w owns rows 16w..16w+15.  The slice's token inputs X[0:MT, slice]
+// k_gemv_part<RB, MT>: workgroup (contraction slice, row group) = 64 rows (MT = 4) or
+// 128 rows (MT = 16) x RB NF4 blocks; wave w owns one or two tiles of 16 consecutive
+// rows.  The slice's token inputs X[0:MT, slice]
 // (MT = 4 or 16 staged token rows, rows past M reading zero) are staged once into
 // LDS, rows padded by 16 bytes for the banks.  Every wave then requests all of its
 // codes at once, so the whole slice is in flight and no later request waits behind an
@@ -32,7 +33,8 @@ namespace nf4 {
 // inputs of the same contraction indices from LDS, give the block's partial dot
 // products, which the block's decoded constant c1' scales into the fp32 accumulator.
 // Levels come from a 256-entry LDS table that maps one code byte to its two bf16
-// levels; c1' from an E4M3 table, the row's 8-bit constants (one aligned window) and
+// levels, held in 16 copies so that lanes with different bytes mostly read different
+// banks; c1' from an E4M3 table, the row's 8-bit constants (one aligned window) and
 // at most two second-level steps per row and slice.  Row groups past the weight run
 // the adapter rows A (bf16, no scale): partial sums of T = X A^T from the same pass.
 // Partial sums go to part[slice][token][row] (rows N.. hold T).
@@ -72,35 +74,49 @@ struct GvArgs {
     uint16_t* T;             // [M x r]
 };
 
-// Four code bytes (8 codes) -> the MFMA operand of their 8 unscaled bf16 levels.
-__device__ __forceinline__ bf16x8v lookup8(const uint32_t* s_pair, uint32_t w) {
-    return __builtin_bit_cast(bf16x8v, make_uint4(s_pair[w & 0xFFu], s_pair[(w >> 8) & 0xFFu],
-                                                  s_pair[(w >> 16) & 0xFFu], s_pair[w >> 24]));
+// Four code bytes (8 codes) -> the MFMA operand of their 8 unscaled bf16 levels.  The
+// table holds CP copies of each entry, copy c of entry b at dword CP b + c; lane l reads
+// copy l % CP (s_lane = table + l % CP), so that the lanes of one LDS cycle mostly read
+// distinct banks whatever their code bytes (all of them for CP = 32).
+template <int CP>
+__device__ __forceinline__ bf16x8v lookup8(const uint32_t* s_lane, uint32_t w) {
+    return __builtin_bit_cast(bf16x8v, make_uint4(s_lane[(w & 0xFFu) * CP], s_lane[((w >> 8) & 0xFFu) * CP],
+                                                  s_lane[((w >> 16) & 0xFFu) * CP], s_lane[(w >> 24) * CP]));
 }
 
 constexpr int GV_WV = 4;                   // waves per workgroup of k_gemv_part
-constexpr int GV_ROWS = 16 * GV_WV;        // weight rows per workgroup (16 per wave)
 constexpr int GV_AROWS = 16;               // adapter rows per workgroup
+// 16-row tiles per wave: with 16 staged tokens two tiles share each input operand read
+// from LDS (the reads cost as much LDS time as the level lookups); with 4, one tile
+// keeps more, smaller workgroups in flight
+constexpr int gv_tiles(int MT) { return MT == 16 ? 2 : 1; }
+constexpr int gv_rows(int MT) { return 16 * gv_tiles(MT) * GV_WV; }   // weight rows per workgroup
+// copies of the level table (16 KB): lane l reads copy l % 16.  32 copies make the lookups
+// conflict-free but cost a workgroup slot per CU, which measured slower.
+constexpr int GV_CP = 16;
 
-// Dynamic LDS of k_gemv_part: staged inputs, adapter partial sums (the level and E4M3
-// tables are static, at fixed addresses, so that a lookup is one shift of a code byte).
-constexpr int gv_lds_bytes(int MT) { return MT * (GV_RB * 128 + 16) + GV_WV * 64 * 16; }
+// Dynamic LDS of k_gemv_part: the staged inputs (the level and E4M3 tables are static, at
+// fixed addresses; adapter workgroups keep their cross-wave sums in the level table's
+// space, which they do not use).
+constexpr int gv_lds_bytes(int MT) { return MT * (GV_RB * 128 + 16); }
 
-// One workgroup of k_gemv_part: GV_ROWS weight rows (ADAPTER false), or GV_AROWS adapter
+// One workgroup of k_gemv_part: gv_rows(MT) weight rows (ADAPTER false), or GV_AROWS adapter
 // rows A (bf16, no scale) whose slice is split among the waves (wave w: blocks
 // w RB/WV ..) and summed across the waves in LDS, so that an adapter workgroup moves
 // about as many bytes as a weight workgroup.  Straight-line code from the first
 // request to the last wait, so that every wait names exactly the requests it needs.
 template <int RB, int MT, bool ADAPTER>
-__device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& tab, int64_t group) {
+__device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& tab, int64_t group,
+                                               uint32_t* s_pair, float* s_e4m3) {
+    constexpr int CP = GV_CP;
     extern __shared__ __attribute__((aligned(16))) uint8_t gv_lds[];
-    __shared__ uint32_t s_pair[256];                   // code byte -> two bf16 levels
-    __shared__ float s_e4m3[256];                      // 8-bit constant -> E4M3 value
     constexpr int NT = 64 * GV_WV;                     // threads
     constexpr int XSTRIDE = RB * 128 + 16;             // bytes per staged token row
     constexpr int RBW = RB / GV_WV;                    // adapter blocks per wave
+    constexpr int TT = ADAPTER ? 1 : gv_tiles(MT);     // row tiles of this wave
+    static_assert(GV_WV * 64 * 16 <= 256 * CP * 4, "adapter sums fit in the table space");
     uint8_t* s_x = gv_lds;                                         // [MT][XSTRIDE] token inputs
-    f32x4* s_red = reinterpret_cast<f32x4*>(s_x + MT * XSTRIDE);   // [WV][64] adapter partials
+    f32x4* s_red = reinterpret_cast<f32x4*>(s_pair);               // [WV][64] adapter partials
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t KB = a.K >> 6;
@@ -108,13 +124,10 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
     const int64_t b0 = slice * RB;                      // first block of the slice
     const int nb = KB - b0 < RB ? (int)(KB - b0) : RB;  // blocks of the slice inside the row
     const int nl = lane & 15, g = lane >> 4;
-    // row of this lane
-    const int64_t n = ADAPTER ? group * GV_AROWS + nl : group * GV_ROWS + 16 * wave + nl;
+    // row of this lane in tile t: n0 + 16 t
+    const int64_t n0 = ADAPTER ? group * GV_AROWS + nl : group * gv_rows(MT) + 16 * TT * wave + nl;
 
     // ---- requests: token inputs of the slice first, then this wave's rows ----
-    // The inputs (MT token rows x RB*8 chunks of 16 bytes; tokens past M and chunks
-    // past the row lie outside the range and read zero) pass through registers into
-    // LDS.  Being requested first, the wait for them leaves the later requests in flight.
     const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(a.X + b0 * 64, (int64_t)a.M * a.K * 2 - b0 * 128);
     constexpr int XCH = MT * RB * 8 / NT;               // chunks per thread
     uint4 xs[XCH];
@@ -124,38 +137,42 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
         const uint32_t vo = (m < a.M && c < nb * 8) ? (uint32_t)((int64_t)m * a.K * 2 + c * 16) : 0x80000000u;
         xs[i] = buf_load16(rs_x, vo, 0);
     }
-    uint4 cw[RB / 2];
-    uint32_t qw[RB / 4 + 1];
+    uint4 cw[TT][RB / 2];
+    uint32_t qw[TT][RB / 4 + 1];
     uint4 al[RBW][2];
-    float mean = 0.0f, c2f = 0.0f, c2l = 0.0f;
-    int64_t g_first = 0;
+    float mean = 0.0f, c2f[TT], c2l[TT];
     if constexpr (!ADAPTER) {
         mean = *a.mean;
         // second-level constants: a row's slice meets at most two 256-blocks
         const int64_t n2 = (a.N * KB + 255) >> 8;
-        const int64_t ci0 = n * KB + b0;
-        g_first = ci0 >> 8;
-        const int64_t gl = (ci0 + nb - 1) >> 8;
-        c2f = a.c2[g_first < n2 ? g_first : n2 - 1];
-        c2l = a.c2[gl < n2 ? gl : n2 - 1];
-        // 8-bit constants of the slice (aligned window), then the codes in block order.
-        // The pair offset goes in the range-checked part of the address: a pair past
-        // the row reads the next row (finite codes, given a zero constant below) or,
-        // past the last row, zero.
         const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(a.qc, a.N * KB);
-        const uint32_t qa = (uint32_t)ci0 & ~3u;
 #pragma unroll
-        for (int i = 0; i < RB / 4 + 1; ++i) qw[i] = buf_load4(rs_q, qa + 4 * i, 0);
+        for (int t = 0; t < TT; ++t) {
+            const int64_t ci0 = (n0 + 16 * t) * KB + b0;
+            const int64_t gf = ci0 >> 8, gl = (ci0 + nb - 1) >> 8;
+            c2f[t] = a.c2[gf < n2 ? gf : n2 - 1];
+            c2l[t] = a.c2[gl < n2 ? gl : n2 - 1];
+            // 8-bit constants of the slice (aligned window); past the last row: zero
+            const uint32_t qa = (uint32_t)ci0 & ~3u;
+#pragma unroll
+            for (int i = 0; i < RB / 4 + 1; ++i) qw[t][i] = buf_load4(rs_q, qa + 4 * i, 0);
+        }
+        // the codes, block pair by block pair (the order they are used in).  A pair past
+        // the row reads the next row (finite codes, given a zero constant below) or, past
+        // the last row, zero.
         const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes, a.N * (a.K >> 1));
-        const uint32_t c_voff = (uint32_t)(n * (a.K >> 1) + b0 * 32 + 16 * g);
+        const uint32_t c_voff = (uint32_t)(n0 * (a.K >> 1) + b0 * 32 + 16 * g);
+        const uint32_t t_step = (uint32_t)(16 * (a.K >> 1));
 #pragma unroll
-        for (int p = 0; p < RB / 2; ++p) cw[p] = buf_load16(rs_codes, c_voff + 64 * p, 0);
+        for (int p = 0; p < RB / 2; ++p)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) cw[t][p] = buf_load16(rs_codes, c_voff + t * t_step + 64 * p, 0);
     } else {
         // this wave's blocks of the adapter rows; lane (n, g) takes contraction indices
         // 16g..16g+15 of each block (block index clamped into the row: the wave-uniform
         // offset is not range-checked; blocks past the row are skipped below)
         const __amdgpu_buffer_rsrc_t rs_al = make_rsrc(a.Al, (int64_t)a.r * a.K * 2);
-        const uint32_t a_voff = n < a.r ? (uint32_t)(n * a.K * 2 + 32 * g) : 0x80000000u;
+        const uint32_t a_voff = n0 < a.r ? (uint32_t)(n0 * a.K * 2 + 32 * g) : 0x80000000u;
 #pragma unroll
         for (int u = 0; u < RBW; ++u) {
             const int64_t j = b0 + wave * RBW + u;
@@ -173,7 +190,14 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
             lo = (tid & 15) == j ? tab.lv[j] : lo;
             hi = (tid >> 4) == j ? tab.lv[j] : hi;
         }
-        s_pair[tid] = pack_bf16x2(lo, hi);
+        if constexpr (!ADAPTER) {
+            // entry tid, all CP copies; the rotation spreads one instruction's lanes over the banks
+            const uint32_t pv = pack_bf16x2(lo, hi);
+            const uint4 p4 = make_uint4(pv, pv, pv, pv);
+#pragma unroll
+            for (int i = 0; i < CP / 4; ++i)
+                *reinterpret_cast<uint4*>(s_pair + tid * CP + 4 * ((tid + i) & (CP / 4 - 1))) = p4;
+        }
         s_e4m3[tid] = e4m3_to_f32((uint32_t)tid);
     }
 #pragma unroll
@@ -186,48 +210,59 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
     // MFMA A operand rows: token m = lane % 16 (rows past MT repeat rows below MT; their
     // outputs are never stored)
     const uint8_t* xtok = s_x + (lane & (MT - 1)) * XSTRIDE;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (!ADAPTER) {
-        const float st_first = c2_step(c2f);
-        const float st_last = c2_step(c2l);
-        const int64_t ci0 = n * KB + b0;                 // constant index of the slice's first block
-        // blocks j >= jsplit of this row's slice belong to the next second-level block
-        const int jsplit = 256 - (int)(ci0 & 255);
-        // the slice's 8-bit constants, realigned: byte j of q4[] is block j's
-        const uint32_t sh = ((uint32_t)ci0 & 3u) * 8;
-        uint32_t q4[RB / 4];
+    const uint32_t* s_lane = s_pair + (lane & (CP - 1));
+    f32x4 acc[TT];
 #pragma unroll
-        for (int i = 0; i < RB / 4; ++i) q4[i] = (uint32_t)__builtin_amdgcn_alignbit(qw[i + 1], qw[i], sh);
+    for (int t = 0; t < TT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!ADAPTER) {
+        float st_first[TT], st_last[TT];
+        int jsplit[TT];
+        uint32_t q4[TT][RB / 4];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            st_first[t] = c2_step(c2f[t]);
+            st_last[t] = c2_step(c2l[t]);
+            const int64_t ci0 = (n0 + 16 * t) * KB + b0;  // constant index of the slice's first block
+            // blocks j >= jsplit of this row's slice belong to the next second-level block
+            jsplit[t] = 256 - (int)(ci0 & 255);
+            // the slice's 8-bit constants, realigned: byte j of q4[] is block j's
+            const uint32_t sh = ((uint32_t)ci0 & 3u) * 8;
+#pragma unroll
+            for (int i = 0; i < RB / 4; ++i) q4[t][i] = (uint32_t)__builtin_amdgcn_alignbit(qw[t][i + 1], qw[t][i], sh);
+        }
         const int kA = 32 * (g & 1) + 16 * (g >> 1);     // first contraction index of the lane
         // valid: blocks past the row contribute zero (a factor, not a branch: the decoded
         // constant of any byte is finite)
-        auto c1_of = [&](int j, bool all_valid) {
-            const uint32_t qbyte = (q4[j / 4] >> (8 * (j & 3))) & 0xFFu;
-            const float c = __fmaf_rn(s_e4m3[qbyte], j < jsplit ? st_first : st_last, mean);
+        auto c1_of = [&](int t, int j, bool all_valid) {
+            const uint32_t qbyte = (q4[t][j / 4] >> (8 * (j & 3))) & 0xFFu;
+            const float c = __fmaf_rn(s_e4m3[qbyte], j < jsplit[t] ? st_first[t] : st_last[t], mean);
             return all_valid ? c : c * (float)(j < nb);
         };
         auto run = [&](bool all_valid) {
 #pragma unroll
             for (int p = 0; p < RB / 2; ++p) {
-                // lanes 0-31: bytes of block 2p, lanes 32-63: block 2p+1 -> both blocks per lane
-                uint32_t x = cw[p].x, y = cw[p].y, z = cw[p].z, w = cw[p].w;
-                const auto xz = __builtin_amdgcn_permlane32_swap(x, z, false, false);
-                const auto yw = __builtin_amdgcn_permlane32_swap(y, w, false, false);
-                x = xz[0]; z = xz[1]; y = yw[0]; w = yw[1];
                 const uint8_t* xa = xtok + (2 * p) * 128 + kA * 2;
                 const uint8_t* xb = xa + 128;
-                f32x4 pa = {0.0f, 0.0f, 0.0f, 0.0f}, pb = {0.0f, 0.0f, 0.0f, 0.0f};
-                pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8v*>(xa),
-                                                             lookup8(s_pair, x), pa, 0, 0, 0);
-                pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8v*>(xa + 16),
-                                                             lookup8(s_pair, y), pa, 0, 0, 0);
-                pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8v*>(xb),
-                                                             lookup8(s_pair, z), pb, 0, 0, 0);
-                pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8v*>(xb + 16),
-                                                             lookup8(s_pair, w), pb, 0, 0, 0);
-                const float ca = c1_of(2 * p, all_valid), cb = c1_of(2 * p + 1, all_valid);
+                const bf16x8v xa0 = *reinterpret_cast<const bf16x8v*>(xa);
+                const bf16x8v xa1 = *reinterpret_cast<const bf16x8v*>(xa + 16);
+                const bf16x8v xb0 = *reinterpret_cast<const bf16x8v*>(xb);
+                const bf16x8v xb1 = *reinterpret_cast<const bf16x8v*>(xb + 16);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = __fmaf_rn(cb, pb[i], __fmaf_rn(ca, pa[i], acc[i]));
+                for (int t = 0; t < TT; ++t) {
+                    // lanes 0-31: bytes of block 2p, lanes 32-63: block 2p+1 -> both blocks per lane
+                    uint32_t x = cw[t][p].x, y = cw[t][p].y, z = cw[t][p].z, w = cw[t][p].w;
+                    const auto xz = __builtin_amdgcn_permlane32_swap(x, z, false, false);
+                    const auto yw = __builtin_amdgcn_permlane32_swap(y, w, false, false);
+                    x = xz[0]; z = xz[1]; y = yw[0]; w = yw[1];
+                    f32x4 pa = {0.0f, 0.0f, 0.0f, 0.0f}, pb = {0.0f, 0.0f, 0.0f, 0.0f};
+                    pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0, lookup8<CP>(s_lane, x), pa, 0, 0, 0);
+                    pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa1, lookup8<CP>(s_lane, y), pa, 0, 0, 0);
+                    pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb0, lookup8<CP>(s_lane, z), pb, 0, 0, 0);
+                    pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb1, lookup8<CP>(s_lane, w), pb, 0, 0, 0);
+                    const float ca = c1_of(t, 2 * p, all_valid), cb = c1_of(t, 2 * p + 1, all_valid);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[t][i] = __fmaf_rn(cb, pb[i], __fmaf_rn(ca, pa[i], acc[t][i]));
+                }
             }
         };
         // a whole slice (all but a row's last), or the last, with blocks past the row
@@ -241,29 +276,33 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
             if (j < nb) {
                 const bf16x8v x0 = *reinterpret_cast<const bf16x8v*>(xrow + j * 128);
                 const bf16x8v x1 = *reinterpret_cast<const bf16x8v*>(xrow + j * 128 + 16);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, __builtin_bit_cast(bf16x8v, al[u][0]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, __builtin_bit_cast(bf16x8v, al[u][1]), acc, 0, 0, 0);
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, __builtin_bit_cast(bf16x8v, al[u][0]), acc[0], 0, 0, 0);
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, __builtin_bit_cast(bf16x8v, al[u][1]), acc[0], 0, 0, 0);
             }
         }
         // sum over the waves, in wave order
-        s_red[wave * 64 + lane] = acc;
+        s_red[wave * 64 + lane] = acc[0];
         __syncthreads();
         if (wave != 0) return;
-        acc = s_red[lane];
+        acc[0] = s_red[lane];
 #pragma unroll
         for (int w = 1; w < GV_WV; ++w) {
             const f32x4 v = s_red[w * 64 + lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] += v[i];
+            for (int i = 0; i < 4; ++i) acc[0][i] += v[i];
         }
     }
     // lane holds tokens 4g..4g+3 of row n
     const int64_t nrows = ADAPTER ? a.r : a.N;
-    if (n < nrows) {
-        const int64_t col = ADAPTER ? a.N + n : n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * g + i < a.M) a.part[(slice * a.M + 4 * g + i) * (a.N + a.r) + col] = acc[i];
+    for (int t = 0; t < TT; ++t) {
+        const int64_t n = n0 + 16 * t;
+        if (n < nrows) {
+            const int64_t col = ADAPTER ? a.N + n : n;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * g + i < a.M) a.part[(slice * a.M + 4 * g + i) * (a.N + a.r) + col] = acc[t][i];
+        }
     }
 }
 
@@ -271,11 +310,13 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
 // workgroups in flight read whole rows of codes (long runs within one DRAM page);
 // the adapter row groups come first.
 template <int RB, int MT>
-__global__ __launch_bounds__(64 * GV_WV) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(64 * GV_WV) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void k_gemv_part(GvArgs a, Nf4Table tab) {
+    __shared__ __attribute__((aligned(16))) uint32_t s_pair[256 * GV_CP];   // code byte -> two bf16 levels
+    __shared__ float s_e4m3[256];                      // 8-bit constant -> E4M3 value
     const int64_t nag = (a.r + GV_AROWS - 1) / GV_AROWS;
-    if ((int64_t)blockIdx.y < nag) gemv_part_body<RB, MT, true>(a, tab, blockIdx.y);
-    else gemv_part_body<RB, MT, false>(a, tab, (int64_t)blockIdx.y - nag);
+    if ((int64_t)blockIdx.y < nag) gemv_part_body<RB, MT, true>(a, tab, blockIdx.y, s_pair, s_e4m3);
+    else gemv_part_body<RB, MT, false>(a, tab, (int64_t)blockIdx.y - nag, s_pair, s_e4m3);
 }
 
 // k_gemv_reduce<ROWS, NO, NT>: workgroup of ROWS weight rows; thread (row n = n0 + tid %
@@ -382,10 +423,11 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
     if (M == 0) return hipSuccess;
     const int64_t slices = gemv_slices(M, W.cols);
     GvArgs ga{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, X, (int)M, Al, Bl, r, s, part, Y, T};
-    dim3 g1((unsigned)slices, (unsigned)((r + GV_AROWS - 1) / GV_AROWS + (W.rows + GV_ROWS - 1) / GV_ROWS));
+    const bool small = M <= 4;
+    const int64_t wrows = small ? gv_rows(4) : gv_rows(16);
+    dim3 g1((unsigned)slices, (unsigned)((r + GV_AROWS - 1) / GV_AROWS + (W.rows + wrows - 1) / wrows));
     // reduce: 32 rows x 8 token groups (one output per thread) for up to 4 tokens,
     // 64 rows x 4 token groups (four outputs) above
-    const bool small = M <= 4;
     const int64_t rrows = small ? 32 : 64;
     dim3 g2((unsigned)((W.rows + rrows - 1) / rrows > 0 ? (W.rows + rrows - 1) / rrows : 1));
     return with_events(st, [&] {
