@@ -49,6 +49,9 @@ def _load():
                                          ctypes.c_double, _i64p, _i64, _f64p, _f64p]
     lib.orc_qlora_linear_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _i64, _i64, _i64,
                                          _i64, ctypes.c_double, _i64p, _i64, _f64p, _f64p, _f64p]
+    _d = ctypes.c_double
+    lib.orc_adamw_step.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _d, _d, _d, _d, _d, _i64,
+                                   _f64p, _f64p, _f64p]
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_pairwise_sum.restype = ctypes.c_double
     lib.orc_pairwise_sum.argtypes = [_f32p, _i64]
@@ -200,3 +203,21 @@ def qlora_linear_bwd(Wd, X, dY, A, B, alpha, rows=None, want_dx=True, want_da=Tr
                                  _p(B, _f32p), M, N, K, r, float(alpha), _p(rows_a, _i64p), nr,
                                  _p(dX, _f64p), _p(dA, _f64p), _p(dB, _f64p))
     return dX, dA, dB
+
+
+def adamw_step(p, g, m, v, lr, beta1, beta2, eps, weight_decay, step):
+    """One AdamW step on fp32 state (p, g, m, v); returns (p', m', v') in float64.
+
+    The pages ("Paged optimizers, and QLoRA end to end", zerotofrontier.app
+    "sft/peft") page the adapters' Adam states and give the learning rates; the
+    update is Kingma & Ba (2015) Algorithm 1 with Loshchilov & Hutter (2019)
+    decoupled weight decay, evaluated in float64.
+    """
+    p, g, m, v = (_f32(a).ravel() for a in (p, g, m, v))
+    n = p.size
+    assert g.size == n and m.size == n and v.size == n and int(step) >= 1
+    po, mo, vo = (np.empty(n, np.float64) for _ in range(3))
+    _load().orc_adamw_step(_p(p, _f32p), _p(g, _f32p), _p(m, _f32p), _p(v, _f32p), n,
+                           float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                           int(step), _p(po, _f64p), _p(mo, _f64p), _p(vo, _f64p))
+    return po, mo, vo

@@ -13,6 +13,8 @@
  *   [E2E] "Paged optimizers, and QLoRA end to end" (same page)
  *   [RW]  "The real way"                           (same page)
  *   [PT]  "Putting it together", forward formula   (prism.theerrors.in QLoRA explainer)
+ *   AdamW: Kingma & Ba (2015) Algorithm 1 with Loshchilov & Hutter (2019)
+ *          decoupled weight decay; the pages give only the paging and the rates
  *
  * Arithmetic conventions: fp32 operations are IEEE round-to-nearest-even,
  * compiled with -ffp-contract=off so that no multiply-add is silently fused.
@@ -412,6 +414,39 @@ void orc_qlora_linear_bwd(const float* Wd, const float* X, const float* dY, cons
     }
     free(U);
     free(T);
+}
+
+/* ------------------------------------------------------------------------ */
+/* One step of Adam with decoupled weight decay (AdamW) on the adapter       */
+/* parameters.  The pages ("Paged optimizers, and QLoRA end to end",         */
+/* zerotofrontier.app "sft/peft") keep the adapters' Adam states in paged    */
+/* memory and give the learning rates; they do not restate the update, so   */
+/* it is the published one: Kingma & Ba, "Adam: A Method for Stochastic      */
+/* Optimization" (ICLR 2015), Algorithm 1, with the weight decay decoupled   */
+/* from the gradient as in Loshchilov & Hutter, "Decoupled Weight Decay      */
+/* Regularization" (ICLR 2019), Algorithm 2 (schedule multiplier folded into */
+/* lr).  Step t >= 1, every value in float64 from the fp32 inputs:           */
+/*   m' = b1 m + (1 - b1) g                                                  */
+/*   v' = b2 v + (1 - b2) g^2                                                */
+/*   p' = p - lr wd p - lr (m' / (1 - b1^t)) / (sqrt(v' / (1 - b2^t)) + eps) */
+/* ------------------------------------------------------------------------ */
+void orc_adamw_step(const float* p, const float* g, const float* m, const float* v, int64_t n,
+                    double lr, double b1, double b2, double eps, double wd, int64_t t,
+                    double* p_out, double* m_out, double* v_out)
+{
+    const double bc1 = 1.0 - pow(b1, (double)t);
+    const double bc2 = 1.0 - pow(b2, (double)t);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const double gi = (double)g[i];
+        const double mi = b1 * (double)m[i] + (1.0 - b1) * gi;
+        const double vi = b2 * (double)v[i] + (1.0 - b2) * gi * gi;
+        const double mh = mi / bc1, vh = vi / bc2;
+        const double pi = (double)p[i];
+        p_out[i] = pi - lr * wd * pi - lr * mh / (sqrt(vh) + eps);
+        m_out[i] = mi;
+        v_out[i] = vi;
+    }
 }
 
 /* Number of OpenMP threads the parallel loops above use. */
