@@ -8,7 +8,8 @@ down; 4096 tokens; LoRA r = 64, alpha = 16 on every projection) the seven
 forwards in layer order, then the seven backwards in reverse order.  The
 frozen weights are quantized once beforehand (as in training); that codec
 path, and the few-token dequant-GEMV, are measured in the same run and
-reported under "paths".  Inputs are resident in HBM before timing starts.
+reported under "paths", with the adapter optimizer step (AdamW, device-resident
+and paged).  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `roofline` covers the dominant kernel (the fused
 dequant GEMM of the forward), timed with HIP events that the library records
@@ -428,6 +429,61 @@ def gemv_paths(layer, dev, r, alpha, reps=5):
     return out
 
 
+def adamw_paths(layer, dev, r, layers=80, reps=10):
+    """The adapter optimizer step ("Paged optimizers, and QLoRA end to end"): AdamW over
+    the LoRA parameters of `layers` decoder layers shaped like this one (A r x K and B
+    N x r on every projection), held as one flat fp32 state (master p, m, v) with an fp32
+    gradient and a bf16 copy of p: 30 bytes per parameter.  Device-resident state is
+    timed over `reps` steps; state paged out to page-locked host memory (one layer's
+    adapters through a 64 MiB staging buffer) is timed over one step and reported as
+    host-link traffic (24 bytes per parameter: p, m, v in and out)."""
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+    from workloads import Draw, seed_of
+
+    per_layer = sum(r * (p["N"] + p["K"]) for p in layer)
+    n = per_layer * layers
+    d = Draw(seed_of(8, layers), dev)
+    pp = d.normal((n,), 0.02)
+    g = d.normal((n,), 1e-3)
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    pbf = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    for t in range(1, 3):
+        nf4.adamw_step(pp, g, m, v, 1e-4, t, p_bf16=pbf)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for t in range(3, 3 + reps):
+        nf4.adamw_step(pp, g, m, v, 1e-4, t, p_bf16=pbf)
+    t1.record()
+    torch.cuda.synchronize()
+    sec = t0.elapsed_time(t1) / 1e3 / reps
+    dev_rate = 30 * n / sec / 1e9
+    del pp, m, v, pbf
+    # one layer's adapters paged out to host memory
+    k = per_layer
+    ph, mh, vh = (torch.empty(k, dtype=torch.float32, pin_memory=True) for _ in range(3))
+    ph.copy_(g[:k].cpu())
+    mh.zero_()
+    vh.zero_()
+    stage = nf4._workspace(64 << 20, torch.device(dev))
+    nf4.adamw_step_paged(ph, g[:k], mh, vh, 1e-4, 1, stage=stage)
+    torch.cuda.synchronize()
+    t0.record()
+    nf4.adamw_step_paged(ph, g[:k], mh, vh, 1e-4, 2, stage=stage)
+    t1.record()
+    torch.cuda.synchronize()
+    psec = t0.elapsed_time(t1) / 1e3
+    del g, stage
+    return dict(params=n, layers=layers,
+                device=dict(GBps=dev_rate, frac_hbm=dev_rate / PEAK_HBM_GBS, us_per_step=sec * 1e6,
+                            bytes_per_param=30),
+                paged=dict(params=k, host_link_GBps=24 * k / psec / 1e9, us_per_step=psec * 1e6,
+                           stage_bytes=64 << 20))
+
+
 def cpu_baseline(layer, alpha, r, tokens):
     """The CPU oracle (float64, OpenMP) on `tokens` tokens through every projection."""
     import numpy as np
@@ -537,7 +593,8 @@ def main():
                                        "avg_us": round(kb["avg_us"], 2)}},
     }
     if not args.no_paths and args.workload != "tiny":
-        line["paths"] = {"codec": codec_paths(layer, dev), "gemv": gemv_paths(layer, dev, r, alpha)}
+        line["paths"] = {"codec": codec_paths(layer, dev), "gemv": gemv_paths(layer, dev, r, alpha),
+                         "adamw": adamw_paths(layer, dev, r)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layer, alpha, r, min(args.cpu_tokens, M))
     print(json.dumps(line), flush=True)

@@ -23,7 +23,7 @@ __all__ = [
     "NF4Error", "NF4Weight", "lib_path", "load_library", "nf4_quantize", "nf4_double_quantize",
     "nf4_double_dequantize", "nf4_dequantize", "quantize_weight", "qlora_linear_fwd",
     "qlora_linear_bwd", "nf4_storage_bytes", "nf4_codebook", "nf4_workspace_bytes",
-    "nf4_profile_next_fused",
+    "nf4_profile_next_fused", "adamw_step", "adamw_step_paged", "PagedAdamW",
     "NF4_OP_DOUBLE_QUANTIZE", "NF4_OP_LINEAR_FWD", "NF4_OP_LINEAR_BWD",
 ]
 
@@ -89,6 +89,12 @@ def load_library():
     L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
     L.nf4_profile_next_fused.restype = None
     L.nf4_profile_next_fused.argtypes = [_vp, _vp]
+    _f = ctypes.c_float
+    L.nf4_adamw_step.restype = ctypes.c_int
+    L.nf4_adamw_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _f, _f, _f, _f, _f, _i64, _vp]
+    L.nf4_adamw_step_paged.restype = ctypes.c_int
+    L.nf4_adamw_step_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _f, _f, _f, _f, _f, _i64,
+                                       _vp, _sz, _vp]
     L.nf4_last_error.restype = ctypes.c_char_p
     L.nf4_last_error.argtypes = []
     _lib = L
@@ -291,3 +297,140 @@ def qlora_linear_bwd(W: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
     _check(L.qlora_linear_bwd(ctypes.byref(d), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, float(alpha),
                               _ptr(T), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(X.device)))
     return dX, dA, dB
+
+
+# ---------------------------------------------------------------------------
+# Adapter optimizer ("Paged optimizers, and QLoRA end to end", zerotofrontier.app
+# "sft/peft"): AdamW over fp32 master copies of the adapters, states paged between
+# GPU and host memory.
+# ---------------------------------------------------------------------------
+def _check_state(name, t, n, device=None):
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+        raise ValueError("%s must be a contiguous float32 tensor of %d values" % (name, n))
+    if device == "cuda" and not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if device == "host" and (t.is_cuda or not t.is_pinned()):
+        raise ValueError("%s must be a page-locked host tensor" % name)
+
+
+def adamw_step(p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tensor, lr: float,
+               step: int, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+               weight_decay: float = 0.0, p_bf16: Optional[torch.Tensor] = None):
+    """One AdamW step in place on fp32 GPU state p, m, v with gradient g (all the same
+    size); writes bf16(p) into p_bf16 when given (the layer's A or B)."""
+    L = load_library()
+    n = p.numel()
+    for name, t in (("p", p), ("g", g), ("m", m), ("v", v)):
+        _check_state(name, t, n, "cuda")
+    if p_bf16 is not None:
+        _dev(p_bf16, "p_bf16", torch.bfloat16)
+        if p_bf16.numel() != n:
+            raise ValueError("p_bf16 must have %d values" % n)
+    _check(L.nf4_adamw_step(_ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(p_bf16), n, float(lr), float(beta1),
+                            float(beta2), float(eps), float(weight_decay), int(step), _stream(p.device)))
+
+
+def adamw_step_paged(p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tensor, lr: float,
+                     step: int, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                     weight_decay: float = 0.0, p_bf16: Optional[torch.Tensor] = None,
+                     stage: Optional[torch.Tensor] = None):
+    """adamw_step for state paged out to page-locked host tensors p, m, v; g (and
+    p_bf16) on the GPU.  The state streams through `stage` (a GPU uint8 buffer,
+    64 MiB by default) in stream order; the host tensors must not be touched until
+    the stream has run the step."""
+    L = load_library()
+    n = p.numel()
+    for name, t in (("p", p), ("m", m), ("v", v)):
+        _check_state(name, t, n, "host")
+    _check_state("g", g, n, "cuda")
+    if p_bf16 is not None:
+        _dev(p_bf16, "p_bf16", torch.bfloat16)
+        if p_bf16.numel() != n:
+            raise ValueError("p_bf16 must have %d values" % n)
+    if stage is None:
+        stage = _workspace(64 << 20, g.device)
+    _dev(stage, "stage", torch.uint8)
+    _check(L.nf4_adamw_step_paged(_ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(p_bf16), n, float(lr),
+                                  float(beta1), float(beta2), float(eps), float(weight_decay), int(step),
+                                  _ptr(stage), stage.numel(), _stream(g.device)))
+
+
+class PagedAdamW:
+    """AdamW for the adapter tensors with paged optimizer state.
+
+    Each parameter (a bf16 GPU tensor: a layer's A or B) gets an fp32 master copy and
+    fp32 moments m, v.  That state lives on the GPU while the total fits
+    `device_budget_bytes` (None: no limit) and in page-locked host memory past it;
+    `page_out(i)` / `page_in(i)` move one parameter's state between the two.  step()
+    updates every parameter from its fp32 gradient and writes the bf16 copy back into
+    the parameter tensor: device state in one kernel, host state through a staging
+    buffer of `stage_bytes`.  Both paths give identical bits.
+    """
+
+    def __init__(self, params, lr: float, betas=(0.9, 0.999), eps: float = 1e-8,
+                 weight_decay: float = 0.0, device_budget_bytes: Optional[int] = None,
+                 stage_bytes: int = 64 << 20):
+        self.params = list(params)
+        self.lr, self.betas, self.eps, self.weight_decay = float(lr), tuple(betas), float(eps), float(weight_decay)
+        self.t = 0
+        self.state = []
+        used = 0
+        for q in self.params:
+            _dev(q, "param", torch.bfloat16)
+            nb = q.numel() * 12
+            on_gpu = device_budget_bytes is None or used + nb <= device_budget_bytes
+            p32 = q.detach().float().reshape(-1)
+            st = {"p": p32, "m": torch.zeros_like(p32), "v": torch.zeros_like(p32), "host": False}
+            if on_gpu:
+                used += nb
+            else:
+                self._to_host(st)
+            self.state.append(st)
+        self._stage_bytes = int(stage_bytes)
+        self._stage = None
+
+    @staticmethod
+    def _to_host(st):
+        for k in ("p", "m", "v"):
+            h = torch.empty(st[k].numel(), dtype=torch.float32, pin_memory=True)
+            h.copy_(st[k])
+            st[k] = h
+        st["host"] = True
+
+    def page_out(self, i: int):
+        """Move parameter i's fp32 state to page-locked host memory."""
+        st = self.state[i]
+        if not st["host"]:
+            torch.cuda.current_stream(self.params[i].device).synchronize()
+            self._to_host(st)
+
+    def page_in(self, i: int):
+        """Move parameter i's fp32 state back to the GPU."""
+        st = self.state[i]
+        if st["host"]:
+            torch.cuda.current_stream(self.params[i].device).synchronize()
+            dev = self.params[i].device
+            for k in ("p", "m", "v"):
+                st[k] = st[k].to(dev)
+            st["host"] = False
+
+    def on_host(self, i: int) -> bool:
+        return self.state[i]["host"]
+
+    def step(self, grads):
+        """One AdamW step for every parameter; grads are fp32 GPU tensors (dA, dB)."""
+        grads = list(grads)
+        if len(grads) != len(self.params):
+            raise ValueError("one gradient per parameter")
+        self.t += 1
+        b1, b2 = self.betas
+        for q, g, st in zip(self.params, grads, self.state):
+            gq = g.reshape(-1)
+            if st["host"]:
+                if self._stage is None:
+                    self._stage = _workspace(self._stage_bytes, q.device)
+                adamw_step_paged(st["p"], gq, st["m"], st["v"], self.lr, self.t, b1, b2, self.eps,
+                                 self.weight_decay, p_bf16=q, stage=self._stage)
+            else:
+                adamw_step(st["p"], gq, st["m"], st["v"], self.lr, self.t, b1, b2, self.eps,
+                           self.weight_decay, p_bf16=q)

@@ -2,7 +2,7 @@
 //
 // Host side only: argument validation (before any HIP call), the NF4 table,
 // workspace carving and kernel dispatch.  Every product step runs in the
-// gfx950 kernels of codec.hip, lora.hip and fused.hip.
+// gfx950 kernels of codec.hip, lora.hip, fused.hip, gemv.hip and adamw.hip.
 #include <math.h>
 #include <string.h>
 
@@ -343,6 +343,99 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     e = nf4::launch_lora_gemm(g, true, Tb, true, v.rows, r, M, part, s, dB, true, false, nullptr,
                               0.0f, hs);
     return hip_status(e, "qlora_linear_bwd (dB)");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Hyperparameter checks and the per-step scalars of the AdamW update (bias
+// corrections and the decay factor in double, rounded once to fp32).
+nf4_status adamw_scalars(float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                         nf4::AdamwScalars& k) {
+    if (step < 1) return fail(NF4_ERR_ARG, "step must be >= 1");
+    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+        return fail(NF4_ERR_ARG, "beta1 and beta2 must lie in [0, 1)");
+    if (!(eps > 0.0f) || !isfinite(eps)) return fail(NF4_ERR_ARG, "eps must be positive and finite");
+    if (!isfinite(lr) || !isfinite(weight_decay)) return fail(NF4_ERR_ARG, "lr and weight_decay must be finite");
+    const double bc1 = 1.0 - pow((double)beta1, (double)step);
+    const double bc2 = 1.0 - pow((double)beta2, (double)step);
+    if (!(bc1 > 0.0) || !(bc2 > 0.0)) return fail(NF4_ERR_ARG, "bias correction vanishes (beta = 0 with step 0?)");
+    k.b1 = beta1;
+    k.omb1 = (float)(1.0 - (double)beta1);
+    k.b2 = beta2;
+    k.omb2 = (float)(1.0 - (double)beta2);
+    k.step_size = (float)((double)lr / bc1);
+    k.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+    k.eps = eps;
+    k.decay = (float)(1.0 - (double)lr * (double)weight_decay);
+    return NF4_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return a && b && x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+nf4_status nf4_adamw_step(float* p, const float* g, float* m, float* v, uint16_t* p_bf16, int64_t n,
+                          float lr, float beta1, float beta2, float eps, float weight_decay,
+                          int64_t step, void* stream) {
+    nf4::AdamwScalars k;
+    nf4_status st = adamw_scalars(lr, beta1, beta2, eps, weight_decay, step, k);
+    if (st != NF4_OK) return st;
+    if (n < 0) return fail(NF4_ERR_ARG, "n must be >= 0");
+    if (n == 0) return NF4_OK;
+    if (!p || !g || !m || !v) return fail(NF4_ERR_ARG, "p, g, m or v is NULL");
+    if (!aligned(p, 16) || !aligned(g, 16) || !aligned(m, 16) || !aligned(v, 16))
+        return fail(NF4_ERR_ARG, "p, g, m and v must be 16-byte aligned");
+    if (!aligned(p_bf16, 8)) return fail(NF4_ERR_ARG, "p_bf16 must be 8-byte aligned");
+    const size_t b4 = (size_t)n * 4, b2 = (size_t)n * 2;
+    const void* bufs[4] = {p, g, m, v};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(bufs[i], b4, bufs[j], b4)) return fail(NF4_ERR_ARG, "p, g, m and v must not overlap");
+        if (overlaps(bufs[i], b4, p_bf16, b2)) return fail(NF4_ERR_ARG, "p_bf16 overlaps the state");
+    }
+    return hip_status(nf4::launch_adamw(p, g, m, v, p_bf16, n, k, (hipStream_t)stream), "nf4_adamw_step");
+}
+
+nf4_status nf4_adamw_step_paged(float* p_host, const float* g, float* m_host, float* v_host,
+                                uint16_t* p_bf16, int64_t n, float lr, float beta1, float beta2,
+                                float eps, float weight_decay, int64_t step, void* stage,
+                                size_t stage_bytes, void* stream) {
+    nf4::AdamwScalars k;
+    nf4_status st = adamw_scalars(lr, beta1, beta2, eps, weight_decay, step, k);
+    if (st != NF4_OK) return st;
+    if (n < 0) return fail(NF4_ERR_ARG, "n must be >= 0");
+    if (n == 0) return NF4_OK;
+    if (!p_host || !g || !m_host || !v_host) return fail(NF4_ERR_ARG, "p, g, m or v is NULL");
+    if (!aligned(g, 16)) return fail(NF4_ERR_ARG, "g must be 16-byte aligned");
+    if (!aligned(p_bf16, 8)) return fail(NF4_ERR_ARG, "p_bf16 must be 8-byte aligned");
+    if (!stage || !aligned(stage, 256)) return fail(NF4_ERR_ARG, "stage must be a 256-byte aligned buffer");
+    if (stage_bytes < 768) return fail(NF4_ERR_WORKSPACE, "stage must hold at least 768 bytes");
+    // chunk: a multiple of 64 parameters, so that the three staged vectors stay 256-byte aligned
+    const int64_t chunk = (int64_t)(stage_bytes / 768) * 64;
+    float* sp = (float*)stage;
+    float* sm = sp + chunk;
+    float* sv = sm + chunk;
+    hipStream_t hs = (hipStream_t)stream;
+    for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+        const int64_t cn = n - c0 < chunk ? n - c0 : chunk;
+        const size_t nb = (size_t)cn * 4;
+        hipError_t e = hipMemcpyAsync(sp, p_host + c0, nb, hipMemcpyHostToDevice, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(sm, m_host + c0, nb, hipMemcpyHostToDevice, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(sv, v_host + c0, nb, hipMemcpyHostToDevice, hs);
+        if (e == hipSuccess) e = nf4::launch_adamw(sp, g + c0, sm, sv, p_bf16 ? p_bf16 + c0 : nullptr, cn, k, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(p_host + c0, sp, nb, hipMemcpyDeviceToHost, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(m_host + c0, sm, nb, hipMemcpyDeviceToHost, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(v_host + c0, sv, nb, hipMemcpyDeviceToHost, hs);
+        if (e != hipSuccess) return hip_status(e, "nf4_adamw_step_paged");
+    }
+    return NF4_OK;
 }
 
 }  // extern "C"

@@ -84,4 +84,14 @@ hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint1
                                const uint16_t* Al, int r, uint16_t* dX, void* split_ws, const Nf4Table& tab,
                                hipStream_t st);
 
+// ---- adapter optimizer step (AdamW over fp32 state) -------------------------
+// Scalars of one step, formed on the host: omb1 = 1 - b1, omb2 = 1 - b2,
+// step_size = lr / (1 - b1^t), inv_sqrt_bc2 = 1 / sqrt(1 - b2^t), decay = 1 - lr wd.
+struct AdamwScalars {
+    float b1, omb1, b2, omb2, step_size, inv_sqrt_bc2, eps, decay;
+};
+// p, g, m, v: n fp32 values (16-byte aligned); pbf: bf16 copy of p or null (8-byte aligned).
+hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* pbf, int64_t n,
+                        const AdamwScalars& k, hipStream_t s);
+
 }  // namespace nf4

@@ -13,6 +13,10 @@
  *   [E2E] same page, "Paged optimizers, and QLoRA end to end" (r, alpha, gradient flow)
  *   [RW]  same page, "The real way" (two codes per byte, dequant fused into the matmul)
  *   [PT]  prism.theerrors.in QLoRA explainer, "Putting it together" (layer formula)
+ *   [PO]  zerotofrontier.app "sft/peft", "Paged optimizers, and QLoRA end to end"
+ *         (only the adapters learn; their Adam states are paged between GPU and host
+ *         RAM; learning rates).  The update itself is Adam (Kingma & Ba, ICLR 2015,
+ *         Algorithm 1) with decoupled weight decay (Loshchilov & Hutter, ICLR 2019).
  *
  * Conventions shared by every entry point:
  *   - Memory: every pointer argument is device memory unless stated; the
@@ -135,6 +139,37 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
                             const void* A, const void* B, int32_t r, float alpha, const void* T,
                             void* dX, float* dA, float* dB, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* [PO]: one AdamW step over n adapter parameters, in fp32 with no fused
+ * multiply-add:
+ *   m = b1 m + (1 - b1) g;   v = b2 v + (1 - b2) g^2
+ *   p = p (1 - lr wd) - (lr / (1 - b1^t)) * m / (sqrt(v) / sqrt(1 - b2^t) + eps)
+ * 1 - b1, 1 - b2, the bias corrections and 1 - lr wd are formed in double on the
+ * host and rounded once to fp32; sqrt and the division are correctly rounded.
+ *   p, m, v  n fp32 values each (master parameters, first and second moments),
+ *            updated in place; 16-byte aligned
+ *   g        n fp32 gradient values (dA or dB of qlora_linear_bwd); 16-byte aligned
+ *   p_bf16   out: bf16 copy of the updated p (round to nearest even), the A or B
+ *            operand of the layer; or NULL.  8-byte aligned
+ *   step     t >= 1, the step being taken;  0 <= beta1, beta2 < 1;  eps > 0;
+ *            lr and weight_decay finite
+ * n == 0 enqueues nothing.  No buffer may overlap another. */
+nf4_status nf4_adamw_step(float* p, const float* g, float* m, float* v, uint16_t* p_bf16, int64_t n,
+                          float lr, float beta1, float beta2, float eps, float weight_decay,
+                          int64_t step, void* stream);
+
+/* [PO]: the same step for state paged out to host memory.  p_host, m_host and
+ * v_host are page-locked host buffers (hipHostMalloc or equivalent); g and p_bf16
+ * are device memory as above.  The state passes through the device buffer `stage`
+ * in chunks of floor(stage_bytes / 768) * 64 parameters: each chunk is copied in,
+ * updated and copied back, in stream order on `stream`.  The host buffers must
+ * stay untouched until the stream has run the work.  Results are bit-identical to
+ * nf4_adamw_step on device-resident state.
+ *   stage        device scratch, 256-byte aligned, stage_bytes >= 768 */
+nf4_status nf4_adamw_step_paged(float* p_host, const float* g, float* m_host, float* v_host,
+                                uint16_t* p_bf16, int64_t n, float lr, float beta1, float beta2,
+                                float eps, float weight_decay, int64_t step, void* stage,
+                                size_t stage_bytes, void* stream);
 
 /* Bytes of device workspace an operation needs (0 = none).  For
  * NF4_OP_DOUBLE_QUANTIZE pass n1 as N.  The linear products keep their

@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted(["nf4_quantize", "nf4_double_quantize", "nf4_double_dequantize",
                             "nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
                             "nf4_workspace_bytes", "nf4_storage_bytes", "nf4_codebook",
-                            "nf4_last_error", "nf4_profile_next_fused"])
+                            "nf4_last_error", "nf4_profile_next_fused", "nf4_adamw_step",
+                            "nf4_adamw_step_paged"])
     for name in names:
         assert hasattr(L, name), name
     # and the C symbols are unmangled (extern "C")
@@ -156,3 +157,34 @@ def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     with pytest.raises(ValueError):
         nf4.nf4_quantize(torch.zeros(64))
+
+
+def test_adamw_rejects_bad_arguments():
+    # checks happen on the host, before any HIP call
+    L = nf4.load_library()
+    p = ctypes.c_void_p(1 << 20)
+    q = ctypes.c_void_p(2 << 20)
+    m = ctypes.c_void_p(3 << 20)
+    v = ctypes.c_void_p(4 << 20)
+    step = L.nf4_adamw_step
+    assert step(p, q, m, v, None, 0, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, None) == nf4.NF4_OK     # n == 0
+    assert step(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 0, None) == nf4.NF4_ERR_ARG  # step 0
+    assert step(p, q, m, v, None, 64, 1e-4, 1.0, 0.999, 1e-8, 0.0, 1, None) == nf4.NF4_ERR_ARG  # beta1 = 1
+    assert step(p, q, m, v, None, 64, 1e-4, 0.9, -0.1, 1e-8, 0.0, 1, None) == nf4.NF4_ERR_ARG  # beta2 < 0
+    assert step(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 0.0, 0.0, 1, None) == nf4.NF4_ERR_ARG  # eps = 0
+    assert step(p, q, m, v, None, 64, float("nan"), 0.9, 0.999, 1e-8, 0.0, 1, None) == nf4.NF4_ERR_ARG
+    assert step(p, q, m, v, None, -1, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, None) == nf4.NF4_ERR_ARG
+    assert step(None, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, None) == nf4.NF4_ERR_ARG
+    assert step(ctypes.c_void_p((1 << 20) + 4), q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1,
+                None) == nf4.NF4_ERR_ARG                                                      # misaligned
+    assert step(p, q, m, v, ctypes.c_void_p((5 << 20) + 2), 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1,
+                None) == nf4.NF4_ERR_ARG                                                      # bf16 copy
+    assert step(p, ctypes.c_void_p((1 << 20) + 128), m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1,
+                None) == nf4.NF4_ERR_ARG                                                      # overlap
+    assert "overlap" in L.nf4_last_error().decode()
+    paged = L.nf4_adamw_step_paged
+    st = ctypes.c_void_p(8 << 20)
+    assert paged(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, st, 512, None) == nf4.NF4_ERR_WORKSPACE
+    assert paged(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, None, 1 << 20, None) == nf4.NF4_ERR_ARG
+    assert paged(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, ctypes.c_void_p((8 << 20) + 16),
+                 1 << 20, None) == nf4.NF4_ERR_ARG                                            # stage alignment
