@@ -55,6 +55,9 @@ def _args():
                         "{1, 4, 16} (for a kernel trace; see --summarize-gemv-trace)")
     p.add_argument("--summarize-gemv-trace", metavar="KERNEL_TRACE_CSV",
                    help="per-shape kernel durations of a --gemv-sweep kernel trace, as a markdown table")
+    p.add_argument("--adamw-only", action="store_true",
+                   help="the adapter optimizer step only (the 'adamw' path figures), as a JSON line "
+                        "(for kernel traces and counter runs)")
     p.add_argument("--plain-gemm", action="store_true",
                    help="time the vendor library's plain bf16 GEMM (torch.matmul) at the layer shapes, "
                         "for context, and print a markdown table")
@@ -554,6 +557,11 @@ def main():
         return
     if args.pmc_workload:
         pmc_workload(args)
+        return
+    if args.adamw_only:
+        from workloads import LLAMA65B, layer_projections
+        shapes = [dict(N=N, K=K) for _, N, K in layer_projections(LLAMA65B["d"], LLAMA65B["ffn"])]
+        print(json.dumps({"adamw": adamw_paths(shapes, dev, 64)}), flush=True)
         return
     layer, projs, M, r, alpha = build_layer(args.workload, dev)
     fwd_flops, bwd_flops = layer_flops(M, projs, r)
