@@ -49,6 +49,9 @@ def _load():
                                          ctypes.c_double, _i64p, _i64, _f64p, _f64p]
     lib.orc_qlora_linear_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _i64, _i64, _i64,
                                          _i64, ctypes.c_double, _i64p, _i64, _f64p, _f64p, _f64p]
+    lib.orc_quantize_levels.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64, _f32p, _u8p, _f32p]
+    lib.orc_codebook_stats.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64, _u8p, _f32p, _f32p, _i64p,
+                                       _f64p, _f64p]
     _d = ctypes.c_double
     lib.orc_adamw_step.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _d, _d, _d, _d, _d, _i64,
                                    _f64p, _f64p, _f64p]
@@ -221,3 +224,36 @@ def adamw_step(p, g, m, v, lr, beta1, beta2, eps, weight_decay, step):
                            float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
                            int(step), _p(po, _f64p), _p(mo, _f64p), _p(vo, _f64p))
     return po, mo, vo
+
+
+def quantize_levels(w: np.ndarray, levels: np.ndarray):
+    """Blockwise absmax quantization (blocks of 64) onto an ascending 16-level codebook
+    ("Block-wise quantization in one page"); returns (codes uint8[ceil(n/2)], absmax)."""
+    levels = np.ascontiguousarray(levels, np.float32).ravel()
+    assert levels.size == 16 and np.all(np.diff(levels.astype(np.float64)) > 0)
+    is_bf16 = 1 if w.dtype == np.uint16 else 0
+    w = np.ascontiguousarray(w).ravel()
+    n = w.size
+    codes = np.zeros((n + 1) // 2, np.uint8)
+    absmax = np.zeros((n + 63) // 64, np.float32)
+    _load().orc_quantize_levels(w.ctypes.data_as(ctypes.c_void_p), is_bf16, n, _p(levels, _f32p),
+                                _p(codes, _u8p), _p(absmax, _f32p))
+    return codes, absmax
+
+
+def codebook_stats(w: np.ndarray, codes: np.ndarray, absmax: np.ndarray, levels: np.ndarray):
+    """(count int64[16], sum_x float64[16], sse float64) of a blockwise quantization:
+    values per code, sum of x = fp32(w/absmax) per code, and the float64 sum of
+    (w - fp32(level[code] * absmax))^2 ("NF4, derived from normal quantiles")."""
+    levels = np.ascontiguousarray(levels, np.float32).ravel()
+    is_bf16 = 1 if w.dtype == np.uint16 else 0
+    w = np.ascontiguousarray(w).ravel()
+    codes = np.ascontiguousarray(codes, np.uint8)
+    absmax = np.ascontiguousarray(absmax, np.float32)
+    count = np.zeros(16, np.int64)
+    sum_x = np.zeros(16, np.float64)
+    sse = np.zeros(1, np.float64)
+    _load().orc_codebook_stats(w.ctypes.data_as(ctypes.c_void_p), is_bf16, w.size, _p(codes, _u8p),
+                               _p(absmax, _f32p), _p(levels, _f32p), _p(count, _i64p), _p(sum_x, _f64p),
+                               _p(sse, _f64p))
+    return count, sum_x, float(sse[0])

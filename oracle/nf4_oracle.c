@@ -148,17 +148,20 @@ static int nearest_level(float x, const double mid[15])
 }
 
 /* ------------------------------------------------------------------------ */
-/* [BQ]+[NF]+[RW] blockwise absmax NF4 quantization with blocksize 64.       */
+/* [BQ] blockwise absmax quantization with blocksize 64 onto any ascending   */
+/* codebook of 16 levels (the page's comparison of NF4 with integer grids    */
+/* and a Lloyd codebook quantizes the same blocks with each table).          */
 /* w: n values, fp32 (is_bf16 == 0) or bf16 bit patterns (is_bf16 == 1).   */
-/* codes: ceil(n/2) bytes.  absmax: ceil(n/64) fp32 constants.               */
+/* codes: ceil(n/2) bytes.  absmax: ceil(n/64) fp32 constants.  A block     */
+/* with absmax 0 takes the code of x = 0 under the same rule.                */
 /* ------------------------------------------------------------------------ */
-void orc_nf4_quantize(const void* w, int is_bf16, int64_t n, uint8_t* codes, float* absmax)
+void orc_quantize_levels(const void* w, int is_bf16, int64_t n, const float lv[16], uint8_t* codes,
+                         float* absmax)
 {
-    float lv[16];
     double mid[15];
-    orc_nf4_codebook(lv);
     for (int j = 0; j < 15; ++j)
         mid[j] = ((double)lv[j] + (double)lv[j + 1]) / 2.0;
+    const int zero_code = nearest_level(0.0f, mid);
 
     const int64_t nblk = (n + 63) / 64;
     const float* wf = (const float*)w;
@@ -180,7 +183,7 @@ void orc_nf4_quantize(const void* w, int is_bf16, int64_t n, uint8_t* codes, flo
         for (int64_t i = lo; i < hi; ++i) {
             int code;
             if (c == 0.0f) {
-                code = 7;                          /* exact-zero level */
+                code = zero_code;
             } else {
                 volatile float x = v[i - lo] / c;  /* one IEEE fp32 division */
                 code = nearest_level(x, mid);
@@ -190,6 +193,77 @@ void orc_nf4_quantize(const void* w, int is_bf16, int64_t n, uint8_t* codes, flo
             else       codes[i >> 1] |= (uint8_t)code;
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* [BQ]+[NF]+[RW] blockwise absmax NF4 quantization with blocksize 64: the   */
+/* NF4 table in the rule above (an all-zero block gets code 7, the exact     */
+/* zero level).                                                              */
+/* ------------------------------------------------------------------------ */
+void orc_nf4_quantize(const void* w, int is_bf16, int64_t n, uint8_t* codes, float* absmax)
+{
+    float lv[16];
+    orc_nf4_codebook(lv);
+    orc_quantize_levels(w, is_bf16, n, lv, codes, absmax);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Statistics of a blockwise quantization with a 16-level codebook (the      */
+/* page's comparison, "NF4, derived from normal quantiles"): per code, the   */
+/* number of values and the sum of x = fp32(w / absmax) (a Lloyd step moves  */
+/* each level to the mean x of its values); over all values, the squared    */
+/* error sum of (w - fp32(level[code] * absmax))^2, in float64.  A block     */
+/* with absmax 0 has x = 0 and no error.  Per-thread partial sums (static    */
+/* schedule) are added in thread order.                                      */
+/* ------------------------------------------------------------------------ */
+void orc_codebook_stats(const void* w, int is_bf16, int64_t n, const uint8_t* codes, const float* absmax,
+                        const float lv[16], int64_t count[16], double sum_x[16], double* sse)
+{
+    const float* wf = (const float*)w;
+    const uint16_t* wb = (const uint16_t*)w;
+    int nt = 1;
+#ifdef _OPENMP
+    nt = omp_get_max_threads();
+#endif
+    int64_t* pc = (int64_t*)calloc((size_t)nt * 16, sizeof(int64_t));
+    double* px = (double*)calloc((size_t)nt * 16, sizeof(double));
+    double* pe = (double*)calloc((size_t)nt, sizeof(double));
+#pragma omp parallel
+    {
+        int t = 0;
+#ifdef _OPENMP
+        t = omp_get_thread_num();
+#endif
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            const float wi = is_bf16 ? bf16_bits_to_f32(wb[i]) : wf[i];
+            const int code = (codes[i >> 1] >> (4 * (i & 1))) & 15;
+            const float c = absmax[i / 64];
+            pc[t * 16 + code] += 1;
+            if (c != 0.0f) {
+                volatile float x = wi / c;
+                volatile float wq = lv[code] * c;
+                const double e = (double)wi - (double)wq;
+                px[t * 16 + code] += (double)x;
+                pe[t] += e * e;
+            }
+        }
+    }
+    for (int j = 0; j < 16; ++j) {
+        count[j] = 0;
+        sum_x[j] = 0.0;
+    }
+    *sse = 0.0;
+    for (int t = 0; t < nt; ++t) {
+        for (int j = 0; j < 16; ++j) {
+            count[j] += pc[t * 16 + j];
+            sum_x[j] += px[t * 16 + j];
+        }
+        *sse += pe[t];
+    }
+    free(pc);
+    free(px);
+    free(pe);
 }
 
 /* ------------------------------------------------------------------------ */
