@@ -9,7 +9,7 @@ forwards in layer order, then the seven backwards in reverse order.  The
 frozen weights are quantized once beforehand (as in training); that codec
 path, and the few-token dequant-GEMV, are measured in the same run and
 reported under "paths", with the adapter optimizer step (AdamW, device-resident
-and paged).  Inputs are resident in HBM before timing starts.
+and paged) and the page's codebook comparison (NF4, integer grids, Lloyd).  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `roofline` covers the dominant kernel (the fused
 dequant GEMM of the forward), timed with HIP events that the library records
@@ -55,6 +55,8 @@ def _args():
                         "{1, 4, 16} (for a kernel trace; see --summarize-gemv-trace)")
     p.add_argument("--summarize-gemv-trace", metavar="KERNEL_TRACE_CSV",
                    help="per-shape kernel durations of a --gemv-sweep kernel trace, as a markdown table")
+    p.add_argument("--codebooks-only", action="store_true",
+                   help="the codebook comparison only (the 'codebooks' path figures), as a JSON line")
     p.add_argument("--adamw-only", action="store_true",
                    help="the adapter optimizer step only (the 'adamw' path figures), as a JSON line "
                         "(for kernel traces and counter runs)")
@@ -487,6 +489,53 @@ def adamw_paths(layer, dev, r, layers=80, reps=10):
                            stage_bytes=64 << 20))
 
 
+def codebook_paths(dev, n=1 << 28, reps=5):
+    """The page's codebook comparison ("NF4, derived from normal quantiles") at GPU scale:
+    n N(0,1) fp32 values in blocks of 64, quantized with NF4, the symmetric int4 grid
+    {-7..7}/7, the grid {-8..7}/8 and a Lloyd codebook (30 GPU Lloyd steps from NF4);
+    code entropy and RMS error of each, and the rates of the quantize and statistics
+    kernels (the statistics pass reads 4 + 0.5 + 4/64 bytes per value)."""
+    import numpy as np
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+    from workloads import Draw, seed_of
+
+    w = Draw(seed_of(9), dev).normal((n,), 1.0)
+    tables = {"nf4": [float(x) for x in nf4.nf4_codebook()], "int4_sym": nf4.codebook_int4_symmetric(),
+              "uniform16": nf4.codebook_uniform16()}
+    tables["lloyd"] = nf4.lloyd_codebook(w, tables["nf4"], iters=30)
+    out = {"values": n}
+    for name, lv in tables.items():
+        codes, absmax = nf4.nf4_quantize_codebook(w, lv)
+        count, _, sse = nf4.nf4_codebook_stats(w, codes, absmax, lv)
+        p = count[count > 0] / count.sum()
+        out[name] = dict(entropy_bits=float(-(p * np.log2(p)).sum()), rms=float(np.sqrt(sse / n)))
+    out["rms_gain_nf4_vs_int4_sym"] = 1 - out["nf4"]["rms"] / out["int4_sym"]["rms"]
+    out["rms_gain_lloyd_vs_nf4"] = 1 - out["lloyd"]["rms"] / out["nf4"]["rms"]
+    lv = tables["nf4"]
+    codes, absmax = nf4.nf4_quantize_codebook(w, lv)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        nf4.nf4_quantize_codebook(w, lv)
+    t1.record()
+    torch.cuda.synchronize()
+    tq = t0.elapsed_time(t1) / 1e3 / reps
+    t0.record()
+    for _ in range(reps):
+        nf4.nf4_codebook_stats(w, codes, absmax, lv)
+    t1.record()
+    torch.cuda.synchronize()
+    ts = t0.elapsed_time(t1) / 1e3 / reps
+    qb, sb = n * (4 + 0.5 + 4 / 64), n * (4 + 0.5 + 4 / 64)
+    out["quantize"] = dict(GBps=qb / tq / 1e9, frac_hbm=qb / tq / 1e9 / PEAK_HBM_GBS)
+    out["stats"] = dict(GBps=sb / ts / 1e9, frac_hbm=sb / ts / 1e9 / PEAK_HBM_GBS,
+                        note="includes the host copy of the 33 results")
+    return out
+
+
 def cpu_baseline(layer, alpha, r, tokens):
     """The CPU oracle (float64, OpenMP) on `tokens` tokens through every projection."""
     import numpy as np
@@ -558,6 +607,9 @@ def main():
     if args.pmc_workload:
         pmc_workload(args)
         return
+    if args.codebooks_only:
+        print(json.dumps({"codebooks": codebook_paths(dev)}), flush=True)
+        return
     if args.adamw_only:
         from workloads import LLAMA65B, layer_projections
         shapes = [dict(N=N, K=K) for _, N, K in layer_projections(LLAMA65B["d"], LLAMA65B["ffn"])]
@@ -602,7 +654,7 @@ def main():
     }
     if not args.no_paths and args.workload != "tiny":
         line["paths"] = {"codec": codec_paths(layer, dev), "gemv": gemv_paths(layer, dev, r, alpha),
-                         "adamw": adamw_paths(layer, dev, r)}
+                         "adamw": adamw_paths(layer, dev, r), "codebooks": codebook_paths(dev)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layer, alpha, r, min(args.cpu_tokens, M))
     print(json.dumps(line), flush=True)

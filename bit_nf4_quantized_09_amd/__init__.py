@@ -24,12 +24,14 @@ __all__ = [
     "nf4_double_dequantize", "nf4_dequantize", "quantize_weight", "qlora_linear_fwd",
     "qlora_linear_bwd", "nf4_storage_bytes", "nf4_codebook", "nf4_workspace_bytes",
     "nf4_profile_next_fused", "adamw_step", "adamw_step_paged", "PagedAdamW",
+    "nf4_quantize_codebook", "nf4_codebook_stats", "codebook_int4_symmetric", "codebook_uniform16",
+    "lloyd_codebook", "NF4_OP_CODEBOOK_STATS",
     "NF4_OP_DOUBLE_QUANTIZE", "NF4_OP_LINEAR_FWD", "NF4_OP_LINEAR_BWD",
 ]
 
 NF4_OK, NF4_ERR_ARG, NF4_ERR_UNSUPPORTED, NF4_ERR_WORKSPACE, NF4_ERR_HIP = range(5)
 NF4_F32, NF4_BF16 = 0, 1
-NF4_OP_DOUBLE_QUANTIZE, NF4_OP_LINEAR_FWD, NF4_OP_LINEAR_BWD = 1, 2, 3
+NF4_OP_DOUBLE_QUANTIZE, NF4_OP_LINEAR_FWD, NF4_OP_LINEAR_BWD, NF4_OP_CODEBOOK_STATS = 1, 2, 3, 4
 _STATUS = {1: "NF4_ERR_ARG", 2: "NF4_ERR_UNSUPPORTED", 3: "NF4_ERR_WORKSPACE", 4: "NF4_ERR_HIP"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +92,11 @@ def load_library():
     L.nf4_profile_next_fused.restype = None
     L.nf4_profile_next_fused.argtypes = [_vp, _vp]
     _f = ctypes.c_float
+    _fp = ctypes.POINTER(ctypes.c_float)
+    L.nf4_quantize_codebook.restype = ctypes.c_int
+    L.nf4_quantize_codebook.argtypes = [_vp, ctypes.c_int, _i64, _i32, _fp, _vp, _vp, _vp]
+    L.nf4_codebook_stats.restype = ctypes.c_int
+    L.nf4_codebook_stats.argtypes = [_vp, ctypes.c_int, _i64, _vp, _vp, _fp, _vp, _vp, _sz, _vp]
     L.nf4_adamw_step.restype = ctypes.c_int
     L.nf4_adamw_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _f, _f, _f, _f, _f, _i64, _vp]
     L.nf4_adamw_step_paged.restype = ctypes.c_int
@@ -434,3 +441,77 @@ class PagedAdamW:
             else:
                 adamw_step(st["p"], gq, st["m"], st["v"], self.lr, self.t, b1, b2, self.eps,
                            self.weight_decay, p_bf16=q)
+
+
+# ---------------------------------------------------------------------------
+# Codebook comparison ("NF4, derived from normal quantiles", zerotofrontier.app
+# "sft/peft"): the same blockwise quantization onto other 16-level tables, and the
+# statistics the page compares them by.
+# ---------------------------------------------------------------------------
+def codebook_int4_symmetric():
+    """The symmetric int4 grid {-7..7}/7, with an unused 16th level above 1."""
+    return [k / 7 for k in range(-7, 8)] + [2.0]
+
+
+def codebook_uniform16():
+    """The 16-level grid {-8..7}/8."""
+    return [k / 8 for k in range(-8, 8)]
+
+
+def _levels16(levels):
+    lv = [float(x) for x in levels]
+    if len(lv) != 16:
+        raise ValueError("a codebook has 16 levels")
+    return (ctypes.c_float * 16)(*lv)
+
+
+def nf4_quantize_codebook(w: torch.Tensor, levels, blocksize: int = 64):
+    """nf4_quantize onto a caller's 16 ascending levels: (codes uint8, absmax fp32)."""
+    L = load_library()
+    _dev(w, "w")
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be float32 or bfloat16")
+    n = w.numel()
+    codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty((n + blocksize - 1) // blocksize, dtype=torch.float32, device=w.device)
+    dt = NF4_BF16 if w.dtype == torch.bfloat16 else NF4_F32
+    _check(L.nf4_quantize_codebook(_ptr(w), dt, n, blocksize, _levels16(levels), _ptr(codes), _ptr(absmax),
+                                   _stream(w.device)))
+    return codes, absmax
+
+
+def nf4_codebook_stats(w: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor, levels):
+    """Per-code counts, per-code sums of x = w/absmax and the squared error of a
+    blockwise quantization, computed on the GPU: (count int64[16], sum_x float64[16],
+    sse float) as host values."""
+    L = load_library()
+    _dev(w, "w")
+    _dev(codes, "codes", torch.uint8)
+    _dev(absmax, "absmax", torch.float32)
+    n = w.numel()
+    dt = NF4_BF16 if w.dtype == torch.bfloat16 else NF4_F32
+    out = torch.empty(33, dtype=torch.float64, device=w.device)
+    wsb = L.nf4_workspace_bytes(NF4_OP_CODEBOOK_STATS, 0, n, 0, 0)
+    ws = _workspace(wsb, w.device)
+    _check(L.nf4_codebook_stats(_ptr(w), dt, n, _ptr(codes), _ptr(absmax), _levels16(levels), _ptr(out),
+                                _ptr(ws), wsb, _stream(w.device)))
+    host = out.cpu()
+    count = host[:16].view(torch.int64).numpy().copy()
+    return count, host[16:32].numpy().copy(), float(host[32])
+
+
+def lloyd_codebook(w: torch.Tensor, levels, iters: int = 30):
+    """Lloyd's algorithm (one-dimensional k-means) for the squared error of the blockwise
+    quantization of w, from `levels`: each step quantizes on the GPU and moves every used
+    level to the mean x = w/absmax of its values.  Returns the 16 levels (ascending)."""
+    lv = sorted(float(x) for x in levels)
+    for _ in range(iters):
+        codes, absmax = nf4_quantize_codebook(w, lv)
+        count, sum_x, _ = nf4_codebook_stats(w, codes, absmax, lv)
+        new = [float(torch.tensor(sum_x[j] / count[j], dtype=torch.float32)) if count[j] > 0 else lv[j]
+               for j in range(16)]
+        new.sort()
+        if new == lv:
+            break
+        lv = new
+    return lv

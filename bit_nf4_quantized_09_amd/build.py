@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libqlora_nf4.so")
-SOURCES = ["api.hip", "codec.hip", "lora.hip", "fused.hip", "gemv.hip", "adamw.hip"]
+SOURCES = ["api.hip", "codec.hip", "lora.hip", "fused.hip", "gemv.hip", "adamw.hip", "codebook.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -2,7 +2,7 @@
 //
 // Host side only: argument validation (before any HIP call), the NF4 table,
 // workspace carving and kernel dispatch.  Every product step runs in the
-// gfx950 kernels of codec.hip, lora.hip, fused.hip, gemv.hip and adamw.hip.
+// gfx950 kernels of codec.hip, lora.hip, fused.hip, gemv.hip, adamw.hip and codebook.hip.
 #include <math.h>
 #include <string.h>
 
@@ -51,6 +51,41 @@ long double norm_quantile(long double p) {
     return 0.5L * (lo + hi);
 }
 
+// Encode table of an ascending 16-level codebook ("Block-wise quantization in one
+// page": the nearest level, a value exactly between two taking the lower one).  The
+// quantize kernel compares x = w/absmax with th[j], the largest fp32 not above the
+// float64 midpoint, which decides x > midpoint exactly for every fp32 x.  It finds the
+// candidate threshold through 1/32-wide buckets of [-1, 1 + 1/32), so at most one
+// threshold may fall in a bucket; and its division is exact for every normal quotient,
+// so no threshold may lie within the subnormal range around 0 (there every quotient
+// must fall on the same side as 0).  Returns false, with the reason, for a codebook
+// outside these limits.
+bool make_table(const float lv[16], Nf4Table& t, std::string& why) {
+    for (int i = 0; i < 16; ++i) {
+        if (!isfinite(lv[i])) { why = "levels must be finite"; return false; }
+        if (i > 0 && !(lv[i] > lv[i - 1])) { why = "levels must be strictly ascending"; return false; }
+        t.lv[i] = lv[i];
+    }
+    int zero_code = 0;
+    int last_bucket = -1;
+    for (int j = 0; j < 15; ++j) {
+        // largest fp32 not above the (exact) midpoint: x > th[j] <=> x > midpoint
+        const double mid = ((double)lv[j] + (double)lv[j + 1]) / 2.0;
+        float th = (float)mid;
+        if ((double)th > mid) th = nextafterf(th, -INFINITY);
+        t.th[j] = th;
+        if (fabsf(th) < 1.1754943508222875e-38f) { why = "a decision threshold lies in the subnormal range around 0"; return false; }
+        if (th >= -1.0f && th < 1.0f + 1.0f / 32.0f) {
+            const int b = (int)floorf(th * 32.0f) + 32;
+            if (b == last_bucket) { why = "two decision thresholds lie within one 1/32-wide bucket"; return false; }
+            last_bucket = b;
+        }
+        zero_code += th < 0.0f ? 1 : 0;
+    }
+    t.zero_word = 0x11111111u * (uint32_t)zero_code;
+    return true;
+}
+
 Nf4Table build_table() {
     const long double pmax = ((1.0L - 1.0L / 30.0L) + (1.0L - 1.0L / 32.0L)) / 2.0L;
     const long double top = norm_quantile(pmax);
@@ -58,16 +93,12 @@ Nf4Table build_table() {
     for (int i = 0; i < 7; ++i) v[i] = -norm_quantile(pmax - (long double)i * (pmax - 0.5L) / 7.0L);
     v[7] = 0.0L;
     for (int i = 0; i < 8; ++i) v[8 + i] = norm_quantile(pmax - (long double)(7 - i) * (pmax - 0.5L) / 8.0L);
+    float lv[16];
+    for (int i = 0; i < 16; ++i) lv[i] = (float)(v[i] / top);
+    lv[7] = 0.0f;
     Nf4Table t;
-    for (int i = 0; i < 16; ++i) t.lv[i] = (float)(v[i] / top);
-    t.lv[7] = 0.0f;
-    for (int j = 0; j < 15; ++j) {
-        // largest fp32 not above the (exact) midpoint: x > th[j] <=> x > midpoint
-        const double mid = ((double)t.lv[j] + (double)t.lv[j + 1]) / 2.0;
-        float th = (float)mid;
-        if ((double)th > mid) th = nextafterf(th, -INFINITY);
-        t.th[j] = th;
-    }
+    std::string why;
+    make_table(lv, t, why);
     return t;
 }
 
@@ -179,6 +210,7 @@ size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t 
     if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
     switch (op) {
         case NF4_OP_DOUBLE_QUANTIZE: return nf4::double_quantize_ws_bytes(N);
+        case NF4_OP_CODEBOOK_STATS: return N > 0 ? nf4::codebook_stats_ws_bytes(N) : 0;
         case NF4_OP_LINEAR_FWD:
             return 2 * rank_buffer_bytes(M, r) + c1_buffer_bytes(op, M, N, K) + fwd_partial_bytes(M, N, K, r);
         case NF4_OP_LINEAR_BWD:
@@ -199,6 +231,55 @@ nf4_status nf4_quantize(const void* w, nf4_dtype dtype, int64_t n, int32_t block
     return hip_status(nf4::launch_quantize(w, dtype == NF4_BF16, n, codes, absmax, table(),
                                            (hipStream_t)stream),
                       "nf4_quantize");
+}
+
+nf4_status nf4_quantize_codebook(const void* w, nf4_dtype dtype, int64_t n, int32_t blocksize,
+                                 const float* levels, uint8_t* codes, float* absmax, void* stream) {
+    if (blocksize != 64) return fail(NF4_ERR_UNSUPPORTED, "blocksize must be 64");
+    if (dtype != NF4_F32 && dtype != NF4_BF16) return fail(NF4_ERR_ARG, "dtype must be NF4_F32 or NF4_BF16");
+    if (!levels) return fail(NF4_ERR_ARG, "levels is NULL");
+    Nf4Table tab;
+    std::string why;
+    if (!make_table(levels, tab, why)) return fail(NF4_ERR_UNSUPPORTED, "codebook: " + why);
+    if (n < 0) return fail(NF4_ERR_ARG, "n must be >= 0");
+    if (n == 0) return NF4_OK;
+    if (!w || !codes || !absmax) return fail(NF4_ERR_ARG, "NULL w/codes/absmax");
+    if (!aligned(w, 16)) return fail(NF4_ERR_ARG, "w must be 16-byte aligned");
+    if (!aligned(codes, 4) || !aligned(absmax, 4)) return fail(NF4_ERR_ARG, "codes/absmax must be 4-byte aligned");
+    return hip_status(nf4::launch_quantize(w, dtype == NF4_BF16, n, codes, absmax, tab, (hipStream_t)stream),
+                      "nf4_quantize_codebook");
+}
+
+nf4_status nf4_codebook_stats(const void* w, nf4_dtype dtype, int64_t n, const uint8_t* codes,
+                              const float* absmax, const float* levels, nf4_codebook_stats_t* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    static_assert(sizeof(nf4_codebook_stats_t) == sizeof(nf4::CodebookStats), "stats layout");
+    if (dtype != NF4_F32 && dtype != NF4_BF16) return fail(NF4_ERR_ARG, "dtype must be NF4_F32 or NF4_BF16");
+    if (!levels) return fail(NF4_ERR_ARG, "levels is NULL");
+    if (n < 0) return fail(NF4_ERR_ARG, "n must be >= 0");
+    if (!out || !aligned(out, 8)) return fail(NF4_ERR_ARG, "out must be an 8-byte aligned device struct");
+    Nf4Table tab;
+    for (int i = 0; i < 16; ++i) {
+        if (!isfinite(levels[i])) return fail(NF4_ERR_ARG, "levels must be finite");
+        tab.lv[i] = levels[i];
+    }
+    if (n == 0) {
+        nf4_codebook_stats_t zero;
+        memset(&zero, 0, sizeof(zero));
+        return hip_status(hipMemcpyAsync(out, &zero, sizeof(zero), hipMemcpyHostToDevice, (hipStream_t)stream),
+                          "nf4_codebook_stats");
+    }
+    if (!w || !codes || !absmax) return fail(NF4_ERR_ARG, "NULL w/codes/absmax");
+    if (!aligned(w, 16)) return fail(NF4_ERR_ARG, "w must be 16-byte aligned");
+    if (!aligned(codes, 4) || !aligned(absmax, 4)) return fail(NF4_ERR_ARG, "codes/absmax must be 4-byte aligned");
+    const size_t need = nf4::codebook_stats_ws_bytes(n);
+    if (!workspace || workspace_bytes < need)
+        return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_CODEBOOK_STATS)");
+    if (!aligned(workspace, 8)) return fail(NF4_ERR_ARG, "workspace must be 8-byte aligned");
+    return hip_status(nf4::launch_codebook_stats(w, dtype == NF4_BF16, n, codes, absmax, tab,
+                                                 (nf4::CodebookStats*)workspace, (nf4::CodebookStats*)out,
+                                                 (hipStream_t)stream),
+                      "nf4_codebook_stats");
 }
 
 nf4_status nf4_double_quantize(const float* absmax, int64_t n1, int32_t blocksize2, uint8_t* q,

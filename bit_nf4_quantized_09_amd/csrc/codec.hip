@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ w, int64
             const uint32_t code = bk.x + (x > __uint_as_float(bk.y) ? 1u : 0u);
             packed |= code << (4 * e);
         }
-        if (m == 0.0f) packed = 0x77777777u;   // an all-zero block: the exact-zero level
+        if (m == 0.0f) packed = tab.zero_word;  // an all-zero block: the code of x = 0 (NF4: 7)
         uint8_t* dst = codes + base / 2;
         if (full) {
             *reinterpret_cast<uint32_t*>(dst) = packed;

@@ -84,6 +84,19 @@ hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint1
                                const uint16_t* Al, int r, uint16_t* dX, void* split_ws, const Nf4Table& tab,
                                hipStream_t st);
 
+// ---- codebook statistics ----------------------------------------------------
+// Layout shared with nf4_codebook_stats_t of the C ABI.
+struct CodebookStats {
+    int64_t count[16];
+    double sum_x[16];
+    double sse;
+};
+size_t codebook_stats_ws_bytes(int64_t n);
+// part: codebook_stats_ws_bytes(n) bytes of workspace; out: device CodebookStats.
+hipError_t launch_codebook_stats(const void* w, bool w_bf16, int64_t n, const uint8_t* codes,
+                                 const float* absmax, const Nf4Table& tab, CodebookStats* part,
+                                 CodebookStats* out, hipStream_t s);
+
 // ---- adapter optimizer step (AdamW over fp32 state) -------------------------
 // Scalars of one step, formed on the host: omb1 = 1 - b1, omb2 = 1 - b2,
 // step_size = lr / (1 - b1^t), inv_sqrt_bc2 = 1 / sqrt(1 - b2^t), decay = 1 - lr wd.

@@ -16,8 +16,9 @@ namespace nf4 {
 // 16 levels (ascending) and the 15 fp32 thresholds t_j: x > t_j exactly when
 // x lies above the float64 midpoint between levels j and j+1.
 struct Nf4Table {
-    float lv[16];
-    float th[15];
+    float lv[16];          // levels, ascending
+    float th[15];          // th[j]: the largest fp32 not above the midpoint of lv[j], lv[j+1]
+    uint32_t zero_word;    // eight codes of x = 0 (the code an all-zero block takes)
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

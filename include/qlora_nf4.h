@@ -71,6 +71,7 @@ typedef struct nf4_weight {
 #define NF4_OP_DOUBLE_QUANTIZE 1
 #define NF4_OP_LINEAR_FWD 2
 #define NF4_OP_LINEAR_BWD 3
+#define NF4_OP_CODEBOOK_STATS 4
 
 /* [BQ]+[NF]: blockwise absmax NF4 quantization (stub nf4_quantize(w, block=64)).
  * For each block of 64 consecutive values (the last may be partial):
@@ -85,6 +86,45 @@ typedef struct nf4_weight {
  *   absmax  out: ceil(n/64) fp32 first-level constants c1 */
 nf4_status nf4_quantize(const void* w, nf4_dtype dtype, int64_t n, int32_t blocksize,
                         uint8_t* codes, float* absmax, void* stream);
+
+/* [BQ]+[NF] comparison: the same quantization onto a caller's codebook of 16
+ * ascending levels (the page compares NF4 with the integer grids {-7..7}/7 and
+ * {-8..7}/8 and with a Lloyd codebook).  Each value becomes the code of the
+ * nearest level of w/absmax (a value exactly between two levels takes the lower
+ * code); an all-zero block takes the code of x = 0.  Arguments as for
+ * nf4_quantize, plus
+ *   levels  host array of 16 finite, strictly ascending fp32 levels.  Levels
+ *           outside [-1, 1] are allowed (never nearest past the last one inside).
+ * The kernel finds the nearest level through 1/32-wide buckets of [-1, 1] and an
+ * exact division for normal quotients, so a codebook is rejected
+ * (NF4_ERR_UNSUPPORTED) when two midpoints of adjacent levels fall within one
+ * bucket [k/32, (k+1)/32), or a midpoint lies within the fp32 subnormal range
+ * around 0. */
+nf4_status nf4_quantize_codebook(const void* w, nf4_dtype dtype, int64_t n, int32_t blocksize,
+                                 const float* levels, uint8_t* codes, float* absmax, void* stream);
+
+/* Statistics of such a quantization (device struct, written by
+ * nf4_codebook_stats): per code the number of values and the sum of
+ * x = fp32(w / absmax) (a Lloyd step moves each level to sum_x / count), and the
+ * float64 sum of (w - fp32(level[code] * absmax))^2.  Values of all-zero blocks
+ * count, with x = 0 and no error. */
+typedef struct nf4_codebook_stats_t {
+    int64_t count[16];
+    double sum_x[16];
+    double sse;
+} nf4_codebook_stats_t;
+
+/* One pass over (w, codes, absmax) of nf4_quantize_codebook (or nf4_quantize
+ * with the NF4 levels of nf4_codebook) into *out.  Sums are float64 in a fixed
+ * order, so the result does not depend on timing.
+ *   w, dtype, n, codes, absmax  as for nf4_quantize (blocksize 64)
+ *   levels     host array of the 16 levels the codes index
+ *   out        device nf4_codebook_stats_t, overwritten
+ *   workspace  nf4_workspace_bytes(NF4_OP_CODEBOOK_STATS, 0, n, 0, 0) bytes,
+ *              8-byte aligned */
+nf4_status nf4_codebook_stats(const void* w, nf4_dtype dtype, int64_t n, const uint8_t* codes,
+                              const float* absmax, const float* levels, nf4_codebook_stats_t* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* [DQ]: double quantization of the first-level constants (stub
  * double_quantize(c1, block=256)).  mean = fp32(S / n1), S the float64 sum of
@@ -172,7 +212,7 @@ nf4_status nf4_adamw_step_paged(float* p_host, const float* g, float* m_host, fl
                                 size_t stage_bytes, void* stream);
 
 /* Bytes of device workspace an operation needs (0 = none).  For
- * NF4_OP_DOUBLE_QUANTIZE pass n1 as N.  The linear products keep their
+ * NF4_OP_DOUBLE_QUANTIZE pass n1 as N; for NF4_OP_CODEBOOK_STATS pass n as N.  The linear products keep their
  * intermediates there: the rank-r activations (s*T, T, s*U), the decoded
  * first-level constants c1' of W (4 bytes per 64-block, written before the
  * fused MFMA product; not needed by the M <= 16 forward) and fp32 partial sums

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
                             "nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
                             "nf4_workspace_bytes", "nf4_storage_bytes", "nf4_codebook",
                             "nf4_last_error", "nf4_profile_next_fused", "nf4_adamw_step",
-                            "nf4_adamw_step_paged"])
+                            "nf4_adamw_step_paged", "nf4_quantize_codebook", "nf4_codebook_stats"])
     for name in names:
         assert hasattr(L, name), name
     # and the C symbols are unmangled (extern "C")
@@ -188,3 +188,31 @@ def test_adamw_rejects_bad_arguments():
     assert paged(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, None, 1 << 20, None) == nf4.NF4_ERR_ARG
     assert paged(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, ctypes.c_void_p((8 << 20) + 16),
                  1 << 20, None) == nf4.NF4_ERR_ARG                                            # stage alignment
+
+
+def test_codebook_entry_points_reject_bad_arguments():
+    L = nf4.load_library()
+    p = ctypes.c_void_p(1 << 20)
+    lv = lambda xs: (ctypes.c_float * 16)(*xs)
+    good = lv([k / 8 for k in range(-8, 8)])
+    q = L.nf4_quantize_codebook
+    assert q(p, 0, 0, 64, good, p, p, None) == nf4.NF4_OK                         # n == 0
+    assert q(p, 0, 64, 32, good, p, p, None) == nf4.NF4_ERR_UNSUPPORTED           # blocksize
+    assert q(p, 0, 64, 64, None, p, p, None) == nf4.NF4_ERR_ARG
+    desc = lv([k / 8 for k in range(7, -9, -1)])
+    assert q(p, 0, 64, 64, desc, p, p, None) == nf4.NF4_ERR_UNSUPPORTED            # not ascending
+    # two midpoints inside one 1/32 bucket: levels 0, 0.01, 0.02 around the middle
+    crowded = [k / 8 for k in range(-8, 0)] + [0.0, 0.01, 0.02] + [k / 8 for k in range(1, 6)]
+    assert q(p, 0, 64, 64, lv(crowded), p, p, None) == nf4.NF4_ERR_UNSUPPORTED
+    assert "bucket" in L.nf4_last_error().decode()
+    # a symmetric table without a zero level puts a midpoint exactly at 0
+    sym = [(k + 0.5) / 8 for k in range(-8, 8)]
+    assert q(p, 0, 64, 64, lv(sym), p, p, None) == nf4.NF4_ERR_UNSUPPORTED
+    assert "subnormal" in L.nf4_last_error().decode()
+    st = L.nf4_codebook_stats
+    assert nf4.nf4_workspace_bytes(nf4.NF4_OP_CODEBOOK_STATS, 0, 0, 0, 0) == 0
+    wsb = nf4.nf4_workspace_bytes(nf4.NF4_OP_CODEBOOK_STATS, 0, 1 << 20, 0, 0)
+    assert wsb > 0
+    assert st(p, 0, 1 << 20, p, p, good, p, p, wsb - 8, None) == nf4.NF4_ERR_WORKSPACE
+    assert st(p, 0, 1 << 20, p, p, None, p, p, wsb, None) == nf4.NF4_ERR_ARG
+    assert st(p, 0, 1 << 20, p, p, good, None, p, wsb, None) == nf4.NF4_ERR_ARG
