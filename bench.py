@@ -304,7 +304,11 @@ def event_pool(n):
     return iter(pool)
 
 
-def run_step(layer, alpha, events=None, pool=None):
+def run_step(layer, alpha, events=None, pool=None, weight="Wq", recompute=False):
+    """The layer's seven forwards, then its seven backwards.  `weight` picks the weight
+    tuple (double-quantized "Wq", or "Wq_plain" with the constants kept as fp32);
+    recompute=True keeps nothing of the forward but its output and recomputes T = X A^T
+    in the backward (gradient checkpointing of the adapter activations)."""
     import bit_nf4_quantized_09_amd as nf4
 
     saved = []
@@ -313,7 +317,7 @@ def run_step(layer, alpha, events=None, pool=None):
             ev = next(pool)
             events["fwd"].append((ev, p))
             nf4.nf4_profile_next_fused(*ev)
-        Y, T = nf4.qlora_linear_fwd(p["Wq"], p["X"], p["A"], p["B"], alpha)
+        Y, T = nf4.qlora_linear_fwd(p[weight], p["X"], p["A"], p["B"], alpha, save_t=not recompute)
         saved.append((Y, T))
     grads = []
     for p, (Y, T) in zip(reversed(layer), reversed(saved)):
@@ -321,8 +325,38 @@ def run_step(layer, alpha, events=None, pool=None):
             ev = next(pool)
             events["bwd"].append((ev, p))
             nf4.nf4_profile_next_fused(*ev)
-        grads.append(nf4.qlora_linear_bwd(p["Wq"], p["X"], p["dY"], p["A"], p["B"], alpha, T=T))
+        grads.append(nf4.qlora_linear_bwd(p[weight], p["X"], p["dY"], p["A"], p["B"], alpha, T=T))
     return saved, grads
+
+
+def variant_paths(layer, alpha, flops, steps=5):
+    """The step with double quantization off (plain fp32 constants, "Double
+    quantization") and with T recomputed in the backward (gradient checkpointing of the
+    adapter activations): TFLOP/s over `steps` timed steps each, and the weight storage
+    of the layer with and without double quantization."""
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+
+    for p in layer:
+        p["Wq_plain"] = nf4.quantize_weight(p["W"], double_quant=False)
+    torch.cuda.synchronize()
+    out = {}
+    for name, kw in (("dq_off", dict(weight="Wq_plain")), ("recompute_t", dict(recompute=True))):
+        run_step(layer, alpha, **kw)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run_step(layer, alpha, **kw)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        out[name] = dict(tflops=flops / dt / 1e12, ms_per_step=dt * 1e3)
+    n = sum(p["N"] * p["K"] for p in layer)
+    dq = sum(p["Wq"].nbytes() for p in layer)
+    plain = sum(p["Wq_plain"].nbytes() for p in layer)
+    out["weight_bits_per_param"] = dict(dq_on=8 * dq / n, dq_off=8 * plain / n)
+    for p in layer:
+        del p["Wq_plain"]
+    return out
 
 
 def kernel_roofline(events, M, r, kind):
@@ -654,7 +688,8 @@ def main():
     }
     if not args.no_paths and args.workload != "tiny":
         line["paths"] = {"codec": codec_paths(layer, dev), "gemv": gemv_paths(layer, dev, r, alpha),
-                         "adamw": adamw_paths(layer, dev, r), "codebooks": codebook_paths(dev)}
+                         "adamw": adamw_paths(layer, dev, r), "codebooks": codebook_paths(dev),
+                         "variants": variant_paths(layer, alpha, fwd_flops + bwd_flops)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layer, alpha, r, min(args.cpu_tokens, M))
     print(json.dumps(line), flush=True)

@@ -49,7 +49,8 @@ class NF4Error(RuntimeError):
 
 class _Weight(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("q", ctypes.c_void_p), ("c2", ctypes.c_void_p),
-                ("mean", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+                ("mean", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("absmax", ctypes.c_void_p)]
 
 
 _lib = None
@@ -141,24 +142,29 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 @dataclass
 class NF4Weight:
-    """A frozen weight as double-quantized NF4: codes, q, c2, mean on the GPU."""
-    codes: torch.Tensor   # uint8 [ceil(n/2)]
-    q: torch.Tensor       # uint8 [ceil(n/64)]
-    c2: torch.Tensor      # float32 [ceil(n1/256)]
-    mean: torch.Tensor    # float32 [1]
+    """A frozen weight as NF4 on the GPU: codes with double-quantized constants (q, c2,
+    mean), or, with double quantization off, with the plain fp32 constants (absmax;
+    q, c2 and mean None)."""
+    codes: torch.Tensor             # uint8 [ceil(n/2)]
+    q: Optional[torch.Tensor]       # uint8 [ceil(n/64)]
+    c2: Optional[torch.Tensor]      # float32 [ceil(n1/256)]
+    mean: Optional[torch.Tensor]    # float32 [1]
     shape: Tuple[int, int]
+    absmax: Optional[torch.Tensor] = None   # float32 [ceil(n/64)], when q is None
 
     def descriptor(self) -> _Weight:
         rows, cols = self.shape
-        return _Weight(self.codes.data_ptr(), self.q.data_ptr(), self.c2.data_ptr(),
-                       self.mean.data_ptr(), rows, cols)
+        ptr = lambda t: t.data_ptr() if t is not None else None
+        return _Weight(self.codes.data_ptr(), ptr(self.q), ptr(self.c2), ptr(self.mean), rows, cols,
+                       ptr(self.absmax) if self.q is None else None)
 
     @property
     def device(self):
         return self.codes.device
 
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.codes, self.q, self.c2, self.mean))
+        parts = (self.codes, self.q, self.c2, self.mean) if self.q is not None else (self.codes, self.absmax)
+        return sum(t.numel() * t.element_size() for t in parts)
 
 
 def nf4_profile_next_fused(start: "torch.cuda.Event", stop: "torch.cuda.Event"):
@@ -230,13 +236,17 @@ def nf4_double_dequantize(q: torch.Tensor, c2: torch.Tensor, mean: torch.Tensor,
     return out
 
 
-def quantize_weight(w: torch.Tensor) -> NF4Weight:
-    """Quantize a 2-D (out x in) fp32/bf16 weight to the double-quantized NF4 tuple."""
+def quantize_weight(w: torch.Tensor, double_quant: bool = True) -> NF4Weight:
+    """Quantize a 2-D (out x in) fp32/bf16 weight to NF4: the double-quantized tuple, or
+    with double_quant=False the codes and plain fp32 constants."""
     if w.dim() != 2:
         raise ValueError("weight must be 2-D (out x in)")
     codes, absmax = nf4_quantize(w)
+    shape = (int(w.shape[0]), int(w.shape[1]))
+    if not double_quant:
+        return NF4Weight(codes, None, None, None, shape, absmax)
     q, c2, mean = nf4_double_quantize(absmax)
-    return NF4Weight(codes, q, c2, mean, (int(w.shape[0]), int(w.shape[1])))
+    return NF4Weight(codes, q, c2, mean, shape)
 
 
 def nf4_dequantize(W: NF4Weight, dtype=torch.float32) -> torch.Tensor:

@@ -115,9 +115,15 @@ nf4_status check_weight(const nf4_weight* W, WeightView& v, bool linear) {
     if (!W) return fail(NF4_ERR_ARG, "weight descriptor is NULL");
     if (W->rows < 0 || W->cols < 0) return fail(NF4_ERR_ARG, "negative weight shape");
     const int64_t n = W->rows * W->cols;
-    if (n > 0 && (!W->codes || !W->q || !W->c2 || !W->mean))
-        return fail(NF4_ERR_ARG, "weight has a NULL codes/q/c2/mean pointer");
-    if (!W->mean) return fail(NF4_ERR_ARG, "weight mean pointer is NULL");
+    const bool plain = W->q == nullptr;
+    if (plain) {
+        if (n > 0 && (!W->codes || !W->absmax)) return fail(NF4_ERR_ARG, "weight has a NULL codes/absmax pointer");
+        if (!aligned(W->absmax, 4)) return fail(NF4_ERR_ARG, "misaligned absmax");
+    } else {
+        if (n > 0 && (!W->codes || !W->c2 || !W->mean))
+            return fail(NF4_ERR_ARG, "weight has a NULL codes/q/c2/mean pointer");
+        if (!W->mean) return fail(NF4_ERR_ARG, "weight mean pointer is NULL");
+    }
     if (linear) {
         if (W->cols % 64 != 0) return fail(NF4_ERR_UNSUPPORTED, "K (cols) must be a multiple of 64");
         if (W->rows % 8 != 0) return fail(NF4_ERR_UNSUPPORTED, "N (rows) must be a multiple of 8");
@@ -126,13 +132,14 @@ nf4_status check_weight(const nf4_weight* W, WeightView& v, bool linear) {
         if (n / 2 >= ((int64_t)1 << 31)) return fail(NF4_ERR_UNSUPPORTED, "weight larger than 2^32 values");
     }
     if (!aligned(W->codes, 16)) return fail(NF4_ERR_ARG, "codes must be 16-byte aligned");
-    if (!aligned(W->c2, 4) || !aligned(W->mean, 4)) return fail(NF4_ERR_ARG, "misaligned c2/mean");
+    if (!plain && (!aligned(W->c2, 4) || !aligned(W->mean, 4))) return fail(NF4_ERR_ARG, "misaligned c2/mean");
     v.codes = W->codes;
     v.q = W->q;
-    v.c2 = W->c2;
-    v.mean = W->mean;
+    v.c2 = plain ? nullptr : W->c2;
+    v.mean = plain ? nullptr : W->mean;
     v.rows = W->rows;
     v.cols = W->cols;
+    v.absmax = plain ? W->absmax : nullptr;
     return NF4_OK;
 }
 
@@ -359,8 +366,12 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     e = nf4::launch_lora_gemm(x, false, (const uint16_t*)A, false, M, r, v.cols, part, 1.0f, Tb,
                               false, false, Ts, s, hs);
     if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
-    e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
-    if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (constants)");
+    if (v.absmax) {
+        c1 = (float*)v.absmax;            // plain constants: read as they are
+    } else {
+        e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
+        if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (constants)");
+    }
     e = nf4::launch_fused_fwd(v, c1, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, part, table(), hs);
     return hip_status(e, "qlora_linear_fwd (gemm)");
 }
@@ -410,9 +421,13 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
             Tb = Tw;
         }
         if (dX) {
-            e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
-            if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (constants)");
-            e = nf4::launch_fused_bwd_dx(v, c1, g, M, Us, al, r, (uint16_t*)dX, part, table(), hs);
+            const float* c1b = v.absmax;   // plain constants: read as they are
+            if (!c1b) {
+                e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
+                if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (constants)");
+                c1b = c1;
+            }
+            e = nf4::launch_fused_bwd_dx(v, c1b, g, M, Us, al, r, (uint16_t*)dX, part, table(), hs);
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dX)");
         }
     }

@@ -293,11 +293,12 @@ hipError_t launch_double_dequantize(const uint8_t* q, const float* c2, const flo
 // its first store.  Levels come from a 256-entry LDS table of code byte -> the two
 // fp32 levels.
 // ---------------------------------------------------------------------------
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool PLAIN>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ q,
                                                     const float* __restrict__ c2,
-                                                    const float* __restrict__ mean_p, int64_t n,
+                                                    const float* __restrict__ mean_p,
+                                                    const float* __restrict__ absmax, int64_t n,
                                                     void* __restrict__ out, Nf4Table tab) {
     constexpr int E = OUT_BF16 ? 8 : 4;            // values per group (16 bytes of output)
     constexpr int CHUNK = 256 * 8 * E;             // values per chunk
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
         s_pair[threadIdx.x] = make_float2(lo, hi);
     }
     __syncthreads();
-    const float mean = *mean_p;
+    const float mean = PLAIN ? 0.0f : *mean_p;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t nblk = (n + 63) / 64;
     const int64_t nbytes = (n + 1) / 2;
@@ -338,14 +339,19 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
             }
             // the group's block, clamped into the arrays (a group past n stores nothing)
             const int64_t blk = WHOLE ? i0 / 64 : (i0 / 64 < nblk ? i0 / 64 : nblk - 1);
-            qb[j] = q[blk];
-            cs[j] = c2[WHOLE ? (blk >> 8) : ((blk >> 8) < n2 ? (blk >> 8) : n2 - 1)];
+            if constexpr (PLAIN) {
+                cs[j] = absmax[blk];          // the constant itself
+                qb[j] = 0;
+            } else {
+                qb[j] = q[blk];
+                cs[j] = c2[WHOLE ? (blk >> 8) : ((blk >> 8) < n2 ? (blk >> 8) : n2 - 1)];
+            }
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int64_t i0 = c0 + ((int64_t)(8 * wave + j) * 64 + lane) * E;
             if (!WHOLE && i0 >= n) continue;
-            const float c1p = decode_c1(qb[j], c2_step(cs[j]), mean);
+            const float c1p = PLAIN ? cs[j] : decode_c1(qb[j], c2_step(cs[j]), mean);
             float v[E];
 #pragma unroll
             for (int e = 0; e < E / 2; ++e) {
@@ -388,12 +394,19 @@ hipError_t launch_dequantize(const WeightView& W, void* out, bool out_bf16, cons
     const int64_t chunk = out_bf16 ? 256 * 8 * 8 : 256 * 8 * 4;
     const int64_t need = ceil_div(n, chunk);
     const unsigned grid = (unsigned)(need < 2048 ? need : 2048);
-    if (out_bf16)
-        hipLaunchKernelGGL(k_dequantize<true>, dim3(grid), dim3(256), 0, s, W.codes, W.q, W.c2,
-                           W.mean, n, out, tab);
+    const bool plain = W.absmax != nullptr;
+    if (out_bf16 && plain)
+        hipLaunchKernelGGL((k_dequantize<true, true>), dim3(grid), dim3(256), 0, s, W.codes, W.q, W.c2,
+                           W.mean, W.absmax, n, out, tab);
+    else if (out_bf16)
+        hipLaunchKernelGGL((k_dequantize<true, false>), dim3(grid), dim3(256), 0, s, W.codes, W.q, W.c2,
+                           W.mean, W.absmax, n, out, tab);
+    else if (plain)
+        hipLaunchKernelGGL((k_dequantize<false, true>), dim3(grid), dim3(256), 0, s, W.codes, W.q, W.c2,
+                           W.mean, W.absmax, n, out, tab);
     else
-        hipLaunchKernelGGL(k_dequantize<false>, dim3(grid), dim3(256), 0, s, W.codes, W.q, W.c2,
-                           W.mean, n, out, tab);
+        hipLaunchKernelGGL((k_dequantize<false, false>), dim3(grid), dim3(256), 0, s, W.codes, W.q, W.c2,
+                           W.mean, W.absmax, n, out, tab);
     return hipGetLastError();
 }
 

@@ -72,6 +72,7 @@ struct GvArgs {
     float* part;             // [slices][M][N + r]
     uint16_t* Y;             // [M x N]
     uint16_t* T;             // [M x r]
+    const float* absmax;     // plain first-level constants (no double quantization), or null
 };
 
 // Four code bytes (8 codes) -> the MFMA operand of their 8 unscaled bf16 levels.  The
@@ -105,7 +106,7 @@ constexpr int gv_lds_bytes(int MT) { return MT * (GV_RB * 128 + 16); }
 // w RB/WV ..) and summed across the waves in LDS, so that an adapter workgroup moves
 // about as many bytes as a weight workgroup.  Straight-line code from the first
 // request to the last wait, so that every wait names exactly the requests it needs.
-template <int RB, int MT, bool ADAPTER>
+template <int RB, int MT, bool ADAPTER, bool PLAIN>
 __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& tab, int64_t group,
                                                uint32_t* s_pair, float* s_e4m3) {
     constexpr int CP = GV_CP;
@@ -141,7 +142,19 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
     uint32_t qw[TT][RB / 4 + 1];
     uint4 al[RBW][2];
     float mean = 0.0f, c2f[TT], c2l[TT];
-    if constexpr (!ADAPTER) {
+    float cpl[PLAIN ? TT : 1][PLAIN ? RB : 1];           // plain constants of the slice
+    if constexpr (!ADAPTER && PLAIN) {
+        // the row's RB constants of the slice; past the row: the next row's (finite, given
+        // a zero factor below); past the last row: zero
+        const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.absmax, a.N * KB * 4);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const uint32_t ca = (uint32_t)(((n0 + 16 * t) * KB + b0) * 4);
+#pragma unroll
+            for (int j = 0; j < RB; ++j) cpl[t][j] = buf_loadf(rs_a, ca + 4 * j, 0);
+        }
+    }
+    if constexpr (!ADAPTER && !PLAIN) {
         mean = *a.mean;
         // second-level constants: a row's slice meets at most two 256-blocks
         const int64_t n2 = (a.N * KB + 255) >> 8;
@@ -157,6 +170,8 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
 #pragma unroll
             for (int i = 0; i < RB / 4 + 1; ++i) qw[t][i] = buf_load4(rs_q, qa + 4 * i, 0);
         }
+    }
+    if constexpr (!ADAPTER) {
         // the codes, block pair by block pair (the order they are used in).  A pair past
         // the row reads the next row (finite codes, given a zero constant below) or, past
         // the last row, zero.
@@ -219,7 +234,7 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
         int jsplit[TT];
         uint32_t q4[TT][RB / 4];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
+        for (int t = 0; t < TT && !PLAIN; ++t) {
             st_first[t] = c2_step(c2f[t]);
             st_last[t] = c2_step(c2l[t]);
             const int64_t ci0 = (n0 + 16 * t) * KB + b0;  // constant index of the slice's first block
@@ -234,8 +249,13 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
         // valid: blocks past the row contribute zero (a factor, not a branch: the decoded
         // constant of any byte is finite)
         auto c1_of = [&](int t, int j, bool all_valid) {
-            const uint32_t qbyte = (q4[t][j / 4] >> (8 * (j & 3))) & 0xFFu;
-            const float c = __fmaf_rn(s_e4m3[qbyte], j < jsplit[t] ? st_first[t] : st_last[t], mean);
+            float c;
+            if constexpr (PLAIN) {
+                c = cpl[t][j];
+            } else {
+                const uint32_t qbyte = (q4[t][j / 4] >> (8 * (j & 3))) & 0xFFu;
+                c = __fmaf_rn(s_e4m3[qbyte], j < jsplit[t] ? st_first[t] : st_last[t], mean);
+            }
             return all_valid ? c : c * (float)(j < nb);
         };
         auto run = [&](bool all_valid) {
@@ -309,14 +329,14 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
 // grid (slice, row group): the slices of one row group are dispatched together, so the
 // workgroups in flight read whole rows of codes (long runs within one DRAM page);
 // the adapter row groups come first.
-template <int RB, int MT>
+template <int RB, int MT, bool PLAIN>
 __global__ __launch_bounds__(64 * GV_WV) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void k_gemv_part(GvArgs a, Nf4Table tab) {
     __shared__ __attribute__((aligned(16))) uint32_t s_pair[256 * GV_CP];   // code byte -> two bf16 levels
     __shared__ float s_e4m3[256];                      // 8-bit constant -> E4M3 value
     const int64_t nag = (a.r + GV_AROWS - 1) / GV_AROWS;
-    if ((int64_t)blockIdx.y < nag) gemv_part_body<RB, MT, true>(a, tab, blockIdx.y, s_pair, s_e4m3);
-    else gemv_part_body<RB, MT, false>(a, tab, (int64_t)blockIdx.y - nag, s_pair, s_e4m3);
+    if ((int64_t)blockIdx.y < nag) gemv_part_body<RB, MT, true, PLAIN>(a, tab, blockIdx.y, s_pair, s_e4m3);
+    else gemv_part_body<RB, MT, false, PLAIN>(a, tab, (int64_t)blockIdx.y - nag, s_pair, s_e4m3);
 }
 
 // k_gemv_reduce<ROWS, NO, NT>: workgroup of ROWS weight rows; thread (row n = n0 + tid %
@@ -403,17 +423,17 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(GvArgs a, int64_t slices) {
     }
 }
 
-template <int MT>
+template <int MT, bool PLAIN>
 static hipError_t launch_gemv_part(dim3 grid, const GvArgs& ga, const Nf4Table& tab, hipStream_t st) {
     const int lds = gv_lds_bytes(MT);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_gemv_part<GV_RB, MT>,
+        hipError_t e = hipFuncSetAttribute((const void*)k_gemv_part<GV_RB, MT, PLAIN>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemv_part<GV_RB, MT>), grid, dim3(64 * GV_WV), lds, st, ga, tab);
+    hipLaunchKernelGGL((k_gemv_part<GV_RB, MT, PLAIN>), grid, dim3(64 * GV_WV), lds, st, ga, tab);
     return hipGetLastError();
 }
 
@@ -422,7 +442,7 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
                              const Nf4Table& tab, hipStream_t st) {
     if (M == 0) return hipSuccess;
     const int64_t slices = gemv_slices(M, W.cols);
-    GvArgs ga{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, X, (int)M, Al, Bl, r, s, part, Y, T};
+    GvArgs ga{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, X, (int)M, Al, Bl, r, s, part, Y, T, W.absmax};
     const bool small = M <= 4;
     const int64_t wrows = small ? gv_rows(4) : gv_rows(16);
     dim3 g1((unsigned)slices, (unsigned)((r + GV_AROWS - 1) / GV_AROWS + (W.rows + wrows - 1) / wrows));
@@ -432,7 +452,11 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
     dim3 g2((unsigned)((W.rows + rrows - 1) / rrows > 0 ? (W.rows + rrows - 1) / rrows : 1));
     return with_events(st, [&] {
         if (g1.x > 0 && g1.y > 0) {
-            hipError_t e = small ? launch_gemv_part<4>(g1, ga, tab, st) : launch_gemv_part<16>(g1, ga, tab, st);
+            const bool plain = W.absmax != nullptr;
+            hipError_t e = small ? (plain ? launch_gemv_part<4, true>(g1, ga, tab, st)
+                                          : launch_gemv_part<4, false>(g1, ga, tab, st))
+                                 : (plain ? launch_gemv_part<16, true>(g1, ga, tab, st)
+                                          : launch_gemv_part<16, false>(g1, ga, tab, st));
             if (e != hipSuccess) return e;
         }
         if (small) hipLaunchKernelGGL((k_gemv_reduce<32, 1, 2>), g2, dim3(256), 0, st, ga, slices);

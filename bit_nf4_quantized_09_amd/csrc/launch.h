@@ -18,6 +18,7 @@ struct WeightView {
     const float* mean;
     int64_t rows;   // N
     int64_t cols;   // K
+    const float* absmax;   // plain first-level constants (no double quantization), or null
 };
 
 // ---- codec ----------------------------------------------------------------

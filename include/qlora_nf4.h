@@ -56,15 +56,20 @@ typedef enum nf4_status {
 
 typedef enum nf4_dtype { NF4_F32 = 0, NF4_BF16 = 1 } nf4_dtype;
 
-/* A double-quantized NF4 weight: the storage tuple of [DQ] + [RW].
- * n = rows * cols values; n1 = ceil(n/64) first-level constants. */
+/* An NF4 weight: the storage tuple of [DQ] + [RW], double-quantized, or with the
+ * first-level constants kept as plain fp32 ([DQ] off: 0.5 instead of about 0.127
+ * bits of constants per value).  n = rows * cols values; n1 = ceil(n/64)
+ * first-level constants.  q != NULL selects the double-quantized constants
+ * (q, c2, mean; absmax ignored); q == NULL selects absmax (c2 and mean ignored,
+ * may be NULL). */
 typedef struct nf4_weight {
     const uint8_t* codes;  /* ceil(n/2) bytes; element 2i in the low nibble of byte i */
-    const uint8_t* q;      /* n1 bytes: OCP FP8 E4M3 codes of 448*(c1 - mean)/c2 */
+    const uint8_t* q;      /* n1 bytes: OCP FP8 E4M3 codes of 448*(c1 - mean)/c2, or NULL */
     const float* c2;       /* ceil(n1/256) fp32 second-level constants */
     const float* mean;     /* 1 fp32: mean of the first-level constants */
     int64_t rows;          /* N (out features) */
     int64_t cols;          /* K (in features) */
+    const float* absmax;   /* with q == NULL: n1 fp32 first-level constants (nf4_quantize) */
 } nf4_weight;
 
 /* Workspace selectors for nf4_workspace_bytes(). */
@@ -148,8 +153,9 @@ nf4_status nf4_double_dequantize(const uint8_t* q, const float* c2, const float*
 
 /* [BQ]+[DQ]: dequantization of a whole weight (stub nf4_dequantize(codes,
  * absmax, shape), with the double-quantized constants in place of absmax):
- * out[i] = fp32(level[code_i] * c1'[i/64]); NF4_BF16 output rounds that value
- * to nearest even.
+ * out[i] = fp32(level[code_i] * c1'[i/64]), c1' the decoded constant (or the
+ * plain absmax when W->q is NULL); NF4_BF16 output rounds that value to nearest
+ * even.
  *   out     rows*cols values of out_dtype */
 nf4_status nf4_dequantize(const nf4_weight* W, void* out, nf4_dtype out_dtype, void* stream);
 

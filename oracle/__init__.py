@@ -49,6 +49,7 @@ def _load():
                                          ctypes.c_double, _i64p, _i64, _f64p, _f64p]
     lib.orc_qlora_linear_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _i64, _i64, _i64,
                                          _i64, ctypes.c_double, _i64p, _i64, _f64p, _f64p, _f64p]
+    lib.orc_nf4_dequantize_plain.argtypes = [_u8p, _f32p, _i64, _f32p]
     lib.orc_quantize_levels.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64, _f32p, _u8p, _f32p]
     lib.orc_codebook_stats.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64, _u8p, _f32p, _f32p, _i64p,
                                        _f64p, _f64p]
@@ -257,3 +258,14 @@ def codebook_stats(w: np.ndarray, codes: np.ndarray, absmax: np.ndarray, levels:
                                _p(absmax, _f32p), _p(levels, _f32p), _p(count, _i64p), _p(sum_x, _f64p),
                                _p(sse, _f64p))
     return count, sum_x, float(sse[0])
+
+
+def nf4_dequantize_plain(codes, absmax, shape) -> np.ndarray:
+    """w' = fp32(level[code] * absmax[i/64]) with plain constants (double quantization
+    off, "Double quantization"); returns float32 `shape`."""
+    n = int(np.prod(shape))
+    codes = np.ascontiguousarray(codes, np.uint8)
+    absmax = np.ascontiguousarray(absmax, np.float32)
+    out = np.empty(n, np.float32)
+    _load().orc_nf4_dequantize_plain(_p(codes, _u8p), _p(absmax, _f32p), n, _p(out, _f32p))
+    return out.reshape(shape)

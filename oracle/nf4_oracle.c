@@ -388,6 +388,20 @@ void orc_nf4_dequantize(const uint8_t* codes, const uint8_t* q, const float* c2,
 /*   T = X A^T (M x r);  Y = X W'^T + s T B^T (M x N).                       */
 /* Rows of Y are computed for the row list `rows` (nrows entries); pass      */
 /* rows == NULL to compute every row.  T is always computed for all rows.   */
+/* [BQ] dequantization with plain first-level constants (double quantization    */
+/* off): w' = fp32(level[code] * absmax[i/64]).                               */
+void orc_nf4_dequantize_plain(const uint8_t* codes, const float* absmax, int64_t n, float* out)
+{
+    float lv[16];
+    orc_nf4_codebook(lv);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const int code = (codes[i >> 1] >> (4 * (i & 1))) & 15;
+        volatile float v = lv[code] * absmax[i / 64];
+        out[i] = v;
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 void orc_qlora_linear_fwd(const float* Wd, const float* X, const float* A, const float* B,
                           int64_t M, int64_t N, int64_t K, int64_t r, double alpha,

@@ -123,3 +123,17 @@ def test_codec_deterministic():
     b = _gpu_tuple(w)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("shape", [(64, 64), (328, 320), (1000, 1088), (4096, 4096)])
+def test_dequantize_plain_constants(shape):
+    # [DQ] off: nf4_dequantize with the plain constants gives fp32(level * absmax) bit for
+    # bit, and its round-to-nearest-even bf16 value
+    w = Draw(seed_of(41, *shape), DEV).normal(shape, 0.02, outlier_frac=0.01)
+    W = nf4.quantize_weight(w, double_quant=False)
+    ref = oracle_weight(w.cpu())
+    exp = oracle.nf4_dequantize_plain(ref["codes"], ref["absmax"], shape)
+    got = nf4.nf4_dequantize(W, torch.float32).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), exp.view(np.uint32))
+    gb = nf4.nf4_dequantize(W, torch.bfloat16)
+    assert torch.equal(gb.cpu().view(torch.int16), torch.from_numpy(exp).bfloat16().view(torch.int16))

@@ -20,16 +20,23 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run(W, X, A, B, dY, alpha, rows=None, check_codes=True, save_t=True):
-    """GPU fwd+bwd on device tensors, oracle on host copies; returns the metrics."""
-    print("linear case N=%d K=%d M=%d r=%d rows=%s" % (W.shape[0], W.shape[1], X.shape[0],
-                                                       A.shape[0], None if rows is None else len(rows)),
-          flush=True)
+def _run(W, X, A, B, dY, alpha, rows=None, check_codes=True, save_t=True, double_quant=True):
+    """GPU fwd+bwd on device tensors, oracle on host copies; returns the metrics.  With
+    double_quant=False the weight keeps plain fp32 constants on both sides."""
+    print("linear case N=%d K=%d M=%d r=%d rows=%s dq=%s" % (W.shape[0], W.shape[1], X.shape[0],
+                                                             A.shape[0], None if rows is None else len(rows),
+                                                             double_quant), flush=True)
     ref = oracle_weight(W.cpu())
-    Wq = nf4.quantize_weight(W)
+    Wq = nf4.quantize_weight(W, double_quant=double_quant)
+    if not double_quant:
+        ref = dict(ref)
+        ref["Wd"] = oracle.nf4_dequantize_plain(ref["codes"], ref["absmax"], tuple(W.shape))
     if check_codes:
         assert np.array_equal(Wq.codes.cpu().numpy(), ref["codes"])
-        assert np.array_equal(Wq.q.cpu().numpy(), ref["q"])
+        if double_quant:
+            assert np.array_equal(Wq.q.cpu().numpy(), ref["q"])
+        else:
+            assert np.array_equal(Wq.absmax.cpu().numpy().view(np.uint32), ref["absmax"].view(np.uint32))
     Y, T = nf4.qlora_linear_fwd(Wq, X, A, B, alpha, save_t=save_t)
     dX, dA, dB = nf4.qlora_linear_bwd(Wq, X, dY, A, B, alpha, T=T)
     torch.cuda.synchronize()
@@ -178,3 +185,12 @@ def test_full_gemv_shapes(M, N, K):
     Yr, Tr = oracle.qlora_linear_fwd(ref["Wd"], host_f32(X), host_f32(A), host_f32(B), 16.0)
     assert_close("Y", to_np(Y), Yr)
     assert_close("T", to_np(T), Tr)
+
+
+@pytest.mark.parametrize("M,N,K,r", [(300, 328, 320, 8), (257, 256, 512, 64), (1, 200, 512, 64),
+                                     (4, 1032, 1088, 16), (16, 1032, 1088, 64), (5, 48, 65600, 40)])
+def test_double_quantization_off(M, N, K, r):
+    # [DQ] off: plain fp32 constants through the fused GEMM (M > 16) and the few-token
+    # forward (M <= 16), against the oracle with w' = level * absmax
+    W, X, A, B, dY = (t.to(DEV) for t in linear_inputs(N, K, M, r, seed=seed_of(40, N, K, M, r)))
+    _run(W, X, A, B, dY, alpha=16.0, double_quant=False)

@@ -156,3 +156,22 @@ def test_tuple_sizes(orc, n):
     assert c2.size == ((n + 63) // 64 + 255) // 256
     if n == 0:
         assert mean[0] == 0.0
+
+
+def test_plain_constants_dequantize_round_trip(orc):
+    # double quantization off ("Double quantization": the 0.5-bit plain constants): w' =
+    # level * absmax.  Each block's absmax element comes back as +-absmax exactly and
+    # every other value stays nearest its level, so re-encoding w' returns the same codes
+    # and the same constants; code 7 is an exact zero
+    rng = np.random.Generator(np.random.PCG64(11))
+    w = rng.normal(0, 0.02, 64 * 300 + 17).astype(np.float32)
+    w[64:128] = 0.0
+    codes, absmax = orc.nf4_quantize(w)
+    wd = orc.nf4_dequantize_plain(codes, absmax, (w.size,))
+    codes2, absmax2 = orc.nf4_quantize(wd)
+    assert np.array_equal(codes2, codes)
+    assert np.array_equal(absmax2.view(np.uint32), absmax.view(np.uint32))
+    c = np.concatenate([codes & 15, codes >> 4], axis=0).reshape(2, -1).T.reshape(-1)[:w.size]
+    assert np.all(wd[c == 7] == 0.0)
+    blk = np.repeat(absmax, 64)[:w.size]
+    assert np.array_equal(wd[c == 15], blk[c == 15]) and np.array_equal(wd[c == 0], -blk[c == 0])
