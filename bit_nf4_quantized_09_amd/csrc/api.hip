@@ -468,6 +468,40 @@ nf4_status adamw_scalars(float lr, float beta1, float beta2, float eps, float we
     return NF4_OK;
 }
 
+// Per device, for the copy-out of paged optimizer state: a helper stream (default
+// priority) and the events that order it against the caller's stream, created on first
+// use and kept for the life of the process.  Calls enqueue their work under the mutex,
+// so every wait pairs with the record its own call made just before.
+struct PagedResources {
+    hipStream_t out = nullptr;
+    hipEvent_t ready[2] = {nullptr, nullptr};
+    hipEvent_t done[2] = {nullptr, nullptr};
+};
+std::mutex g_paged_mu;
+
+hipError_t paged_resources(PagedResources** res) {
+    static PagedResources per_dev[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    PagedResources& r = per_dev[dev];
+    if (!r.out) {
+        for (int b = 0; b < 2; ++b) {
+            if (!r.ready[b]) e = hipEventCreateWithFlags(&r.ready[b], hipEventDisableTiming);
+            if (e == hipSuccess && !r.done[b]) e = hipEventCreateWithFlags(&r.done[b], hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        e = hipStreamCreateWithFlags(&r.out, hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            r.out = nullptr;
+            return e;
+        }
+    }
+    *res = &r;
+    return hipSuccess;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return a && b && x < y + nb && y < x + na;
@@ -512,26 +546,44 @@ nf4_status nf4_adamw_step_paged(float* p_host, const float* g, float* m_host, fl
     if (!aligned(g, 16)) return fail(NF4_ERR_ARG, "g must be 16-byte aligned");
     if (!aligned(p_bf16, 8)) return fail(NF4_ERR_ARG, "p_bf16 must be 8-byte aligned");
     if (!stage || !aligned(stage, 256)) return fail(NF4_ERR_ARG, "stage must be a 256-byte aligned buffer");
-    if (stage_bytes < 768) return fail(NF4_ERR_WORKSPACE, "stage must hold at least 768 bytes");
-    // chunk: a multiple of 64 parameters, so that the three staged vectors stay 256-byte aligned
-    const int64_t chunk = (int64_t)(stage_bytes / 768) * 64;
-    float* sp = (float*)stage;
-    float* sm = sp + chunk;
-    float* sv = sm + chunk;
+    if (stage_bytes < 1536) return fail(NF4_ERR_WORKSPACE, "stage must hold at least 1536 bytes");
+    // two halves, each [p][m][v] of `chunk` parameters (a multiple of 64, so that every
+    // staged vector stays 256-byte aligned): chunk c uses half c % 2
+    const int64_t chunk = (int64_t)(stage_bytes / 1536) * 64;
+    float* half[2] = {(float*)stage, (float*)stage + 3 * chunk};
     hipStream_t hs = (hipStream_t)stream;
-    for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    std::lock_guard<std::mutex> lock(g_paged_mu);
+    PagedResources* res = nullptr;
+    hipError_t e = paged_resources(&res);
+    if (e != hipSuccess) return hip_status(e, "nf4_adamw_step_paged (helper stream)");
+    hipStream_t out_stream = res->out;
+    // ready[b]: half b updated (the copy-out may start); done[b]: half b copied out (the
+    // next chunk of that half may be copied in)
+    hipEvent_t* ready = res->ready;
+    hipEvent_t* done = res->done;
+    int64_t nchunks = 0;
+    for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += chunk, ++nchunks) {
+        const int b = (int)(nchunks & 1);
         const int64_t cn = n - c0 < chunk ? n - c0 : chunk;
         const size_t nb = (size_t)cn * 4;
-        hipError_t e = hipMemcpyAsync(sp, p_host + c0, nb, hipMemcpyHostToDevice, hs);
+        float* sp = half[b];
+        float* sm = sp + chunk;
+        float* sv = sm + chunk;
+        if (nchunks >= 2) e = hipStreamWaitEvent(hs, done[b], 0);
+        if (e == hipSuccess) e = hipMemcpyAsync(sp, p_host + c0, nb, hipMemcpyHostToDevice, hs);
         if (e == hipSuccess) e = hipMemcpyAsync(sm, m_host + c0, nb, hipMemcpyHostToDevice, hs);
         if (e == hipSuccess) e = hipMemcpyAsync(sv, v_host + c0, nb, hipMemcpyHostToDevice, hs);
         if (e == hipSuccess) e = nf4::launch_adamw(sp, g + c0, sm, sv, p_bf16 ? p_bf16 + c0 : nullptr, cn, k, hs);
-        if (e == hipSuccess) e = hipMemcpyAsync(p_host + c0, sp, nb, hipMemcpyDeviceToHost, hs);
-        if (e == hipSuccess) e = hipMemcpyAsync(m_host + c0, sm, nb, hipMemcpyDeviceToHost, hs);
-        if (e == hipSuccess) e = hipMemcpyAsync(v_host + c0, sv, nb, hipMemcpyDeviceToHost, hs);
-        if (e != hipSuccess) return hip_status(e, "nf4_adamw_step_paged");
+        if (e == hipSuccess) e = hipEventRecord(ready[b], hs);
+        if (e == hipSuccess) e = hipStreamWaitEvent(out_stream, ready[b], 0);
+        if (e == hipSuccess) e = hipMemcpyAsync(p_host + c0, sp, nb, hipMemcpyDeviceToHost, out_stream);
+        if (e == hipSuccess) e = hipMemcpyAsync(m_host + c0, sm, nb, hipMemcpyDeviceToHost, out_stream);
+        if (e == hipSuccess) e = hipMemcpyAsync(v_host + c0, sv, nb, hipMemcpyDeviceToHost, out_stream);
+        if (e == hipSuccess) e = hipEventRecord(done[b], out_stream);
     }
-    return NF4_OK;
+    // the caller's stream completes after every copy-out
+    for (int b = 0; b < 2 && b < nchunks && e == hipSuccess; ++b) e = hipStreamWaitEvent(hs, done[b], 0);
+    return hip_status(e, "nf4_adamw_step_paged");
 }
 
 }  // extern "C"

@@ -206,12 +206,15 @@ nf4_status nf4_adamw_step(float* p, const float* g, float* m, float* v, uint16_t
 
 /* [PO]: the same step for state paged out to host memory.  p_host, m_host and
  * v_host are page-locked host buffers (hipHostMalloc or equivalent); g and p_bf16
- * are device memory as above.  The state passes through the device buffer `stage`
- * in chunks of floor(stage_bytes / 768) * 64 parameters: each chunk is copied in,
- * updated and copied back, in stream order on `stream`.  The host buffers must
- * stay untouched until the stream has run the work.  Results are bit-identical to
+ * are device memory as above.  The state passes through the device buffer `stage`,
+ * split in two halves of floor(stage_bytes / 1536) * 64 parameters that chunks use
+ * in turn: a chunk is copied in and updated on `stream`, and copied back on a
+ * helper stream of the library (one per device, created on first use, default
+ * priority), so that one chunk's copy-back overlaps the next chunk's copy-in.
+ * `stream` completes only after every copy-back.  The host buffers must stay
+ * untouched until `stream` has run the work.  Results are bit-identical to
  * nf4_adamw_step on device-resident state.
- *   stage        device scratch, 256-byte aligned, stage_bytes >= 768 */
+ *   stage        device scratch, 256-byte aligned, stage_bytes >= 1536 */
 nf4_status nf4_adamw_step_paged(float* p_host, const float* g, float* m_host, float* v_host,
                                 uint16_t* p_bf16, int64_t n, float lr, float beta1, float beta2,
                                 float eps, float weight_decay, int64_t step, void* stage,

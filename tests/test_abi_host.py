@@ -184,7 +184,7 @@ def test_adamw_rejects_bad_arguments():
     assert "overlap" in L.nf4_last_error().decode()
     paged = L.nf4_adamw_step_paged
     st = ctypes.c_void_p(8 << 20)
-    assert paged(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, st, 512, None) == nf4.NF4_ERR_WORKSPACE
+    assert paged(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, st, 1024, None) == nf4.NF4_ERR_WORKSPACE
     assert paged(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, None, 1 << 20, None) == nf4.NF4_ERR_ARG
     assert paged(p, q, m, v, None, 64, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, ctypes.c_void_p((8 << 20) + 16),
                  1 << 20, None) == nf4.NF4_ERR_ARG                                            # stage alignment

@@ -91,7 +91,8 @@ def test_adamw_step_matches_oracle(n, t, wd):
     assert np.array_equal(pbf.cpu().view(torch.int16).numpy(), expect_bf), "bf16 copy"
 
 
-@pytest.mark.parametrize("n,stage_bytes", [(1000, 768), (1000, 3 * 768), (65537, 1 << 16), (5, 1 << 20)])
+@pytest.mark.parametrize("n,stage_bytes", [(1000, 1536), (1000, 3 * 1536), (65537, 1 << 16), (5, 1 << 20),
+                                           (64 * 5, 1536)])
 def test_paged_step_equals_device_step(n, stage_bytes):
     # the paged path (host-resident state through a staging buffer, several chunks and a
     # partial last chunk) gives the device path's bits
