@@ -270,12 +270,10 @@ nf4_status nf4_codebook_stats(const void* w, nf4_dtype dtype, int64_t n, const u
         if (!isfinite(levels[i])) return fail(NF4_ERR_ARG, "levels must be finite");
         tab.lv[i] = levels[i];
     }
-    if (n == 0) {
-        nf4_codebook_stats_t zero;
-        memset(&zero, 0, sizeof(zero));
-        return hip_status(hipMemcpyAsync(out, &zero, sizeof(zero), hipMemcpyHostToDevice, (hipStream_t)stream),
+    if (n == 0)   // the reduction of no partials writes the zero statistics
+        return hip_status(nf4::launch_codebook_stats(nullptr, false, 0, nullptr, nullptr, tab, nullptr,
+                                                     (nf4::CodebookStats*)out, (hipStream_t)stream),
                           "nf4_codebook_stats");
-    }
     if (!w || !codes || !absmax) return fail(NF4_ERR_ARG, "NULL w/codes/absmax");
     if (!aligned(w, 16)) return fail(NF4_ERR_ARG, "w must be 16-byte aligned");
     if (!aligned(codes, 4) || !aligned(absmax, 4)) return fail(NF4_ERR_ARG, "codes/absmax must be 4-byte aligned");

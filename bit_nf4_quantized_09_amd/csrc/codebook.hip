@@ -187,6 +187,10 @@ __global__ __launch_bounds__(CB_THREADS) void k_codebook_stats_reduce(const Code
 hipError_t launch_codebook_stats(const void* w, bool w_bf16, int64_t n, const uint8_t* codes,
                                  const float* absmax, const Nf4Table& tab, CodebookStats* part,
                                  CodebookStats* out, hipStream_t s) {
+    if (n == 0) {                   // no values: only the reduction, of no partials (zeros)
+        hipLaunchKernelGGL(k_codebook_stats_reduce, dim3(1), dim3(CB_THREADS), 0, s, part, 0, out);
+        return hipGetLastError();
+    }
     const int64_t g = codebook_stats_grid(n);
     if (w_bf16)
         hipLaunchKernelGGL(k_codebook_stats<uint16_t>, dim3((unsigned)g), dim3(CB_THREADS), 0, s,

@@ -118,3 +118,11 @@ def test_gpu_lloyd_follows_oracle_lloyd(nf4_levels):
         lv[used] = (sum_x[used] / count[used]).astype(np.float32)
         lv = np.sort(lv)
     np.testing.assert_allclose(np.array(lv_gpu, np.float32), lv, rtol=1e-6, atol=1e-7)
+
+
+def test_stats_of_nothing_are_zero(nf4_levels):
+    w = torch.empty(0, dtype=torch.float32, device=DEV)
+    codes = torch.empty(0, dtype=torch.uint8, device=DEV)
+    absmax = torch.empty(0, dtype=torch.float32, device=DEV)
+    count, sum_x, sse = nf4.nf4_codebook_stats(w, codes, absmax, [float(x) for x in nf4_levels])
+    assert not count.any() and not sum_x.any() and sse == 0.0
