@@ -111,9 +111,19 @@ const Nf4Table& table() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Limits of the linear products, checked before anything is enqueued.  The adapter
+// products and the fused tiles address an operand through 32-bit per-lane offsets over
+// up to 512 rows of its leading dimension (N or K); a launch holds at most 2^24
+// workgroups of 256 threads (2^32 work-items); the adapter products stack the token
+// rows in 128-row workgroups along the grid's second dimension.
+constexpr int64_t LINEAR_DIM_LIMIT = (int64_t)1 << 22;
+constexpr int64_t LINEAR_M_LIMIT = (int64_t)1 << 23;
+constexpr int64_t FUSED_GRID_LIMIT = (int64_t)1 << 24;
+
 nf4_status check_weight(const nf4_weight* W, WeightView& v, bool linear) {
     if (!W) return fail(NF4_ERR_ARG, "weight descriptor is NULL");
     if (W->rows < 0 || W->cols < 0) return fail(NF4_ERR_ARG, "negative weight shape");
+    if (W->cols > 0 && W->rows > INT64_MAX / W->cols) return fail(NF4_ERR_ARG, "rows * cols overflows 64 bits");
     const int64_t n = W->rows * W->cols;
     const bool plain = W->q == nullptr;
     if (plain) {
@@ -130,6 +140,8 @@ nf4_status check_weight(const nf4_weight* W, WeightView& v, bool linear) {
         if (W->rows == 0 || W->cols == 0) return fail(NF4_ERR_ARG, "empty weight");
         // the fused kernels address the packed weight through 32-bit buffer offsets
         if (n / 2 >= ((int64_t)1 << 31)) return fail(NF4_ERR_UNSUPPORTED, "weight larger than 2^32 values");
+        if (W->rows >= LINEAR_DIM_LIMIT || W->cols >= LINEAR_DIM_LIMIT)
+            return fail(NF4_ERR_UNSUPPORTED, "N (rows) and K (cols) must be below 2^22");
     }
     if (!aligned(W->codes, 16)) return fail(NF4_ERR_ARG, "codes must be 16-byte aligned");
     if (!plain && (!aligned(W->c2, 4) || !aligned(W->mean, 4))) return fail(NF4_ERR_ARG, "misaligned c2/mean");
@@ -338,6 +350,9 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     if (st != NF4_OK) return st;
     if (M < 0) return fail(NF4_ERR_ARG, "M must be >= 0");
     if (M == 0) return NF4_OK;
+    if (M >= LINEAR_M_LIMIT) return fail(NF4_ERR_UNSUPPORTED, "M must be below 2^23");
+    if (M > GEMV_MAX_M && nf4::fused_fwd_plan(M, v.rows, v.cols).grid >= FUSED_GRID_LIMIT)
+        return fail(NF4_ERR_UNSUPPORTED, "M x N needs more than 2^24 workgroups of 512 x 128 output tiles");
     if (!X || !Y) return fail(NF4_ERR_ARG, "X or Y is NULL");
     if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(T_out, 16))
         return fail(NF4_ERR_ARG, "X, Y and T_out must be 16-byte aligned");
@@ -384,6 +399,9 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     st = check_lora(A, B, r, alpha);
     if (st != NF4_OK) return st;
     if (M < 0) return fail(NF4_ERR_ARG, "M must be >= 0");
+    if (M >= LINEAR_M_LIMIT) return fail(NF4_ERR_UNSUPPORTED, "M must be below 2^23");
+    if (M > 0 && dX && nf4::fused_bwd_plan(M, v.rows, v.cols).grid >= FUSED_GRID_LIMIT)
+        return fail(NF4_ERR_UNSUPPORTED, "M x K needs more than 2^24 workgroups of 512 x 128 output tiles");
     if (!dA || !dB) return fail(NF4_ERR_ARG, "dA or dB is NULL");
     if (!aligned(dA, 4) || !aligned(dB, 4)) return fail(NF4_ERR_ARG, "dA/dB must be 4-byte aligned");
     if (M > 0 && (!X || !dY)) return fail(NF4_ERR_ARG, "X or dY is NULL");

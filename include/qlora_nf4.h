@@ -162,8 +162,11 @@ nf4_status nf4_dequantize(const nf4_weight* W, void* out, nf4_dtype out_dtype, v
 /* [PT]+[E2E]+[RW]: QLoRA linear forward.
  *   Y = X W'^T + s (X A^T) B^T,  s = alpha / r,  W' = dequant(W) rounded to bf16
  * with the dequantization fused into the matrix multiply.
- *   W       N x K weight, K a multiple of 64, N a multiple of 8, N*K < 2^32
- *   X       bf16 M x K;  M >= 0 (M == 0 enqueues nothing)
+ *   W       N x K weight, K a multiple of 64, N a multiple of 8, N*K < 2^32,
+ *           N and K below 2^22
+ *   X       bf16 M x K;  0 <= M < 2^23 (M == 0 enqueues nothing); for M > 16 the
+ *           product runs as ceil(M/512) * ceil(N/128) output tiles (plus split
+ *           pieces), which must stay below 2^24 (backward: ceil(M/512) * ceil(K/128))
  *   A       bf16 r x K;  B  bf16 N x r;  1 <= r <= 128, r a multiple of 8
  *   Y       out: bf16 M x N
  *   T_out   out: bf16 M x r copy of X A^T for the backward, or NULL
@@ -226,9 +229,9 @@ nf4_status nf4_adamw_step_paged(float* p_host, const float* g, float* m_host, fl
  * first-level constants c1' of W (4 bytes per 64-block, written before the
  * fused MFMA product; not needed by the M <= 16 forward) and fp32 partial sums
  * of the split-contraction adapter products and of the fused product's tail
- * tiles (when the last wave of 256 x 256 output tiles would leave most compute
- * units idle, those tiles are computed in up to 4 contraction pieces: at most
- * 64 MiB).  Contents are scratch: nothing
+ * tiles (when the last wave of 512 x 128 output tiles, tokens x features, would
+ * leave most compute units idle, those tiles are computed in up to 4
+ * contraction pieces: at most 64 MiB).  Contents are scratch: nothing
  * survives between calls, and two calls that overlap in time on one device
  * need separate workspaces. */
 size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r);

@@ -137,6 +137,17 @@ def test_linear_rejects_bad_arguments():
     assert fwd(ctypes.byref(good), p, 16, p, p, 8, 16.0, p, p, ctypes.c_void_p(8200), 1 << 20, None) == nf4.NF4_ERR_ARG
     assert fwd(ctypes.byref(_w(256, 256, codes=4104)), p, 16, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_ERR_ARG
     assert fwd(ctypes.byref(good), p, 0, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_OK  # M = 0
+    # size limits (32-bit operand offsets, launch grid), before any device call
+    assert fwd(ctypes.byref(_w(1 << 22, 64)), p, 16, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_ERR_UNSUPPORTED
+    assert b"below 2^22" in L.nf4_last_error()
+    assert fwd(ctypes.byref(_w(64, 1 << 22)), p, 16, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_ERR_UNSUPPORTED
+    assert fwd(ctypes.byref(good), p, 1 << 23, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_ERR_UNSUPPORTED
+    wide = _w(1025 * 128, 64)       # (2^14 - 1) token tiles x 1025 feature tiles >= 2^24
+    assert fwd(ctypes.byref(wide), p, (1 << 23) - 512, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_ERR_UNSUPPORTED
+    assert b"2^24 workgroups" in L.nf4_last_error()
+    tall = _w(64, 1025 * 128)
+    assert L.qlora_linear_bwd(ctypes.byref(tall), p, p, (1 << 23) - 512, p, p, 8, 16.0, p, p, p, p, ws,
+                              1 << 20, None) == nf4.NF4_ERR_UNSUPPORTED
     bwd = L.qlora_linear_bwd
     assert bwd(ctypes.byref(good), p, p, 16, p, p, 8, 16.0, p, p, None, p, ws, 1 << 20, None) == nf4.NF4_ERR_ARG
     assert bwd(ctypes.byref(good), p, p, 16, p, p, 8, 16.0, None, p, p, p, ws, 16, None) == nf4.NF4_ERR_WORKSPACE
@@ -150,6 +161,7 @@ def test_dequantize_rejects_bad_arguments():
     assert L.nf4_dequantize(ctypes.byref(_w(4, 4)), p, 9, None) == nf4.NF4_ERR_ARG
     assert L.nf4_dequantize(ctypes.byref(_w(4, 4)), None, 0, None) == nf4.NF4_ERR_ARG
     assert L.nf4_dequantize(ctypes.byref(_w(-1, 4)), p, 0, None) == nf4.NF4_ERR_ARG
+    assert L.nf4_dequantize(ctypes.byref(_w(1 << 40, 1 << 40)), p, 0, None) == nf4.NF4_ERR_ARG   # n overflows
     assert L.nf4_dequantize(ctypes.byref(_w(0, 4)), p, 0, None) == nf4.NF4_OK
 
 
