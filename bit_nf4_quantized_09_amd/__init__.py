@@ -132,6 +132,20 @@ def _dev(t: torch.Tensor, name: str, dtype=None):
     return t
 
 
+def _numel(t: Optional[torch.Tensor], name: str, n: int, dtype):
+    """Size and dtype of a 1-D operand, checked before anything reaches the device."""
+    if t is None:
+        raise ValueError("%s is missing" % name)
+    if t.dtype != dtype or t.numel() != n:
+        raise ValueError("%s must hold %d values of %s, got %d of %s" % (name, n, dtype, t.numel(), t.dtype))
+
+
+def _same_device(*named):
+    devs = {(name, t.device) for name, t in named if t is not None}
+    if len({d for _, d in devs}) > 1:
+        raise ValueError("operands on different devices: %s" % sorted((n, str(d)) for n, d in devs))
+
+
 def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return None
@@ -152,7 +166,28 @@ class NF4Weight:
     shape: Tuple[int, int]
     absmax: Optional[torch.Tensor] = None   # float32 [ceil(n/64)], when q is None
 
+    def validate(self):
+        """Sizes, dtypes and device of the tuple against its shape (raises ValueError)."""
+        rows, cols = self.shape
+        if rows < 0 or cols < 0:
+            raise ValueError("negative weight shape")
+        n = rows * cols
+        n1 = (n + 63) // 64
+        _numel(self.codes, "codes", (n + 1) // 2, torch.uint8)
+        if self.q is not None:
+            _numel(self.q, "q", n1, torch.uint8)
+            _numel(self.c2, "c2", (n1 + 255) // 256, torch.float32)
+            _numel(self.mean, "mean", 1, torch.float32)
+            parts = (("codes", self.codes), ("q", self.q), ("c2", self.c2), ("mean", self.mean))
+        else:
+            _numel(self.absmax, "absmax", n1, torch.float32)
+            parts = (("codes", self.codes), ("absmax", self.absmax))
+        for name, t in parts:
+            _dev(t, name)
+        _same_device(*parts)
+
     def descriptor(self) -> _Weight:
+        self.validate()
         rows, cols = self.shape
         ptr = lambda t: t.data_ptr() if t is not None else None
         return _Weight(self.codes.data_ptr(), ptr(self.q), ptr(self.c2), ptr(self.mean), rows, cols,
@@ -227,9 +262,13 @@ def nf4_double_dequantize(q: torch.Tensor, c2: torch.Tensor, mean: torch.Tensor,
                           blocksize2: int = 256) -> torch.Tensor:
     """c1' = fma(E4M3(q), fp32(c2/448), mean) per constant."""
     L = load_library()
-    _dev(q, "q", torch.uint8)
-    _dev(c2, "c2", torch.float32)
-    _dev(mean, "mean", torch.float32)
+    n1 = q.numel()
+    _numel(q, "q", n1, torch.uint8)
+    _numel(c2, "c2", (n1 + 255) // 256, torch.float32)
+    _numel(mean, "mean", 1, torch.float32)
+    for name, t in (("q", q), ("c2", c2), ("mean", mean)):
+        _dev(t, name)
+    _same_device(("q", q), ("c2", c2), ("mean", mean))
     out = torch.empty(q.numel(), dtype=torch.float32, device=q.device)
     _check(L.nf4_double_dequantize(_ptr(q), _ptr(c2), _ptr(mean), q.numel(), blocksize2, _ptr(out),
                                    _stream(q.device)))
@@ -275,6 +314,7 @@ def qlora_linear_fwd(W: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
     if tuple(A.shape) != (r, K) or tuple(B.shape) != (N, r):
         raise ValueError("A must be [r, K] and B [N, r]")
     M = X.shape[0]
+    _same_device(("W", W.codes), ("X", X), ("A", A), ("B", B))
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     T = torch.empty((M, r), dtype=torch.bfloat16, device=X.device) if save_t else None
     wsb = L.nf4_workspace_bytes(NF4_OP_LINEAR_FWD, M, N, K, r)
@@ -305,6 +345,7 @@ def qlora_linear_bwd(W: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
         _dev(T, "T", torch.bfloat16)
         if tuple(T.shape) != (M, r):
             raise ValueError("T must be [M, r]")
+    _same_device(("W", W.codes), ("X", X), ("dY", dY), ("A", A), ("B", B), ("T", T))
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device) if need_dx else None
     dA = torch.empty((r, K), dtype=torch.float32, device=X.device)
     dB = torch.empty((N, r), dtype=torch.float32, device=X.device)
@@ -495,10 +536,15 @@ def nf4_codebook_stats(w: torch.Tensor, codes: torch.Tensor, absmax: torch.Tenso
     blockwise quantization, computed on the GPU: (count int64[16], sum_x float64[16],
     sse float) as host values."""
     L = load_library()
-    _dev(w, "w")
-    _dev(codes, "codes", torch.uint8)
-    _dev(absmax, "absmax", torch.float32)
     n = w.numel()
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be float32 or bfloat16")
+    _numel(codes, "codes", (n + 1) // 2, torch.uint8)
+    _numel(absmax, "absmax", (n + 63) // 64, torch.float32)
+    _dev(w, "w")
+    _dev(codes, "codes")
+    _dev(absmax, "absmax")
+    _same_device(("w", w), ("codes", codes), ("absmax", absmax))
     dt = NF4_BF16 if w.dtype == torch.bfloat16 else NF4_F32
     out = torch.empty(33, dtype=torch.float64, device=w.device)
     wsb = L.nf4_workspace_bytes(NF4_OP_CODEBOOK_STATS, 0, n, 0, 0)

@@ -14,6 +14,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import bit_nf4_quantized_09_amd as nf4
 
@@ -228,3 +229,30 @@ def test_codebook_entry_points_reject_bad_arguments():
     assert st(p, 0, 1 << 20, p, p, good, p, p, wsb - 8, None) == nf4.NF4_ERR_WORKSPACE
     assert st(p, 0, 1 << 20, p, p, None, p, p, wsb, None) == nf4.NF4_ERR_ARG
     assert st(p, 0, 1 << 20, p, p, good, None, p, wsb, None) == nf4.NF4_ERR_ARG
+
+
+def test_binding_checks_tuple_sizes_before_the_device():
+    # sizes and dtypes of the weight tuple are checked against its shape first, so a
+    # mismatched tuple never reaches a kernel (CPU tensors: the size checks come first)
+    u8, f32 = torch.uint8, torch.float32
+    n = 4 * 64
+    codes, q, c2, mean = torch.zeros(n // 2, dtype=u8), torch.zeros(4, dtype=u8), torch.zeros(1), torch.zeros(1)
+    with pytest.raises(ValueError, match="codes must hold 128"):
+        nf4.NF4Weight(codes[:100], q, c2, mean, (4, 64)).validate()
+    with pytest.raises(ValueError, match="q must hold 4"):
+        nf4.NF4Weight(codes, q[:3], c2, mean, (4, 64)).validate()
+    with pytest.raises(ValueError, match="c2 must hold 1"):
+        nf4.NF4Weight(codes, q, torch.zeros(2), mean, (4, 64)).validate()
+    with pytest.raises(ValueError, match="mean must hold 1"):
+        nf4.NF4Weight(codes, q, c2, mean.double(), (4, 64)).validate()
+    with pytest.raises(ValueError, match="absmax must hold 4"):
+        nf4.NF4Weight(codes, None, None, None, (4, 64), torch.zeros(5, dtype=f32)).validate()
+    with pytest.raises(ValueError, match="absmax is missing"):
+        nf4.NF4Weight(codes, None, None, None, (4, 64)).validate()
+    with pytest.raises(ValueError, match="GPU tensor"):       # consistent, but on the host
+        nf4.NF4Weight(codes, q, c2, mean, (4, 64)).validate()
+    w = torch.zeros(n)
+    with pytest.raises(ValueError, match="absmax must hold 4"):
+        nf4.nf4_codebook_stats(w, codes, torch.zeros(3), nf4.nf4_codebook())
+    with pytest.raises(ValueError, match="c2 must hold 1"):
+        nf4.nf4_double_dequantize(q, torch.zeros(0), mean)
