@@ -283,16 +283,23 @@ hipError_t launch_double_dequantize(const uint8_t* q, const float* c2, const flo
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize.  A workgroup handles chunks of 256 x 8 groups of E values (E = 4
-// for fp32 output, 8 for bf16, so one group is 16 bytes of output) in a
-// grid-stride loop.  Store j of lane l in wave w covers group (8w + j) * 64 + l
-// of the chunk, so every store (and every code load) of a wave is one contiguous
-// run.  Each lane decodes the constant of its group's block itself (the 8-bit
-// constants and second-level constants are L1-resident, 16 / E lanes read the same
-// byte), so a chunk needs no barrier, and every request of a chunk is made before
-// its first store.  Levels come from a 256-entry LDS table of code byte -> the two
-// fp32 levels.
+// Dequantize.  Each wave handles chunks of 8 x 64 groups of E values (E = 4 for
+// fp32 output, 8 for bf16, so one group is 16 bytes of output) in a grid-stride
+// loop over the tensor's chunks; store j of lane l covers group 64 j + l of the
+// chunk, so every store of a wave is one contiguous kilobyte.  The chunk's codes
+// (256 E contiguous bytes) arrive in one or two 16-byte loads per lane, and its
+// 8 E block constants in one load per lane, each lane decoding the constant of one
+// block; both go through a wave-private LDS slot to the lanes that store them
+// (LDS accesses of one wave execute in order, so no barrier is needed).  That is
+// two or three requests per chunk where one request per store and operand cost
+// most of the time; a wave requests its next chunk before storing the current one,
+// so the requests of one chunk are in flight while the previous one is written.
+// Levels come from a 256-entry LDS table of code byte -> the two fp32 levels.  The
+// last chunk, when partial, takes a checked path with a request per group.
 // ---------------------------------------------------------------------------
+// s_waitcnt operand: vmcnt 0, expcnt and lgkmcnt unconstrained
+constexpr int DQ_WAIT_VMCNT0 = 0x0F70;
+
 template <bool OUT_BF16, bool PLAIN>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ q,
@@ -301,8 +308,12 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
                                                     const float* __restrict__ absmax, int64_t n,
                                                     void* __restrict__ out, Nf4Table tab) {
     constexpr int E = OUT_BF16 ? 8 : 4;            // values per group (16 bytes of output)
-    constexpr int CHUNK = 256 * 8 * E;             // values per chunk
+    constexpr int WV = 8 * 64 * E;                 // values per wave chunk
+    constexpr int WB = WV / 64;                    // its blocks: 32 or 64
+    constexpr int WC = WV / 2;                     // its code bytes: 1 or 2 KB
     __shared__ float2 s_pair[256];                 // code byte -> (level of low nibble, of high nibble)
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[4][WC];
+    __shared__ float s_c1[4][WB];
     {
         float lo = 0.0f, hi = 0.0f;
 #pragma unroll
@@ -315,75 +326,120 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
     __syncthreads();
     const float mean = PLAIN ? 0.0f : *mean_p;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t nblk = (n + 63) / 64;
     const int64_t nbytes = (n + 1) / 2;
-    const int64_t n2 = (nblk + 255) / 256;
-    // one chunk; WHOLE: every group of the chunk lies inside the tensor (no checks, no
-    // branches, so the requests of all eight groups are in flight together)
-    auto chunk = [&](int64_t c0, auto whole_tag) {
-        constexpr bool WHOLE = decltype(whole_tag)::value;
-        uint32_t cw[8];
-        uint32_t qb[8];
-        float cs[8];
+    uint8_t* my_codes = s_codes[wave];
+    float* my_c1 = s_c1[wave];
+
+    // E levels of one group (codes cw, E/2 bytes) times its constant, stored at out + i0
+    auto emit = [&](int64_t i0, uint32_t cw, float c1p, bool whole) {
+        float v[E];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t i0 = c0 + ((int64_t)(8 * wave + j) * 64 + lane) * E;
-            if (WHOLE || i0 + E <= n) {
-                if constexpr (E == 4) cw[j] = *reinterpret_cast<const uint16_t*>(codes + i0 / 2);
-                else cw[j] = *reinterpret_cast<const uint32_t*>(codes + i0 / 2);
-            } else {
-                uint32_t x = 0;
-                for (int t = 0; t < E / 2; ++t)
-                    if (i0 / 2 + t < nbytes) x |= (uint32_t)codes[i0 / 2 + t] << (8 * t);
-                cw[j] = x;
-            }
-            // the group's block, clamped into the arrays (a group past n stores nothing)
-            const int64_t blk = WHOLE ? i0 / 64 : (i0 / 64 < nblk ? i0 / 64 : nblk - 1);
-            if constexpr (PLAIN) {
-                cs[j] = absmax[blk];          // the constant itself
-                qb[j] = 0;
-            } else {
-                qb[j] = q[blk];
-                cs[j] = c2[WHOLE ? (blk >> 8) : ((blk >> 8) < n2 ? (blk >> 8) : n2 - 1)];
-            }
+        for (int e = 0; e < E / 2; ++e) {
+            const float2 l = s_pair[(cw >> (8 * e)) & 0xFFu];
+            v[2 * e] = l.x * c1p;
+            v[2 * e + 1] = l.y * c1p;
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t i0 = c0 + ((int64_t)(8 * wave + j) * 64 + lane) * E;
-            if (!WHOLE && i0 >= n) continue;
-            const float c1p = PLAIN ? cs[j] : decode_c1(qb[j], c2_step(cs[j]), mean);
-            float v[E];
-#pragma unroll
-            for (int e = 0; e < E / 2; ++e) {
-                const float2 l = s_pair[(cw[j] >> (8 * e)) & 0xFFu];
-                v[2 * e] = l.x * c1p;
-                v[2 * e + 1] = l.y * c1p;
-            }
-            if constexpr (OUT_BF16) {
-                uint16_t* o = reinterpret_cast<uint16_t*>(out) + i0;
-                if (WHOLE || i0 + E <= n) {
-                    uint4 pk;
-                    pk.x = pack_bf16x2(v[0], v[1]); pk.y = pack_bf16x2(v[2], v[3]);
-                    pk.z = pack_bf16x2(v[4], v[5]); pk.w = pack_bf16x2(v[6], v[7]);
-                    *reinterpret_cast<uint4*>(o) = pk;
-                } else {
-                    for (int e = 0; e < E; ++e)
-                        if (i0 + e < n) o[e] = f32_to_bf16(v[e]);
-                }
+        if constexpr (OUT_BF16) {
+            uint16_t* o = reinterpret_cast<uint16_t*>(out) + i0;
+            if (whole) {
+                uint4 pk;
+                pk.x = pack_bf16x2(v[0], v[1]); pk.y = pack_bf16x2(v[2], v[3]);
+                pk.z = pack_bf16x2(v[4], v[5]); pk.w = pack_bf16x2(v[6], v[7]);
+                *reinterpret_cast<uint4*>(o) = pk;
             } else {
-                float* o = reinterpret_cast<float*>(out) + i0;
-                if (WHOLE || i0 + E <= n) {
-                    *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-                } else {
-                    for (int e = 0; e < E; ++e)
-                        if (i0 + e < n) o[e] = v[e];
-                }
+                for (int e = 0; e < E; ++e)
+                    if (i0 + e < n) o[e] = f32_to_bf16(v[e]);
+            }
+        } else {
+            float* o = reinterpret_cast<float*>(out) + i0;
+            if (whole) {
+                *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                for (int e = 0; e < E; ++e)
+                    if (i0 + e < n) o[e] = v[e];
             }
         }
     };
-    for (int64_t c0 = (int64_t)blockIdx.x * CHUNK; c0 < n; c0 += (int64_t)gridDim.x * CHUNK) {
-        if (c0 + CHUNK <= n) chunk(c0, std::true_type{});
-        else chunk(c0, std::false_type{});
+    auto constant_of = [&](int64_t blk) {
+        if constexpr (PLAIN) return absmax[blk];
+        else return decode_c1(q[blk], c2_step(c2[blk >> 8]), mean);
+    };
+
+    // a whole chunk's requests, made one chunk ahead of their use: the code bytes
+    // 16 (64 k + lane) .. of the chunk, and block b0 + lane % WB (raw operands)
+    auto fetch = [&](int64_t c, uint4& cw0, uint4& cw1, uint32_t& qb, float& cs) {
+        const int64_t v0 = c * WV;
+        const uint4* src = reinterpret_cast<const uint4*>(codes + v0 / 2);
+        cw0 = src[lane];
+        if constexpr (E == 8) cw1 = src[64 + lane];
+        const int64_t blk = v0 / 64 + (lane & (WB - 1));
+        if constexpr (PLAIN) {
+            qb = 0;
+            cs = absmax[blk];
+        } else {
+            qb = q[blk];
+            cs = c2[blk >> 8];
+        }
+    };
+    auto whole_chunk = [&](int64_t c, uint4 cw0, uint4 cw1, uint32_t qb, float cs) {
+        const int64_t v0 = c * WV;
+        const float c1p = PLAIN ? cs : decode_c1(qb, c2_step(cs), mean);
+        *reinterpret_cast<uint4*>(my_codes + 16 * lane) = cw0;
+        if constexpr (E == 8) *reinterpret_cast<uint4*>(my_codes + 16 * (64 + lane)) = cw1;
+        if (lane < WB) my_c1[lane] = c1p;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int g = 64 * j + lane;
+            uint32_t cw;
+            if constexpr (E == 4) cw = *reinterpret_cast<const uint16_t*>(my_codes + 2 * g);
+            else cw = *reinterpret_cast<const uint32_t*>(my_codes + 4 * g);
+            emit(v0 + (int64_t)g * E, cw, my_c1[g * E / 64], true);
+        }
+    };
+
+    // Whole chunks 0 .. nwhole-1 in a grid-stride loop over the waves, software-pipelined
+    // over two register sets: each half waits for everything in flight (its own chunk's
+    // operands and the previous chunk's stores), requests the next chunk (clamped to the
+    // last whole one, so the request count never depends on a branch), then stores its
+    // chunk.  The scheduling barriers keep the next half's work, which waits for the
+    // requests just made, from moving in front of this half's stores.
+    const int64_t gstride = (int64_t)gridDim.x * 4;
+    const int64_t first = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t nwhole = n / WV;
+    if (first < nwhole) {
+        uint4 a0, a1 = {}, b0, b1 = {};
+        uint32_t a_q, b_q;
+        float a_c, b_c;
+        fetch(first, a0, a1, a_q, a_c);
+        int64_t c = first;
+        while (true) {
+            __builtin_amdgcn_s_waitcnt(DQ_WAIT_VMCNT0);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(c + gstride < nwhole ? c + gstride : nwhole - 1, b0, b1, b_q, b_c);
+            whole_chunk(c, a0, a1, a_q, a_c);
+            __builtin_amdgcn_sched_barrier(0);
+            c += gstride;
+            if (c >= nwhole) break;
+            __builtin_amdgcn_s_waitcnt(DQ_WAIT_VMCNT0);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(c + gstride < nwhole ? c + gstride : nwhole - 1, a0, a1, a_q, a_c);
+            whole_chunk(c, b0, b1, b_q, b_c);
+            __builtin_amdgcn_sched_barrier(0);
+            c += gstride;
+            if (c >= nwhole) break;
+        }
+    }
+    // the partial last chunk, by the wave whose sequence reaches it: groups past n store nothing
+    if (nwhole * WV < n && nwhole >= first && (nwhole - first) % gstride == 0) {
+        const int64_t v0 = nwhole * WV;
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i0 = v0 + (int64_t)(64 * j + lane) * E;
+            if (i0 >= n) continue;
+            uint32_t cw = 0;
+            for (int t = 0; t < E / 2; ++t)
+                if (i0 / 2 + t < nbytes) cw |= (uint32_t)codes[i0 / 2 + t] << (8 * t);
+            emit(i0, cw, constant_of(i0 / 64), i0 + E <= n);
+        }
     }
 }
 
