@@ -137,3 +137,25 @@ def test_dequantize_plain_constants(shape):
     assert np.array_equal(got.view(np.uint32), exp.view(np.uint32))
     gb = nf4.nf4_dequantize(W, torch.bfloat16)
     assert torch.equal(gb.cpu().view(torch.int16), torch.from_numpy(exp).bfloat16().view(torch.int16))
+
+
+# Chunks of 2048 (fp32 out) or 4096 (bf16 out) values per wave, 8192 waves at most: these
+# sizes give more whole chunks than waves (waves run 2 or 3 chunks, so the pipelined loop
+# leaves through both register sets) plus a partial last chunk.
+@pytest.mark.parametrize("out_dtype,n", [(torch.float32, (2 * 8192 + 3) * 2048 + 777),
+                                         (torch.bfloat16, (2 * 8192 + 5) * 4096 + 1001)])
+@pytest.mark.parametrize("double_quant", [True, False])
+def test_dequantize_more_chunks_than_waves(out_dtype, n, double_quant):
+    print("dequantize", out_dtype, n, "double_quant", double_quant, flush=True)
+    w = Draw(seed_of(42, n), DEV).normal((1, n), 0.02, outlier_frac=0.01)
+    W = nf4.quantize_weight(w, double_quant=double_quant)
+    ref = oracle_weight(w.cpu())
+    if double_quant:
+        exp = ref["Wd"]
+    else:
+        exp = oracle.nf4_dequantize_plain(ref["codes"], ref["absmax"], (1, n))
+    got = nf4.nf4_dequantize(W, out_dtype)
+    if out_dtype == torch.float32:
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), exp.view(np.uint32))
+    else:
+        assert torch.equal(got.cpu().view(torch.int16), torch.from_numpy(exp).bfloat16().view(torch.int16))
