@@ -79,26 +79,55 @@ __global__ __launch_bounds__(CB_THREADS) void k_codebook_stats(const T* __restri
         }
     };
 
-    // chunk q: values 8q .. 8q+7, one 32-bit word of codes, inside block q / 8
+    // chunk q: values 8q .. 8q+7, one 32-bit word of codes, inside block q / 8.  The
+    // grid-stride loop is software-pipelined over two register sets: a chunk's requests
+    // go out one iteration before its values are used (the next chunk index is clamped,
+    // so the number of requests in flight never depends on a branch, and only loads are
+    // in flight, so each wait covers exactly the chunk it needs).
     const int64_t n8 = n >> 3;
-    for (int64_t q = (int64_t)blockIdx.x * CB_THREADS + tid; q < n8; q += (int64_t)gridDim.x * CB_THREADS) {
+    auto fetch = [&](int64_t q, uint4& a, uint4& b, uint32_t& word, float& c) {
+        if constexpr (sizeof(T) == 4) {
+            a = reinterpret_cast<const uint4*>(w)[2 * q];
+            b = reinterpret_cast<const uint4*>(w)[2 * q + 1];
+        } else {
+            a = reinterpret_cast<const uint4*>(w)[q];
+        }
+        word = reinterpret_cast<const uint32_t*>(codes)[q];
+        c = absmax[q >> 3];
+    };
+    auto chunk = [&](uint4 a, uint4 b, uint32_t word, float c) {
         float v[8];
         if constexpr (sizeof(T) == 4) {
-            const uint4 a = reinterpret_cast<const uint4*>(w)[2 * q];
-            const uint4 b = reinterpret_cast<const uint4*>(w)[2 * q + 1];
             v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
             v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
         } else {
-            const uint4 a = reinterpret_cast<const uint4*>(w)[q];
             const uint32_t r4[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(r4[j]); v[2 * j + 1] = bf16_hi(r4[j]); }
         }
-        const uint32_t word = reinterpret_cast<const uint32_t*>(codes)[q];
-        const float c = absmax[q >> 3];
         const float y = __fdiv_rn(1.0f, c);
 #pragma unroll
         for (int e = 0; e < 8; ++e) one(v[e], (word >> (4 * e)) & 15u, c, y);
+    };
+    const int64_t stride = (int64_t)gridDim.x * CB_THREADS;
+    int64_t q = (int64_t)blockIdx.x * CB_THREADS + tid;
+    if (q < n8) {
+        uint4 a0, a1 = {}, b0, b1 = {};
+        uint32_t aw, bw;
+        float ac, bc;
+        fetch(q, a0, a1, aw, ac);
+        while (true) {
+            int64_t qn = q + stride;
+            fetch(qn < n8 ? qn : q, b0, b1, bw, bc);
+            chunk(a0, a1, aw, ac);
+            if (qn >= n8) break;
+            q = qn;
+            qn = q + stride;
+            fetch(qn < n8 ? qn : q, a0, a1, aw, ac);
+            chunk(b0, b1, bw, bc);
+            if (qn >= n8) break;
+            q = qn;
+        }
     }
     // the last n % 8 values
     if (blockIdx.x == 0 && tid == 0) {
