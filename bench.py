@@ -201,8 +201,8 @@ def summarize_pmc(fetch_csv, write_csv):
         "",
         "Commands (GPU, from the repository root; one counter per run):",
         "",
-        "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- python bench.py --pmc-workload",
-        "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- python bench.py --pmc-workload",
+        "    rocprofv3 --pmc FETCH_SIZE -d pmc_fetch -o run --output-format csv -- python bench.py --pmc-workload",
+        "    rocprofv3 --pmc WRITE_SIZE -d pmc_write -o run --output-format csv -- python bench.py --pmc-workload",
         "    python bench.py --summarize-pmc <pmc_fetch>/run_counter_collection.csv <pmc_write>/run_counter_collection.csv",
         "",
         "Calibration: a plain device copy of %d MiB in the same run reads %.1f KiB by FETCH_SIZE and writes "
@@ -625,7 +625,7 @@ def main():
         summarize_gemv_trace(args.summarize_gemv_trace)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
