@@ -13,9 +13,10 @@
 // Design for CDNA4: a TM x TN output tile per workgroup of 4 waves (each wave
 // 128 x 128 = 4 x 4 tiles of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per
 // lane), one NF4 block (64 values) of contraction per pipeline step, two LDS
-// stages.  The packed codes of one (row, 64-block) are owned by 256/TN lanes, each
-// of which builds a 16-entry bf16 table scaled by the block's decoded constant and
-// expands its share of the codes with byte permutes before writing them to LDS;
+// stages.  The packed codes of one (row, 64-block) are owned by a pair of lanes (TN =
+// 128), which build the block's 16-entry bf16 table scaled by its decoded constant
+// together (each computes half and takes the other half from its partner); each lane
+// then expands its share of the codes with byte permutes before writing them to LDS;
 // every dequantized value is therefore computed once per workgroup and reused by TM
 // rows of the other operand.  The decode work per MFMA falls as TM grows: the
 // 512 x 128 tile (2 x 80 KB stages, the whole 160 KB LDS) decodes half as much per
@@ -166,12 +167,20 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         const uint4 v = bc.w[c >> 2];
         return (c & 3) == 0 ? v.x : (c & 3) == 1 ? v.y : (c & 3) == 2 ? v.z : v.w;
     };
+    // the two lanes of a (row, 64-block) pair (tid 2i, 2i+1) build its scaled table together:
+    // lane `part` computes entries 8 part .. 8 part + 7, and its codes are flipped to match
+    static_assert(G::LPP == 2, "pair lanes");
+    float lvh[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lvh[i] = part ? tab.lv[8 + i] : tab.lv[i];
+    const uint32_t flip = pair_code_flip(part);
+    auto half_table = [&](float c) { return make_pair_table(lvh, c); };
     auto dequant_store = [&](uint8_t* sW, const BlockCodes<G::NW>& bc) {
-        const ScaledTable st = make_scaled_table(tab, bc.c1);
+        const ScaledTable st = half_table(bc.c1);
 #pragma unroll
         for (int c = 0; c < G::NCH; ++c) {
             uint32_t o[4];
-            decode8(st, word(bc, c), o);
+            decode8(st, word(bc, c) ^ flip, o);
             *reinterpret_cast<uint4*>(sW + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     };
@@ -319,11 +328,11 @@ void k_fused(FusedArgs a, Nf4Table tab) {
             // half carries the A tile writes)
             constexpr int D0 = G::DEPTH == 2 ? 0 : 3;
             if (rg == D0) {
-                tbl = make_scaled_table(tab, wcur.c1);
+                tbl = half_table(wcur.c1);
             } else if (rg > D0 && rg - D0 - 1 < G::NCH && rg - D0 - 1 < 7 - D0) {
                 const int c = rg - D0 - 1;
                 uint32_t o[4];
-                decode8(tbl, word(wcur, c), o);
+                decode8(tbl, word(wcur, c) ^ flip, o);
                 *reinterpret_cast<uint4*>(sWn + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
             }
 #pragma unroll
@@ -342,7 +351,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
 #pragma unroll
         for (int c = (G::DEPTH == 2 ? 7 : 4); c < G::NCH; ++c) {
             uint32_t o[4];
-            decode8(tbl, word(wcur, c), o);
+            decode8(tbl, word(wcur, c) ^ flip, o);
             *reinterpret_cast<uint4*>(sWn + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
         }
         if constexpr (G::DEPTH == 2) {

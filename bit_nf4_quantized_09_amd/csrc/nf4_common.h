@@ -117,29 +117,43 @@ __device__ __forceinline__ uint32_t nf4_encode(float x, const Nf4Table& t) {
 // ---------------------------------------------------------------------------
 // NF4 decode of 8 packed codes through a per-lane scaled table.
 //
-// A lane that owns one (row, 64-block) builds the 16 scaled values
-// bf16(fp32(level_j * c1')) once, split into a low-byte table and a high-byte
-// table (4 registers each).  v_perm_b32 then looks up four 8-entry byte
-// tables at a time; bit 3 of each code picks the half.
+// The two lanes that share one (row, 64-block), adjacent lanes 2i and 2i+1, build the 16
+// scaled values bf16(fp32(level_j * c1')) together: lane h of the pair computes entries
+// 8h .. 8h+7 and splits them into a low-byte and a high-byte table (2 registers each), and a
+// quad permute (v_mov_b32 DPP quad_perm [1,0,3,2]) hands each lane its partner's two pairs.
+// Lane 0 then holds entries 0-7 in registers 0-1 and 8-15 in 2-3; lane 1 holds them the other
+// way round, which flipping bit 3 of every code (pair_code_flip) undoes.  v_perm_b32 looks up
+// four 8-entry byte tables at a time; bit 3 of each code picks the half.
 // ---------------------------------------------------------------------------
 struct ScaledTable {
-    uint32_t lo[4];   // low bytes of entries 0..15, four per register
+    uint32_t lo[4];   // low bytes of 16 entries, four per register
     uint32_t hi[4];   // high bytes
 };
 
-__device__ __forceinline__ ScaledTable make_scaled_table(const Nf4Table& t, float c1p) {
-    uint32_t p[8];
+// lvh: this lane's 8 levels (entries 8h .. 8h+7 of the codebook, h = lane & 1).  Both lanes of
+// the pair must be active.
+__device__ __forceinline__ ScaledTable make_pair_table(const float lvh[8], float c1p) {
+    uint32_t p[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = pack_bf16x2(t.lv[2 * j] * c1p, t.lv[2 * j + 1] * c1p);
+    for (int j = 0; j < 4; ++j) p[j] = pack_bf16x2(lvh[2 * j] * c1p, lvh[2 * j + 1] * c1p);
     ScaledTable s;
+    // bytes of p[2k] = [e0.lo e0.hi e1.lo e1.hi], p[2k+1] = [e2.lo ...]
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        // bytes of p[2j] = [e0.lo e0.hi e1.lo e1.hi], p[2j+1] = [e2.lo ...]
-        s.lo[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x06040200u);
-        s.hi[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x07050301u);
+    for (int k = 0; k < 2; ++k) {
+        s.lo[k] = __builtin_amdgcn_perm(p[2 * k + 1], p[2 * k], 0x06040200u);
+        s.hi[k] = __builtin_amdgcn_perm(p[2 * k + 1], p[2 * k], 0x07050301u);
+    }
+    constexpr int SWAP_PAIRS = 0xB1;   // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        s.lo[2 + k] = (uint32_t)__builtin_amdgcn_mov_dpp((int)s.lo[k], SWAP_PAIRS, 0xF, 0xF, false);
+        s.hi[2 + k] = (uint32_t)__builtin_amdgcn_mov_dpp((int)s.hi[k], SWAP_PAIRS, 0xF, 0xF, false);
     }
     return s;
 }
+
+// XOR mask for the code words of lane h of a pair (see make_pair_table)
+__device__ __forceinline__ uint32_t pair_code_flip(int h) { return h ? 0x88888888u : 0u; }
 
 // Byte lane k of `sel` holds a code 0..15 and byte lane k of `hi8` is 0xFF exactly
 // where that code is >= 8; returns the table's low and high bytes for the 4 codes.
