@@ -54,6 +54,17 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
     return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
 }
 
+// Stage layout of the 160 KB of LDS (512 x 128 tiles): the A tiles [512 rows][128 B] of the
+// two stages are interleaved by halves (rows 0-255 of stages 0 and 1 at 0 and 32 KB, rows
+// 256-511 at 64 and 96 KB), then the W' tiles of stages 0 and 1 (16 KB each) at 128 and
+// 144 KB.  Every stage offset (32 KB, 16 KB) then fits the 16-bit immediate of a DS
+// instruction, so with the stage known at compile time each address is a loop-invariant
+// per-lane base plus an immediate.
+constexpr int A_STAGE_OFF = 32768;
+constexpr int W_REGION = 131072;
+constexpr int W_STAGE_OFF = 16384;
+__device__ __forceinline__ int a_off(int row, int chunk) { return tile_off(row, chunk) + ((row >> 8) << 15); }
+
 // Backward W' tile [64 n][TN k] with 2 TN-byte rows, read by ds_read_b64_tr_b16:
 // 32-byte segment u (16 k values) of row r sits at u ^ 2(r & 3), so the 4 rows x 2
 // segments that 32 lanes read in one pass land on distinct banks.
@@ -110,6 +121,8 @@ template <bool BWD, int TM, int TN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fused(FusedArgs a, Nf4Table tab) {
     using G = FusedTile<TM, TN>;
+    static_assert(G::A_BYTES == 2 * A_STAGE_OFF && G::W_BYTES == W_STAGE_OFF && G::LDS == W_REGION + 2 * W_STAGE_OFF,
+                  "stage layout");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
@@ -207,7 +220,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     auto store_a = [&](const XRegs<G::ACH>& X, uint8_t* sA) {
 #pragma unroll
         for (int i = 0; i < G::ACH; ++i)
-            *reinterpret_cast<uint4*>(sA + tile_off((tid >> 3) + 32 * i, achunk)) = X.r[i];
+            *reinterpret_cast<uint4*>(sA + a_off((tid >> 3) + 32 * i, achunk)) = X.r[i];
     };
 
     f32x16 acc[4][4];
@@ -216,14 +229,25 @@ void k_fused(FusedArgs a, Nf4Table tab) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    // B fragment of MFMA column tile j, substep sub (16 contraction values)
+    // B fragment of MFMA column tile j, substep sub (16 contraction values).  Backward: the
+    // swizzle of wt_off depends on row & 3 only, so rows 16 sub + r and r + 4 sit at fixed
+    // distances from row r: one per-lane base per column tile, the rest immediates.
+    // (the bases hold the W' region's offset, which exceeds an immediate; the stage, substep
+    // and second-read offsets do not)
+    int bt_abs[4] = {0, 0, 0, 0};
+    if constexpr (BWD) {
+        const int g = lane >> 4, jl = lane & 15;
+        const int row0 = 8 * (g >> 1) + (jl >> 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bt_abs[j] = W_REGION + wt_off<TN>(row0, wn * 128 + j * 32 + 16 * (g & 1) + 4 * (jl & 3));
+    }
     auto read_b = [&](const uint8_t* sB, int j, int sub) -> bf16x8 {
         if constexpr (BWD) {
-            const int g = lane >> 4, jl = lane & 15;
-            const int row = 16 * sub + 8 * (g >> 1) + (jl >> 2);
-            const int k = wn * 128 + j * 32 + 16 * (g & 1) + 4 * (jl & 3);
-            const uint2 lo = ds_read_tr16(sB + wt_off<TN>(row, k));
-            const uint2 hi = ds_read_tr16(sB + wt_off<TN>(row + 4, k));
+            const int soff = (int)(sB - (lds + W_REGION));      // the stage's offset (0 or 16 KB)
+            const uint8_t* p = lds + bt_abs[j] + (soff + sub * 16 * (2 * TN));
+            const uint2 lo = ds_read_tr16(p);
+            const uint2 hi = ds_read_tr16(p + 4 * (2 * TN));
             return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         } else {
             const int rb = wn * 128 + j * 32 + (lane & 31);
@@ -238,7 +262,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 bf16x8 fa[4], fb[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    fa[i] = *reinterpret_cast<const bf16x8*>(sA + tile_off(wm * 128 + i * 32 + (lane & 31), ch));
+                    fa[i] = *reinterpret_cast<const bf16x8*>(sA + a_off(wm * 128 + i * 32 + (lane & 31), ch));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) fb[j] = read_b(sB, j, sub);
 #pragma unroll
@@ -265,21 +289,21 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     // every chunk has six regions to arrive.  With one set the decode of the next W'
     // tile runs in regions 3-7, away from the A-tile writes of the first regions.
     BlockCodes<G::NW> wcur;
-    auto step_body = [&](int64_t it, XRegs<G::ACH>& xn, const XRegs<G::ACH>& xw) {
-        const int st = (int)(it & 1);
-        const uint8_t* cur = lds + st * G::STAGE;
-        uint8_t* nxt = lds + (st ^ 1) * G::STAGE;
+    // (stage_tag: the stage of step `it`, it & 1, as a compile-time constant)
+    auto step_body = [&](auto stage_tag, int64_t it, XRegs<G::ACH>& xn, const XRegs<G::ACH>& xw) {
+        constexpr int st = decltype(stage_tag)::value;
         const int64_t n2 = it + 2 < steps ? it + 2 : steps - 1;
         const BlockCodes<G::NW> wnxt = load_codes(n2);
         const __amdgpu_buffer_rsrc_t rs_an = a_rsrc(n2);
-        uint8_t* sWn = nxt + G::A_BYTES;
-        const uint8_t* sA = cur;
-        const uint8_t* sB = cur + G::A_BYTES;
+        const uint8_t* sA = lds + st * A_STAGE_OFF;
+        uint8_t* sAn = lds + (st ^ 1) * A_STAGE_OFF;
+        const uint8_t* sB = lds + W_REGION + st * W_STAGE_OFF;
+        uint8_t* sWn = lds + W_REGION + (st ^ 1) * W_STAGE_OFF;
 
         bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            fa[0][i] = *reinterpret_cast<const bf16x8*>(sA + tile_off(wm * 128 + i * 32 + (lane & 31), (lane >> 5)));
+            fa[0][i] = *reinterpret_cast<const bf16x8*>(sA + a_off(wm * 128 + i * 32 + (lane & 31), (lane >> 5)));
 #pragma unroll
         for (int j = 0; j < 4; ++j) fb[0][j] = read_b(sB, j, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -294,7 +318,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 if (half == 0) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        fa[fc ^ 1][i] = *reinterpret_cast<const bf16x8*>(sA + tile_off(wm * 128 + i * 32 + (lane & 31), ch));
+                        fa[fc ^ 1][i] = *reinterpret_cast<const bf16x8*>(sA + a_off(wm * 128 + i * 32 + (lane & 31), ch));
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) fb[fc ^ 1][j] = read_b(sB, j, sub + 1);
@@ -314,7 +338,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     const int i = 2 * rg + q;
-                    *reinterpret_cast<uint4*>(nxt + tile_off((tid >> 3) + 32 * i, achunk)) = xw.r[i];
+                    *reinterpret_cast<uint4*>(sAn + a_off((tid >> 3) + 32 * i, achunk)) = xw.r[i];
                 }
                 if (rg >= 2) {
 #pragma unroll
@@ -355,7 +379,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
             *reinterpret_cast<uint4*>(sWn + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
         }
         if constexpr (G::DEPTH == 2) {
-            store_a(xw, nxt);
+            store_a(xw, sAn);
         } else {
             // the last four chunks of the A tile of step it+2
 #pragma unroll
@@ -371,7 +395,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         load_a(xa, 0);
         const BlockCodes<G::NW> b0 = load_codes(0);
         store_a(xa, lds);
-        dequant_store(lds + G::A_BYTES, b0);
+        dequant_store(lds + W_REGION, b0);
     }
     if constexpr (G::DEPTH == 2) {
         load_a(xb, steps > 1 ? 1 : 0);
@@ -387,12 +411,17 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     if constexpr (G::DEPTH == 2) {
         int64_t it = 0;
         for (; it + 1 < steps; it += 2) {
-            step_body(it, xa, xb);
-            step_body(it + 1, xb, xa);
+            step_body(std::integral_constant<int, 0>{}, it, xa, xb);
+            step_body(std::integral_constant<int, 1>{}, it + 1, xb, xa);
         }
-        if (it < steps) step_body(it, xa, xb);
+        if (it < steps) step_body(std::integral_constant<int, 0>{}, it, xa, xb);
     } else {
-        for (int64_t it = 0; it < steps; ++it) step_body(it, xa, xa);
+        int64_t it = 0;
+        for (; it + 1 < steps; it += 2) {
+            step_body(std::integral_constant<int, 0>{}, it, xa, xa);
+            step_body(std::integral_constant<int, 1>{}, it + 1, xa, xa);
+        }
+        if (it < steps) step_body(std::integral_constant<int, 0>{}, it, xa, xa);
     }
 
     // ---- rank-r adapter term, staged through stage 0 in rank chunks of 64 ----
@@ -401,8 +430,8 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     // (piece 0 only, for a split tile)
     const int rr = u.split <= 0 ? a.r : 0;
     for (int rc = 0; rc < rr; rc += 64) {
-        uint8_t* sR = lds;
-        uint8_t* sL = lds + G::A_BYTES;
+        uint8_t* sR = lds;                 // stage 0 of the layout above
+        uint8_t* sL = lds + W_REGION;
 #pragma unroll
         for (int i = 0; i < TM * 8 / 256; ++i) {
             const int qi = tid + 256 * i;
@@ -411,7 +440,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
             const int64_t gm = m0 + row;
             uint4 v = make_uint4(0, 0, 0, 0);
             if (col < a.r && gm < a.M) v = *reinterpret_cast<const uint4*>(a.Rk + gm * a.r + col);
-            *reinterpret_cast<uint4*>(sR + tile_off(row, c)) = v;
+            *reinterpret_cast<uint4*>(sR + a_off(row, c)) = v;
         }
 #pragma unroll
         for (int i = 0; i < TN * 8 / 256; ++i) {
