@@ -111,12 +111,14 @@ const Nf4Table& table() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Limits of the linear products, checked before anything is enqueued.  The adapter
-// products and the fused tiles address an operand through 32-bit per-lane offsets over
-// up to 512 rows of its leading dimension (N or K); a launch holds at most 2^24
-// workgroups of 256 threads (2^32 work-items); the adapter products stack the token
-// rows in 128-row workgroups along the grid's second dimension.
-constexpr int64_t LINEAR_DIM_LIMIT = (int64_t)1 << 22;
+// Limits of the linear products, checked before anything is enqueued.  The fused tiles
+// read 512 rows of an operand whose leading dimension is K (forward) or N (backward)
+// through one buffer descriptor, whose range the hardware caps at 2^31 - 1 bytes, so N
+// and K are at most nf4::FUSED_LD_LIMIT (2,101,255); the adapter products' and the
+// few-token forward's offsets are smaller.  A launch holds at most 2^24 workgroups of
+// 256 threads (2^32 work-items); the adapter products stack the token rows in 128-row
+// workgroups along the grid's second dimension.
+constexpr int64_t LINEAR_DIM_LIMIT = nf4::FUSED_LD_LIMIT;
 constexpr int64_t LINEAR_M_LIMIT = (int64_t)1 << 23;
 constexpr int64_t FUSED_GRID_LIMIT = (int64_t)1 << 24;
 
@@ -140,8 +142,10 @@ nf4_status check_weight(const nf4_weight* W, WeightView& v, bool linear) {
         if (W->rows == 0 || W->cols == 0) return fail(NF4_ERR_ARG, "empty weight");
         // the fused kernels address the packed weight through 32-bit buffer offsets
         if (n / 2 >= ((int64_t)1 << 31)) return fail(NF4_ERR_UNSUPPORTED, "weight larger than 2^32 values");
-        if (W->rows >= LINEAR_DIM_LIMIT || W->cols >= LINEAR_DIM_LIMIT)
-            return fail(NF4_ERR_UNSUPPORTED, "N (rows) and K (cols) must be below 2^22");
+        if (W->rows > LINEAR_DIM_LIMIT || W->cols > LINEAR_DIM_LIMIT)
+            return fail(NF4_ERR_UNSUPPORTED,
+                        "N (rows) and K (cols) must be at most 2101255 (512 operand rows within a "
+                        "2^31-byte buffer range)");
     }
     if (!aligned(W->codes, 16)) return fail(NF4_ERR_ARG, "codes must be 16-byte aligned");
     if (!plain && (!aligned(W->c2, 4) || !aligned(W->mean, 4))) return fail(NF4_ERR_ARG, "misaligned c2/mean");

@@ -69,9 +69,14 @@ __global__ __launch_bounds__(CB_THREADS) void k_codebook_stats(const T* __restri
     auto one = [&](float v, uint32_t code, float c, float y) {
         atomicAdd(my_cnt + code * CB_THREADS, 1u);
         if (c != 0.0f) {
-            const float q = v * y;
-            const float r = __fmaf_rn(-c, q, v);
-            const float x = __fmaf_rn(r, y, q);
+            float x;
+            if (__builtin_expect(c >= 0x1p-126f && c < 0x1p126f, 1)) {
+                const float q = v * y;
+                const float r = __fmaf_rn(-c, q, v);
+                x = __fmaf_rn(r, y, q);
+            } else {
+                x = __fdiv_rn(v, c);      // reciprocal subnormal, zero or infinite
+            }
             atomicAdd(my_sum + code * CB_THREADS, (double)x);
             const float wq = s_lv[code] * c;
             const double e = (double)v - (double)wq;

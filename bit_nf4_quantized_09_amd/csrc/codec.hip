@@ -17,13 +17,15 @@ namespace nf4 {
 // lane encodes its values and writes one 32-bit word of codes.  A workgroup takes
 // 32 blocks per step and strides over the tensor.
 //
-// Division: x = fp32(w / absmax) is formed from the correctly rounded reciprocal
-// y = RN(1/absmax) (one IEEE division per lane) as q = RN(w y), r = w - absmax q
-// (exact, fma), x = RN(q + r y).  By Markstein's theorem (y within half an ulp of
-// 1/absmax, q within one ulp of the quotient) this is the IEEE quotient whenever it
-// is a normal number.  A quotient small enough to be subnormal lies far inside
-// (-t, t) for the smallest encode threshold t ~ 0.04, so its code is the zero
-// level whichever way it rounds: the codes equal those of the IEEE division.
+// Division: for an absmax in [2^-126, 2^126), x = fp32(w / absmax) is formed from the
+// correctly rounded reciprocal y = RN(1/absmax) (a normal number there; one IEEE
+// division per lane) as q = RN(w y), r = w - absmax q (exact, fma), x = RN(q + r y).
+// By Markstein's theorem (y within half an ulp of 1/absmax, q within one ulp of the
+// quotient) this is the IEEE quotient whenever it is a normal number.  A quotient
+// small enough to be subnormal lies far inside (-t, t) for the smallest encode
+// threshold t ~ 0.04, so its code is the zero level whichever way it rounds: the
+// codes equal those of the IEEE division.  Blocks with an absmax outside that range
+// (subnormal, above 2^126, infinite) take the IEEE division itself.
 //
 // Encode: the code is the number of thresholds below x (nearest level, a value
 // exactly between two levels taking the lower code).  |x| <= 1, so bucket
@@ -41,9 +43,11 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ w, int64
                                                   float* __restrict__ absmax, Nf4Table tab) {
     constexpr int EPL = 8;                 // values per lane
     constexpr int LPB = 64 / EPL;          // lanes per 64-value block
-    __shared__ uint2 s_bucket[65];         // {thresholds below, threshold bits}
-    if (threadIdx.x < 65) {
-        const float lo = (float)((int)threadIdx.x - 32) * (1.0f / 32.0f);
+    // {thresholds below, threshold bits}: entry 1 + b for bucket b; entry 0 takes a NaN
+    // quotient (no threshold below it and none to pass: code 0)
+    __shared__ uint2 s_bucket[66];
+    if (threadIdx.x < 66) {
+        const float lo = (float)((int)threadIdx.x - 33) * (1.0f / 32.0f);
         const float hi = lo + 1.0f / 32.0f;
         uint32_t below = 0;
         float th = __builtin_inff();
@@ -52,7 +56,8 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ w, int64
             below += tab.th[j] < lo ? 1u : 0u;
             th = (tab.th[j] >= lo && tab.th[j] < hi) ? tab.th[j] : th;
         }
-        s_bucket[threadIdx.x] = make_uint2(below, __float_as_uint(th));
+        s_bucket[threadIdx.x] = threadIdx.x == 0 ? make_uint2(0u, 0x7F800000u)   // +inf
+                                                 : make_uint2(below, __float_as_uint(th));
     }
     __syncthreads();
 
@@ -99,17 +104,31 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ w, int64
         for (int o = LPB / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, LPB));
         if (sub == 0) absmax[b] = m;
 
-        const float y = __fdiv_rn(1.0f, m);
+        float x[EPL];
+        if (__builtin_expect(m >= 0x1p-126f && m < 0x1p126f, 1)) {
+            const float y = __fdiv_rn(1.0f, m);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float q = v[e] * y;
+                const float r = __fmaf_rn(-m, q, v[e]);
+                x[e] = __fmaf_rn(r, y, q);
+            }
+        } else {
+            // a subnormal, huge or infinite absmax: the reciprocal would be subnormal,
+            // infinite or zero, so the IEEE division itself
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) x[e] = __fdiv_rn(v[e], m);
+        }
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            const float q = v[e] * y;
-            const float r = __fmaf_rn(-m, q, v[e]);
-            const float x = __fmaf_rn(r, y, q);
-            // bucket index, clamped (a zero block gives NaN here; its codes are replaced below)
-            const int bi = min(max((int)floorf(x * 32.0f) + 32, 0), 64);
+            // table entry of the bucket, clamped in fp32 (|x| <= 1 puts every number in
+            // entries 1..65): a NaN quotient (a NaN value, or an infinite one over an
+            // infinite absmax) takes entry 0 and code 0, as the comparisons x > m_j all
+            // fail for it (a zero block gives NaN too; its codes are replaced below)
+            const int bi = (int)floorf(fminf(fmaxf(x[e] * 32.0f, -33.0f), 32.0f)) + 33;
             const uint2 bk = s_bucket[bi];
-            const uint32_t code = bk.x + (x > __uint_as_float(bk.y) ? 1u : 0u);
+            const uint32_t code = bk.x + (x[e] > __uint_as_float(bk.y) ? 1u : 0u);
             packed |= code << (4 * e);
         }
         if (m == 0.0f) packed = tab.zero_word;  // an all-zero block: the code of x = 0 (NF4: 7)

@@ -204,10 +204,13 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     // first row and ends with the tile's last row, so rows past M, and columns of the
     // last row past its end, read zero.  Backward columns past N of the other rows read
     // finite data of the next row and meet zeroed W' rows.
+    // (the ABI bounds ldA so that every offset, a_chunk_offset(tid, i, ldA) + 16 bytes,
+    // stays inside the descriptor's 2^31 - 1 byte range)
+    static_assert(TM == FUSED_TM && G::ACH == A_CHUNKS, "A-tile offsets of tile_map.h");
     const int achunk = tid & 7;
     const int64_t arows = a.M - m0 < TM ? a.M - m0 : TM;
-    const uint32_t a_voff0 = (uint32_t)(((tid >> 3) * ldA + achunk * 8) * 2);
-    const uint32_t a_rstride = (uint32_t)(32 * ldA * 2);    // bytes between chunk i and i+1
+    const uint32_t a_voff0 = (uint32_t)a_chunk_offset(tid, 0, ldA);
+    const uint32_t a_rstride = (uint32_t)(a_chunk_offset(tid, 1, ldA) - a_chunk_offset(tid, 0, ldA));
     auto a_rsrc = [&](int64_t lstep) {
         const int64_t step = sb + lstep;
         return make_rsrc(a.A + m0 * ldA + step * 64, arows * ldA * 2 - step * 128);

@@ -20,6 +20,22 @@ constexpr int XCDS = 8;                 // accelerator complex dies, each with i
 constexpr int XCD_CUS = 32;             // compute units per XCD (256 / 8)
 constexpr int GROUP_M = 4;              // token tiles per group of the tile order
 constexpr int MAX_SPLIT = 4;            // pieces per tail tile at most
+// The A operand of a fused tile (X forward, dY backward: TM rows of ldA bf16 values) is
+// read through a buffer descriptor whose range the hardware caps at 2^31 - 1 bytes, with
+// 32-bit per-lane offsets from the step's first column of the tile's first row.  A lane's
+// 16-byte chunk i of a step sits at row a_chunk_row(tid, i), byte a_chunk_byte(tid) of
+// the step's 128 (64 bf16), so the furthest chunk ends at (TM - 1) 2 ldA + 128 bytes:
+// the leading dimension of an operand a fused product reads (K forward, N backward) is
+// at most FUSED_LD_LIMIT.
+constexpr int A_CHUNKS = FUSED_TM / 32;  // 16-byte chunks per lane per step
+__host__ __device__ __forceinline__ int a_chunk_row(int tid, int i) { return (tid >> 3) + 32 * i; }
+__host__ __device__ __forceinline__ int a_chunk_byte(int tid) { return (tid & 7) * 16; }
+__host__ __device__ __forceinline__ int64_t a_chunk_offset(int tid, int i, int64_t ldA) {
+    return (int64_t)a_chunk_row(tid, i) * ldA * 2 + a_chunk_byte(tid);
+}
+constexpr int64_t DESC_RANGE_MAX = 0x7FFFFFFF;
+constexpr int64_t FUSED_LD_LIMIT = (DESC_RANGE_MAX - 128) / (2 * (FUSED_TM - 1));   // 2,101,255
+
 // Split of a launch's tail tiles along the contraction (S == 1: none).  A launch with
 // S > 1 needs `bytes` of split workspace: `tails` x S fp32 partial tiles, summed by a
 // second kernel.  A pure function of the shape.

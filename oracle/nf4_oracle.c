@@ -382,12 +382,6 @@ void orc_nf4_dequantize(const uint8_t* codes, const uint8_t* q, const float* c2,
 }
 
 /* ------------------------------------------------------------------------ */
-/* [PT]+[E2E] QLoRA linear layer, float64 from the exact operand values.    */
-/*   W' (N x K, row-major, the dequantized frozen weight), X (M x K),       */
-/*   A (r x K), B (N x r), s = alpha / r.                                    */
-/*   T = X A^T (M x r);  Y = X W'^T + s T B^T (M x N).                       */
-/* Rows of Y are computed for the row list `rows` (nrows entries); pass      */
-/* rows == NULL to compute every row.  T is always computed for all rows.   */
 /* [BQ] dequantization with plain first-level constants (double quantization    */
 /* off): w' = fp32(level[code] * absmax[i/64]).                               */
 void orc_nf4_dequantize_plain(const uint8_t* codes, const float* absmax, int64_t n, float* out)
@@ -403,6 +397,12 @@ void orc_nf4_dequantize_plain(const uint8_t* codes, const float* absmax, int64_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* [PT]+[E2E] QLoRA linear layer, float64 from the exact operand values.    */
+/*   W' (N x K, row-major, the dequantized frozen weight), X (M x K),       */
+/*   A (r x K), B (N x r), s = alpha / r.                                    */
+/*   T = X A^T (M x r);  Y = X W'^T + s T B^T (M x N).                       */
+/* Rows of Y are computed for the row list `rows` (nrows entries); pass      */
+/* rows == NULL to compute every row.  T is always computed for all rows.   */
 void orc_qlora_linear_fwd(const float* Wd, const float* X, const float* A, const float* B,
                           int64_t M, int64_t N, int64_t K, int64_t r, double alpha,
                           const int64_t* rows, int64_t nrows, double* Y, double* T)

@@ -4,12 +4,14 @@
  * thresholds being the largest fp32 values not above the midpoints of adjacent NF4 levels
  * ("Block-wise quantization in one page" and "NF4, derived from normal quantiles" on the
  * zerotofrontier.app "sft/peft" page: nearest level, ties to the lower code).  The kernel
- * instead reads bucket b = floor(32 x) + 32 of a 65-entry table holding the count of
- * thresholds below the bucket and the bucket's own threshold (+inf if none), and adds one
- * strict comparison.  This program takes the 16 levels (hex floats) on the command line,
- * builds both, and compares them for every fp32 x in [-1, 1] (both zeros and the
- * subnormals included).  It prints "<values checked> <mismatches> <max thresholds in a
- * bucket>".
+ * instead reads entry floor(clamp(32 x, -33, 32)) + 33 of a 66-entry table: entry 1 + b
+ * holds, for bucket b = floor(32 x) + 32, the count of thresholds below the bucket and the
+ * bucket's own threshold (+inf if none); entry 0 ({0, +inf}) is where a NaN quotient
+ * lands (the clamp's max returns the number operand), so it takes code 0 as every
+ * comparison x > m_j fails for it.  It adds one strict comparison.  This program takes the
+ * 16 levels (hex floats) on the command line, builds both, and compares them for every
+ * fp32 x in [-1, 1] (both zeros and the subnormals included) and for NaN.  It prints
+ * "<values checked> <mismatches> <max thresholds in a bucket>".
  */
 #include <math.h>
 #include <stdint.h>
@@ -29,11 +31,11 @@ int main(int argc, char** argv) {
         if ((double)t > mid) t = nextafterf(t, -INFINITY);
         th[j] = t;
     }
-    uint32_t below[65];
-    float bth[65];
+    uint32_t below[66];
+    float bth[66];
     int most = 0;
-    for (int b = 0; b < 65; ++b) {
-        const float lo = (float)(b - 32) * (1.0f / 32.0f), hi = lo + 1.0f / 32.0f;
+    for (int b = 0; b < 66; ++b) {
+        const float lo = (float)(b - 33) * (1.0f / 32.0f), hi = lo + 1.0f / 32.0f;
         below[b] = 0;
         bth[b] = INFINITY;
         int in = 0;
@@ -42,6 +44,7 @@ int main(int argc, char** argv) {
             if (th[j] >= lo && th[j] < hi) { bth[b] = th[j]; ++in; }
         }
         if (in > most) most = in;
+        if (b == 0) { below[b] = 0; bth[b] = INFINITY; }
     }
     long bad = 0, n = 0;
     const uint32_t one = 0x3F800000u;      /* bits of 1.0f */
@@ -51,12 +54,17 @@ int main(int argc, char** argv) {
             const float x = from_bits((uint32_t)u | (sgn ? 0x80000000u : 0u));
             uint32_t ref = 0;
             for (int j = 0; j < 15; ++j) ref += x > th[j];
-            int b = (int)floorf(x * 32.0f) + 32;
-            b = b < 0 ? 0 : (b > 64 ? 64 : b);
+            const int b = (int)floorf(fminf(fmaxf(x * 32.0f, -33.0f), 32.0f)) + 33;
             const uint32_t got = below[b] + (x > bth[b]);
             bad += got != ref;
             ++n;
         }
+    }
+    {   /* a NaN quotient: no comparison holds, code 0 */
+        const float x = nanf("");
+        const int b = (int)floorf(fminf(fmaxf(x * 32.0f, -33.0f), 32.0f)) + 33;
+        bad += (below[b] + (x > bth[b])) != 0u;
+        ++n;
     }
     printf("%ld %ld %d\n", n, bad, most);
     return 0;

@@ -72,6 +72,24 @@ def test_stats_match_oracle(n, dtype, nf4_levels):
         np.testing.assert_allclose(sse, rsse, rtol=1e-10)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_stats_extreme_absmax(dtype, nf4_levels):
+    # blocks with a subnormal absmax or one above 2^126: the quotients x = w / absmax the
+    # statistics sum are the IEEE ones there too
+    ramp = np.linspace(-1.0, 1.0, 64)
+    rows = [(ramp * a).astype(np.float32) for a in (2e-39, 1e-44, 1e38, 3.0e38, 1.0)]
+    w = torch.from_numpy(np.stack(rows).reshape(-1)).to(dtype).to(DEV)
+    lv = [float(x) for x in nf4_levels]
+    codes, absmax = nf4.nf4_quantize_codebook(w, lv)
+    count, sum_x, sse = nf4.nf4_codebook_stats(w, codes, absmax, lv)
+    rc, rs, rsse = oracle.codebook_stats(_host(w), codes.cpu().numpy(), absmax.cpu().numpy(),
+                                         np.array(lv, np.float32))
+    assert np.array_equal(count, rc), "count"
+    assert np.all(np.isfinite(sum_x))
+    np.testing.assert_allclose(sum_x, rs, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(sse, rsse, rtol=1e-10)
+
+
 def test_stats_are_deterministic(nf4_levels):
     w = Draw(seed_of(33), DEV).normal((1 << 21,), 1.0)
     lv = [float(x) for x in nf4_levels]

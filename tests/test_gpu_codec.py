@@ -84,6 +84,58 @@ def test_codec_special_values():
     _assert_codec_equal(w, w.to(DEV))
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_codec_extreme_absmax(dtype):
+    # blocks whose absmax lies outside [2^-126, 2^126): subnormal (its reciprocal would
+    # overflow), above 2^126 (a subnormal reciprocal) and the largest finite value.  The
+    # codes must still be those of the IEEE quotient w / absmax, e.g. 0xC2 for the pair
+    # (+0.5, -0.5) x absmax at absmax 2e-39
+    ramp = np.linspace(-1.0, 1.0, 64)
+    rows = []
+    amaxes = [2e-39, 1e-44, 1.1754942e-38, 1e38, 3.0e38]
+    if dtype == torch.float32:
+        amaxes.append(float(np.finfo(np.float32).max))     # rounds to inf in bf16
+    for amax in amaxes:
+        blk = (ramp * amax).astype(np.float32)
+        blk[0] = np.float32(-amax)
+        blk[1] = np.float32(amax)
+        blk[2] = np.float32(0.5 * amax)
+        blk[3] = np.float32(-0.5 * amax)
+        rows.append(blk)
+    w = torch.from_numpy(np.stack(rows)).to(dtype)
+    ref = _assert_codec_equal(w, w.to(DEV), check_dequant=False)
+    assert ref["codes"][0] == 0xF0 and ref["codes"][1] == 0x2C, "oracle codes of -1, 1, 0.5, -0.5 x absmax"
+
+
+def test_codec_non_finite_values():
+    # outside the linear layer's domain, but the codec's codes and constants still follow
+    # the IEEE arithmetic of the definition: an infinite value makes the block's absmax
+    # infinite, finite values then divide to zero (code 7) and the infinite one to NaN,
+    # which no threshold is below (code 0); a NaN value is no larger than the others, so
+    # the absmax comes from the finite values, and its quotient takes code 0; an all-NaN
+    # block has absmax 0 and the zero code
+    rng = np.random.Generator(np.random.PCG64(17))
+    rows = [rng.standard_normal(64).astype(np.float32) * 0.02 for _ in range(5)]
+    rows[0][3] = np.inf
+    rows[1][60] = -np.inf
+    rows[2][7] = np.nan
+    rows[2][8] = np.nan
+    rows[3][:] = np.nan
+    rows[4][0] = np.inf
+    rows[4][1] = np.nan
+    rows[4][2] = -np.inf
+    w = torch.from_numpy(np.stack(rows))
+    for dt in (torch.float32, torch.bfloat16):
+        wt = w.to(dt)
+        h = bf16_bits(wt).reshape(-1) if dt == torch.bfloat16 else host_f32(wt).reshape(-1)
+        rc, ra = oracle.nf4_quantize(h)
+        codes, absmax = nf4.nf4_quantize(wt.to(DEV))
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), rc), "codes (%s)" % dt
+        assert np.array_equal(absmax.cpu().numpy().view(np.uint32), ra.view(np.uint32)), "absmax (%s)" % dt
+    assert rc[1] & 0x0F == 0 and rc[3 * 32] == 0x77         # inf -> code 0; all-NaN block -> 7
+
+
 def test_double_quant_constant_and_mean_tree():
     # a constant absmax vector gives c2 = 0, q = 0 and c1' == mean exactly
     c1 = torch.full((5000,), 0.0625)

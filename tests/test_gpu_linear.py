@@ -149,10 +149,16 @@ def test_deterministic():
         assert torch.equal(x, y)
 
 
-def _sampled_rows(M, n, seed):
+def _sampled_rows(M, per_band, seed, band=32):
+    """`per_band` random token rows out of every `band` consecutive rows, plus the first
+    and the last.  With band = 32 every 32-row MFMA tile of every wave (a wave owns 128
+    rows of a 512-row output tile) contributes a row; with band = 128, every wave of
+    every output tile."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, n)]))
-    return rows.astype(np.int64)
+    picks = [[0, M - 1]]
+    for b0 in range(0, M, band):
+        picks.append(b0 + rng.integers(0, min(band, M - b0), per_band))
+    return np.unique(np.concatenate(picks)).astype(np.int64)
 
 
 @pytest.mark.parametrize("proj", ["q", "gate", "down"])
@@ -161,16 +167,66 @@ def test_full_llama7b_shapes_sampled(proj):
     (name, N, K), = [p for p in layer_projections(LLAMA7B["d"], LLAMA7B["ffn"]) if p[0] == proj]
     M = 2048
     W, X, A, B, dY = linear_inputs(N, K, M, 64, seed=seed_of(20, N, K), device=DEV)
-    _run(W, X, A, B, dY, alpha=16.0, rows=_sampled_rows(M, 24, 1))
+    _run(W, X, A, B, dY, alpha=16.0, rows=_sampled_rows(M, 1, 1))
 
 
-@pytest.mark.parametrize("proj", ["gate", "down"])
+@pytest.mark.parametrize("proj", ["q", "gate", "down"])
 def test_full_llama65b_shapes_sampled(proj):
+    # one row out of every 32-row MFMA tile of every wave and output tile (128 of 4096)
     from workloads import LLAMA65B, layer_projections
     (name, N, K), = [p for p in layer_projections(LLAMA65B["d"], LLAMA65B["ffn"]) if p[0] == proj]
     M = 4096
     W, X, A, B, dY = linear_inputs(N, K, M, 64, seed=seed_of(21, N, K), device=DEV)
-    _run(W, X, A, B, dY, alpha=16.0, rows=_sampled_rows(M, 12, 2))
+    _run(W, X, A, B, dY, alpha=16.0, rows=_sampled_rows(M, 1, 2))
+
+
+def test_llama65b_layer_chain_sampled():
+    # The 65B layer as the benchmark runs it: the seven forwards in layer order (q, k, v,
+    # o, gate, up, down), each saving T, then the seven backwards in reverse order with
+    # the saved T; every output against the oracle, Y and dX on two rows of every wave of
+    # every 512-row output tile, T, dA and dB in full
+    from workloads import LLAMA65B, layer_projections
+    M, r, alpha = 4096, 64, 16.0
+    projs = layer_projections(LLAMA65B["d"], LLAMA65B["ffn"])
+    rows = _sampled_rows(M, 2, 25, band=128)
+    layer = []
+    for i, (name, N, K) in enumerate(projs):
+        W, X, A, B, dY = linear_inputs(N, K, M, r, seed=seed_of(25, i), device=DEV)
+        layer.append(dict(name=name, W=W, Wq=nf4.quantize_weight(W), X=X, A=A, B=B, dY=dY))
+    for p in layer:
+        print("chain forward", p["name"], flush=True)
+        p["Y"], p["T"] = nf4.qlora_linear_fwd(p["Wq"], p["X"], p["A"], p["B"], alpha)
+    for p in reversed(layer):
+        print("chain backward", p["name"], flush=True)
+        p["dX"], p["dA"], p["dB"] = nf4.qlora_linear_bwd(p["Wq"], p["X"], p["dY"], p["A"], p["B"], alpha, T=p["T"])
+    torch.cuda.synchronize()
+    for p in layer:
+        print("chain oracle", p["name"], flush=True)
+        ref = oracle_weight(p["W"].cpu())
+        assert np.array_equal(p["Wq"].codes.cpu().numpy(), ref["codes"]), p["name"]
+        assert np.array_equal(p["Wq"].q.cpu().numpy(), ref["q"]), p["name"]
+        Xh, Ah, Bh, dYh = (host_f32(t) for t in (p["X"], p["A"], p["B"], p["dY"]))
+        Yr, Tr = oracle.qlora_linear_fwd(ref["Wd"], Xh, Ah, Bh, alpha, rows=rows)
+        dXr, dAr, dBr = oracle.qlora_linear_bwd(ref["Wd"], Xh, dYh, Ah, Bh, alpha, rows=rows)
+        assert_close(p["name"] + " Y", to_np(p["Y"])[rows], Yr)
+        assert_close(p["name"] + " T", to_np(p["T"]), Tr)
+        assert_close(p["name"] + " dX", to_np(p["dX"])[rows], dXr)
+        assert_close(p["name"] + " dA", to_np(p["dA"]), dAr)
+        assert_close(p["name"] + " dB", to_np(p["dB"]), dBr)
+        for k in ("W", "Wq", "X", "dY", "Y", "dX"):
+            p[k] = None
+
+
+@pytest.mark.parametrize("N,K", [(8, 2101248), (2101248, 64)])
+def test_operand_rows_at_the_descriptor_limit(N, K):
+    # The fused tiles read 512 rows of X (row length K, forward) or dY (row length N,
+    # backward) through one buffer descriptor of at most 2^31 - 1 bytes; the ABI accepts
+    # N and K up to 2,101,255.  At the largest accepted multiples the last rows of the
+    # 512-row tile (rows 358-511 would have read as zero past 2^31 bytes) must carry their
+    # products: eight rows of every wave are compared
+    M = 512
+    W, X, A, B, dY = linear_inputs(N, K, M, 8, seed=seed_of(24, N, K), device=DEV)
+    _run(W, X, A, B, dY, alpha=16.0, rows=_sampled_rows(M, 8, 3, band=128))
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])

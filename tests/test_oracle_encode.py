@@ -136,6 +136,58 @@ def test_requantize_is_idempotent(orc, nf4_levels):
     assert np.array_equal(absmax, absmax2) and np.array_equal(codes, codes2)
 
 
+def test_dequantize_fixed_points(orc):
+    # Pins of the double-quantized dequantize that do not restate level x c1':
+    #  - code 7 is the exact zero level, so it decodes to +0 or -0 whatever c1' is;
+    #  - codes 0 and 15 are the levels -1 and +1 exactly, so they decode to -c1' and +c1'
+    #    bit for bit, and c1' comes from the oracle's constant decode alone;
+    #  - a block whose 64 values are +-v (v a power of two, so every quotient is exact)
+    #    has absmax v; codes 15/0 for +v/-v; dequantized back to +-c1' (the decoded
+    #    constant), and with every absmax equal, double quantization keeps c1' == v exactly
+    #    (c2 = 0, q = 0, c1' = mean): the weight comes back unchanged;
+    #  - re-encoding the dequantized weight with its decoded constants c1' as absmax
+    #    (those are the block maxima of w' whenever a block holds a code 0 or 15) gives the
+    #    same codes.
+    rng = np.random.Generator(np.random.PCG64(81))
+    n = 64 * 40
+    signs = np.where(rng.standard_normal(n) >= 0, 1.0, -1.0)
+    w = (signs * 0.03125).astype(np.float32)
+    codes, absmax = orc.nf4_quantize(w)
+    assert np.all(absmax == np.float32(0.03125))
+    c = _unpack(codes, n)
+    assert np.array_equal(c, np.where(signs > 0, 15, 0))
+    q, c2, mean = orc.double_quantize(absmax)
+    assert np.all(c2 == 0) and np.all(q == 0) and mean[0] == np.float32(0.03125)
+    out = orc.nf4_dequantize(codes, q, c2, mean, (n,))
+    assert np.array_equal(out.view(np.uint32), w.view(np.uint32))
+
+    # random weights: zero level exact, extremes at +-c1' bit for bit
+    w = (rng.standard_normal(64 * 500) * 0.02).astype(np.float32)
+    w[64 * 7: 64 * 8] = 0.0                                   # a zero block
+    n = w.size
+    codes, absmax = orc.nf4_quantize(w)
+    q, c2, mean = orc.double_quantize(absmax)
+    c1p = np.repeat(orc.double_dequantize(q, c2, mean), 64)
+    out = orc.nf4_dequantize(codes, q, c2, mean, (n,))
+    c = _unpack(codes, n)
+    assert np.all(out[c == 7] == 0.0)
+    assert np.array_equal(out[c == 15].view(np.uint32), c1p[c == 15].view(np.uint32))
+    assert np.array_equal(out[c == 0].view(np.uint32), (-c1p[c == 0]).view(np.uint32))
+    assert np.all(c[64 * 7: 64 * 8] == 7)
+    # every block holds its absmax element, code 0 or 15 (zero block aside)
+    has_ext = np.array([np.any((c[b * 64:(b + 1) * 64] == 0) | (c[b * 64:(b + 1) * 64] == 15))
+                        for b in range(n // 64)])
+    assert np.all(has_ext | (absmax == 0))
+    # re-encode with the decoded constants as absmax: the same codes
+    blocks = out.reshape(-1, 64)
+    bm = np.max(np.abs(blocks), axis=1)
+    ok = bm > 0
+    assert np.array_equal(bm[ok].view(np.uint32), np.abs(c1p.reshape(-1, 64)[ok, 0]).view(np.uint32))
+    codes2, absmax2 = orc.nf4_quantize(out)
+    ok_vals = np.repeat(ok & (c1p.reshape(-1, 64)[:, 0] > 0), 64)
+    assert np.array_equal(_unpack(codes2, n)[ok_vals], c[ok_vals])
+
+
 def test_dequantize_matches_definition(orc, nf4_levels):
     rng = np.random.Generator(np.random.PCG64(8))
     n = 64 * 300 + 17
