@@ -133,7 +133,7 @@ def test_codec_non_finite_values():
         torch.cuda.synchronize()
         assert np.array_equal(codes.cpu().numpy(), rc), "codes (%s)" % dt
         assert np.array_equal(absmax.cpu().numpy().view(np.uint32), ra.view(np.uint32)), "absmax (%s)" % dt
-    assert rc[1] & 0x0F == 0 and rc[3 * 32] == 0x77         # inf -> code 0; all-NaN block -> 7
+    assert (rc[1] >> 4) == 0 and rc[3 * 32] == 0x77           # inf (element 3) -> code 0; all-NaN block -> 7
 
 
 def test_double_quant_constant_and_mean_tree():
