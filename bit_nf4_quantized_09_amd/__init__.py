@@ -24,7 +24,7 @@ __all__ = [
     "nf4_double_dequantize", "nf4_dequantize", "quantize_weight", "qlora_linear_fwd",
     "qlora_linear_bwd", "nf4_storage_bytes", "nf4_codebook", "nf4_workspace_bytes",
     "nf4_profile_next_fused", "adamw_step", "adamw_step_paged", "PagedAdamW",
-    "nf4_quantize_codebook", "nf4_codebook_stats", "codebook_int4_symmetric", "codebook_uniform16",
+    "nf4_quantize_codebook", "nf4_codebook_stats", "qlora_linear_fwd_noalloc", "codebook_int4_symmetric", "codebook_uniform16",
     "lloyd_codebook", "NF4_OP_CODEBOOK_STATS",
     "NF4_OP_DOUBLE_QUANTIZE", "NF4_OP_LINEAR_FWD", "NF4_OP_LINEAR_BWD",
 ]
@@ -80,6 +80,9 @@ def load_library():
     L.qlora_linear_fwd.restype = ctypes.c_int
     L.qlora_linear_fwd.argtypes = [ctypes.POINTER(_Weight), _vp, _i64, _vp, _vp, _i32, ctypes.c_float,
                                    _vp, _vp, _vp, _sz, _vp]
+    L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
+    L.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_Weight), _vp, _i64, _vp, _vp, _i32, ctypes.c_float,
+                                           _vp, _vp, _vp]
     L.qlora_linear_bwd.restype = ctypes.c_int
     L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_Weight), _vp, _vp, _i64, _vp, _vp, _i32,
                                    ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -322,6 +325,39 @@ def qlora_linear_fwd(W: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
     d = W.descriptor()
     _check(L.qlora_linear_fwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(Y),
                               _ptr(T), _ptr(ws), wsb, _stream(X.device)))
+    return Y, T
+
+
+def qlora_linear_fwd_noalloc(W: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, alpha: float,
+                             Y: Optional[torch.Tensor] = None, T: Optional[torch.Tensor] = None,
+                             save_t: bool = True):
+    """qlora_linear_fwd through the allocation-free entry point: no workspace (the library's
+    fixed device scratch serves instead).  Y and T may be given (bf16 [M, N], [M, r]); then
+    the call allocates nothing at all.  Returns (Y, T or None)."""
+    L = load_library()
+    N, K = W.shape
+    _dev(X, "X", torch.bfloat16)
+    _dev(A, "A", torch.bfloat16)
+    _dev(B, "B", torch.bfloat16)
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [M, %d]" % K)
+    r = A.shape[0]
+    if tuple(A.shape) != (r, K) or tuple(B.shape) != (N, r):
+        raise ValueError("A must be [r, K] and B [N, r]")
+    M = X.shape[0]
+    _same_device(("W", W.codes), ("X", X), ("A", A), ("B", B))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    elif Y.dtype != torch.bfloat16 or tuple(Y.shape) != (M, N) or not Y.is_contiguous() or Y.device != X.device:
+        raise ValueError("Y must be a contiguous bf16 [%d, %d] tensor on %s" % (M, N, X.device))
+    if T is None and save_t:
+        T = torch.empty((M, r), dtype=torch.bfloat16, device=X.device)
+    elif T is not None and (T.dtype != torch.bfloat16 or tuple(T.shape) != (M, r) or not T.is_contiguous()
+                            or T.device != X.device):
+        raise ValueError("T must be a contiguous bf16 [%d, %d] tensor on %s" % (M, r, X.device))
+    d = W.descriptor()
+    _check(L.qlora_linear_fwd_noalloc(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(Y),
+                                      _ptr(T), _stream(X.device)))
     return Y, T
 
 

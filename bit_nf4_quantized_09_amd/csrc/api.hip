@@ -200,6 +200,31 @@ size_t bwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
     return b;
 }
 
+// Scratch of qlora_linear_fwd_noalloc: a file-scope device array (each GPU the library runs
+// on holds its own copy, at its own address, until the process ends).  In host code its
+// name is only a stand-in; the device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and that address is what the kernels get.
+static __device__ __align__(256) uint8_t scratch[NF4_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+hipError_t noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p || !aligned(p, 256)) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,6 +416,26 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     }
     e = nf4::launch_fused_fwd(v, c1, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, part, table(), hs);
     return hip_status(e, "qlora_linear_fwd (gemm)");
+}
+
+nf4_status qlora_linear_fwd_noalloc(const nf4_weight* W, const void* X, int64_t M, const void* A,
+                                    const void* B, int32_t r, float alpha, void* Y, void* T_out,
+                                    void* stream) {
+    // the size check needs only the shape; everything else is checked by qlora_linear_fwd
+    WeightView v;
+    nf4_status st = check_weight(W, v, true);
+    if (st != NF4_OK) return st;
+    if (M < 0) return fail(NF4_ERR_ARG, "M must be >= 0");
+    if (r < 0) return fail(NF4_ERR_UNSUPPORTED, "rank r must be in [1, 128]");
+    const size_t need = nf4_workspace_bytes(NF4_OP_LINEAR_FWD, M, v.rows, v.cols, r);
+    if (need > NF4_NOALLOC_SCRATCH_BYTES)
+        return fail(NF4_ERR_WORKSPACE, "this shape's forward needs " + std::to_string(need) +
+                                           " bytes of workspace, more than the 33554432-byte scratch of "
+                                           "qlora_linear_fwd_noalloc");
+    void* ws = nullptr;
+    hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd_noalloc (scratch address)");
+    return qlora_linear_fwd(W, X, M, A, B, r, alpha, Y, T_out, ws, NF4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, int64_t M,

@@ -21,7 +21,9 @@
  * Conventions shared by every entry point:
  *   - Memory: every pointer argument is device memory unless stated; the
  *     caller owns all buffers.  The library never allocates or frees device
- *     memory and keeps no pointer after a call returns.
+ *     memory and keeps no pointer after a call returns.  (The one device memory
+ *     of its own is the fixed scratch array of qlora_linear_fwd_noalloc, part of
+ *     the library's code object on each GPU it runs on.)
  *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls
  *     only enqueue work; inputs must stay alive until the stream has run it.
  *     No call synchronizes the host.
@@ -177,6 +179,26 @@ nf4_status nf4_dequantize(const nf4_weight* W, void* out, nf4_dtype out_dtype, v
 nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const void* A,
                             const void* B, int32_t r, float alpha, void* Y, void* T_out,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free variant of qlora_linear_fwd, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops (the few-token
+ * forward), harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * qlora_linear_fwd, without the workspace: the forward's workspace is taken from a
+ * fixed scratch array of NF4_NOALLOC_SCRATCH_BYTES (32 MiB) that the library keeps on
+ * every GPU it runs on until the process ends.  It covers, for example, the few-token
+ * forward (M <= 16) at every LLaMA-65B projection shape.
+ *   Errors: a shape whose nf4_workspace_bytes(NF4_OP_LINEAR_FWD, M, N, K, r) exceeds the
+ *           scratch returns NF4_ERR_WORKSPACE before anything is enqueued; other
+ *           arguments are checked as for qlora_linear_fwd.  The first call on a device
+ *           looks up that device's scratch address (NF4_ERR_HIP if that fails).
+ *   Concurrency: every call on one GPU uses the same scratch, which keeps the contents
+ *           of the last call (nothing in it needs to start at zero).  Calls that
+ *           overlap in time on one GPU (other streams, or host threads without stream
+ *           order between them) race on it and give wrong results. */
+#define NF4_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+nf4_status qlora_linear_fwd_noalloc(const nf4_weight* W, const void* X, int64_t M, const void* A,
+                                    const void* B, int32_t r, float alpha, void* Y, void* T_out,
+                                    void* stream);
 
 /* [E2E]+[PT]: QLoRA linear backward; the 4-bit weight receives no gradient.
  * With U = dY B:

@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
                             "nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
                             "nf4_workspace_bytes", "nf4_storage_bytes", "nf4_codebook",
                             "nf4_last_error", "nf4_profile_next_fused", "nf4_adamw_step",
-                            "nf4_adamw_step_paged", "nf4_quantize_codebook", "nf4_codebook_stats"])
+                            "nf4_adamw_step_paged", "nf4_quantize_codebook", "nf4_codebook_stats",
+                            "qlora_linear_fwd_noalloc"])
     for name in names:
         assert hasattr(L, name), name
     # and the C symbols are unmangled (extern "C")
@@ -165,6 +166,20 @@ def test_linear_rejects_bad_arguments():
     assert bwd(ctypes.byref(good), p, p, 16, p, p, 8, 16.0, p, p, None, p, ws, 1 << 20, None) == nf4.NF4_ERR_ARG
     assert bwd(ctypes.byref(good), p, p, 16, p, p, 8, 16.0, None, p, p, p, ws, 16, None) == nf4.NF4_ERR_WORKSPACE
     assert bwd(ctypes.byref(good), None, p, 16, p, p, 8, 16.0, p, p, p, p, ws, 1 << 20, None) == nf4.NF4_ERR_ARG
+
+
+def test_noalloc_forward_rejects_before_any_device_call():
+    # the allocation-free forward checks the shape's workspace against its fixed 32 MiB
+    # scratch on the host, before it looks up the scratch on a device
+    L = nf4.load_library()
+    p = ctypes.c_void_p(4096)
+    f = L.qlora_linear_fwd_noalloc
+    assert L.nf4_workspace_bytes(nf4.NF4_OP_LINEAR_FWD, 4096, 22016, 8192, 64) > (32 << 20)
+    assert f(ctypes.byref(_w(22016, 8192)), p, 4096, p, p, 64, 16.0, p, p, None) == nf4.NF4_ERR_WORKSPACE
+    assert b"33554432-byte scratch" in L.nf4_last_error()
+    assert f(None, p, 16, p, p, 8, 16.0, p, p, None) == nf4.NF4_ERR_ARG
+    assert f(ctypes.byref(_w(256, 250)), p, 16, p, p, 8, 16.0, p, p, None) == nf4.NF4_ERR_UNSUPPORTED
+    assert f(ctypes.byref(_w(256, 256)), p, -1, p, p, 8, 16.0, p, p, None) == nf4.NF4_ERR_ARG
 
 
 def test_dequantize_rejects_bad_arguments():
