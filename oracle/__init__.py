@@ -56,6 +56,9 @@ def _load():
     _d = ctypes.c_double
     lib.orc_adamw_step.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _d, _d, _d, _d, _d, _i64,
                                    _f64p, _f64p, _f64p]
+    lib.orc_svd_topr.argtypes = [_f64p, _i64, _i64, _i64, _f64p, _f64p, _f64p]
+    lib.orc_loftq.argtypes = [_f32p, _i64, _i64, _i64, _d, ctypes.c_int, _u8p, _u8p, _f32p, _f32p,
+                              _f64p, _f64p, _f64p]
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_pairwise_sum.restype = ctypes.c_double
     lib.orc_pairwise_sum.argtypes = [_f32p, _i64]
@@ -269,3 +272,38 @@ def nf4_dequantize_plain(codes, absmax, shape) -> np.ndarray:
     out = np.empty(n, np.float32)
     _load().orc_nf4_dequantize_plain(_p(codes, _u8p), _p(absmax, _f32p), n, _p(out, _f32p))
     return out.reshape(shape)
+
+
+def svd_topr(E, r):
+    """Top r singular triplets of E (float64 m x n) by one-sided Jacobi: (S descending,
+    U m x r, Vt r x n), so that U diag(S) Vt is the best rank-r approximation of E."""
+    E = np.ascontiguousarray(E, np.float64)
+    m, n = E.shape
+    assert 0 < r <= min(m, n)
+    S = np.zeros(r, np.float64)
+    U = np.zeros((m, r), np.float64)
+    Vt = np.zeros((r, n), np.float64)
+    _load().orc_svd_topr(_p(E, _f64p), m, n, r, _p(S, _f64p), _p(U, _f64p), _p(Vt, _f64p))
+    return S, U, Vt
+
+
+def loftq(W, r, gamma, iters):
+    """LoftQ-style initialisation ("Paged optimizers, and QLoRA end to end": start the
+    adapter so that dequant(W^NF4) + gamma B A is close to W): `iters` alternations of
+    NF4 + double quantization of the residual W - gamma B A and a rank-r truncated SVD of
+    the quantization error.  Returns dict(codes, q, c2, mean, B (N x r), A (r x K) float64,
+    err (per iteration ||W - dequant(Q_t) - gamma B_t A_t||_F))."""
+    W = np.ascontiguousarray(W, np.float32)
+    N, K = W.shape
+    n = N * K
+    n1 = (n + 63) // 64
+    codes = np.zeros((n + 1) // 2, np.uint8)
+    q = np.zeros(n1, np.uint8)
+    c2 = np.zeros((n1 + 255) // 256, np.float32)
+    mean = np.zeros(1, np.float32)
+    B = np.zeros((N, r), np.float64)
+    A = np.zeros((r, K), np.float64)
+    err = np.zeros(iters, np.float64)
+    _load().orc_loftq(_p(W, _f32p), N, K, r, float(gamma), int(iters), _p(codes, _u8p), _p(q, _u8p),
+                      _p(c2, _f32p), _p(mean, _f32p), _p(B, _f64p), _p(A, _f64p), _p(err, _f64p))
+    return dict(codes=codes, q=q, c2=c2, mean=mean, B=B, A=A, err=err)

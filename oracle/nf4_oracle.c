@@ -15,6 +15,10 @@
  *   [PT]  "Putting it together", forward formula   (prism.theerrors.in QLoRA explainer)
  *   AdamW: Kingma & Ba (2015) Algorithm 1 with Loshchilov & Hutter (2019)
  *          decoupled weight decay; the pages give only the paging and the rates
+ *   LoftQ: the pages ([E2E], closing remark) state only the goal, an adapter with
+ *          dequant(W^NF4) + gamma B A close to W; the alternation of quantizing the
+ *          residual and a rank-r truncated SVD of the quantization error is Li et
+ *          al. (2023); the SVD here is one-sided Jacobi (Hestenes 1958)
  *
  * Arithmetic conventions: fp32 operations are IEEE round-to-nearest-even,
  * compiled with -ffp-contract=off so that no multiply-add is silently fused.
@@ -394,6 +398,189 @@ void orc_nf4_dequantize_plain(const uint8_t* codes, const float* absmax, int64_t
         volatile float v = lv[code] * absmax[i / 64];
         out[i] = v;
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rank-r truncated SVD: the top r singular triplets of E (m x n, float64,   */
+/* row-major), whose sum  sum_i S_i U_i Vt_i  is the best rank-r             */
+/* approximation of E in Frobenius norm (Eckart-Young).  Computed by        */
+/* one-sided Jacobi (Hestenes): the columns of a working copy of E (of E^T   */
+/* when E has more columns than rows) are rotated pairwise, each rotation    */
+/* making one pair orthogonal, with the rotations accumulated into V, until */
+/* a whole sweep finds every pair orthogonal to working precision; then the */
+/* column norms are the singular values, the normalised columns the left    */
+/* singular vectors.  Pairs are visited in round-robin order (n/2 disjoint  */
+/* pairs per round), so a round's rotations commute.                          */
+/*   S: r values, descending; U: m x r; Vt: r x n (row-major).  r <= min(m,n). */
+/* ------------------------------------------------------------------------ */
+static void jacobi_columns(double* a, int64_t m, int64_t n, double* v)
+{
+    /* a: n columns of length m (column j at a + j*m); v: n x n, column j at v + j*n */
+    for (int64_t j = 0; j < n * n; ++j) v[j] = 0.0;
+    for (int64_t j = 0; j < n; ++j) v[j * n + j] = 1.0;
+    const int64_t nn = n + (n & 1);          /* an odd count gets a dummy column */
+    int64_t* slot = (int64_t*)malloc((size_t)nn * sizeof(int64_t));
+    for (int sweep = 0; sweep < 60; ++sweep) {
+        int rotated = 0;
+        for (int64_t j = 0; j < nn; ++j) slot[j] = j;
+        for (int64_t round = 0; round < nn - 1; ++round) {
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : rotated)
+            for (int64_t k = 0; k < nn / 2; ++k) {
+                int64_t p = slot[k], q = slot[nn - 1 - k];
+                if (p >= n || q >= n) continue;
+                if (p > q) { int64_t t = p; p = q; q = t; }
+                double* ap = a + p * m;
+                double* aq = a + q * m;
+                double alpha = 0.0, beta = 0.0, gamma = 0.0;
+                for (int64_t i = 0; i < m; ++i) {
+                    alpha += ap[i] * ap[i];
+                    beta += aq[i] * aq[i];
+                    gamma += ap[i] * aq[i];
+                }
+                if (gamma == 0.0 || fabs(gamma) <= 1e-15 * sqrt(alpha * beta)) continue;
+                rotated = 1;
+                /* the rotation angle that zeroes the pair's inner product */
+                const double zeta = (beta - alpha) / (2.0 * gamma);
+                const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+                const double c = 1.0 / sqrt(1.0 + t * t), sn = c * t;
+                for (int64_t i = 0; i < m; ++i) {
+                    const double x = ap[i], y = aq[i];
+                    ap[i] = c * x - sn * y;
+                    aq[i] = sn * x + c * y;
+                }
+                double* vp = v + p * n;
+                double* vq = v + q * n;
+                for (int64_t i = 0; i < n; ++i) {
+                    const double x = vp[i], y = vq[i];
+                    vp[i] = c * x - sn * y;
+                    vq[i] = sn * x + c * y;
+                }
+            }
+            /* round-robin: slot 0 stays, the others rotate by one */
+            const int64_t last = slot[nn - 1];
+            for (int64_t j = nn - 1; j > 1; --j) slot[j] = slot[j - 1];
+            slot[1] = last;
+        }
+        if (!rotated) break;
+    }
+    free(slot);
+}
+
+void orc_svd_topr(const double* E, int64_t m, int64_t n, int64_t r, double* S, double* U, double* Vt)
+{
+    const int tr = n > m;                    /* work on E^T: more columns than rows */
+    const int64_t rows = tr ? n : m, cols = tr ? m : n;
+    double* a = (double*)malloc((size_t)(rows * cols) * sizeof(double));
+    double* v = (double*)malloc((size_t)(cols * cols) * sizeof(double));
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            if (tr) a[i * n + j] = E[i * n + j];       /* column i of E^T = row i of E */
+            else a[j * m + i] = E[i * n + j];          /* column j of E */
+        }
+    jacobi_columns(a, rows, cols, v);
+    double* norm = (double*)malloc((size_t)cols * sizeof(double));
+    int64_t* order = (int64_t*)malloc((size_t)cols * sizeof(int64_t));
+    for (int64_t j = 0; j < cols; ++j) {
+        double t = 0.0;
+        for (int64_t i = 0; i < rows; ++i) t += a[j * rows + i] * a[j * rows + i];
+        norm[j] = sqrt(t);
+        order[j] = j;
+    }
+    for (int64_t i = 1; i < cols; ++i) {       /* descending singular values */
+        const int64_t o = order[i];
+        int64_t k = i;
+        while (k > 0 && norm[order[k - 1]] < norm[o]) { order[k] = order[k - 1]; --k; }
+        order[k] = o;
+    }
+    for (int64_t t = 0; t < r; ++t) {
+        const int64_t j = order[t];
+        S[t] = norm[j];
+        const double inv = norm[j] > 0.0 ? 1.0 / norm[j] : 0.0;
+        /* working matrix = (E or E^T) V: its normalised columns are the left singular
+           vectors of that matrix, V's columns its right ones */
+        for (int64_t i = 0; i < rows; ++i) {
+            const double lu = a[j * rows + i] * inv;
+            if (tr) Vt[t * n + i] = lu;        /* E^T = U' S V'^T  =>  E = V' S U'^T */
+            else U[i * r + t] = lu;
+        }
+        for (int64_t i = 0; i < cols; ++i) {
+            const double rv = v[j * cols + i];
+            if (tr) U[i * r + t] = rv;
+            else Vt[t * n + i] = rv;
+        }
+    }
+    free(a);
+    free(v);
+    free(norm);
+    free(order);
+}
+
+/* ------------------------------------------------------------------------ */
+/* [E2E] LoftQ-style initialisation of the adapter of a quantized base: the  */
+/* pages ask that dequant(W^NF4) + gamma B A start close to W ("Paged       */
+/* optimizers, and QLoRA end to end", closing remark on LoftQ, Li et al.     */
+/* 2023).  The published alternation, from B A = 0, repeated `iters` times:  */
+/*   Q_t = NF4 + double quantization of the residual  W - gamma B A  (fp32); */
+/*   E_t = W - dequant(Q_t)  (fp32, exact difference of two fp32 values     */
+/*         rounded once);                                                     */
+/*   U S V^T = the rank-r truncated SVD of E_t;                              */
+/*   B = U S^(1/2) / sqrt(gamma),  A = S^(1/2) V^T / sqrt(gamma).            */
+/* err[t] = || W - dequant(Q_t) - gamma B_t A_t ||_F, float64.  Outputs the  */
+/* last Q (codes, q, c2, mean) and B (N x r), A (r x K) in float64.          */
+/* ------------------------------------------------------------------------ */
+void orc_loftq(const float* W, int64_t N, int64_t K, int64_t r, double gamma, int iters,
+               uint8_t* codes, uint8_t* q, float* c2, float* mean, double* B, double* A, double* err)
+{
+    const int64_t n = N * K, n1 = (n + 63) / 64;
+    float* R = (float*)malloc((size_t)n * sizeof(float));
+    float* absmax = (float*)malloc((size_t)n1 * sizeof(float));
+    float* Wd = (float*)malloc((size_t)n * sizeof(float));
+    double* E = (double*)malloc((size_t)n * sizeof(double));
+    double* S = (double*)malloc((size_t)r * sizeof(double));
+    double* U = (double*)malloc((size_t)(N * r) * sizeof(double));
+    double* Vt = (double*)malloc((size_t)(r * K) * sizeof(double));
+    for (int64_t i = 0; i < N * r; ++i) B[i] = 0.0;
+    for (int64_t i = 0; i < r * K; ++i) A[i] = 0.0;
+    for (int t = 0; t < iters; ++t) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t k = 0; k < K; ++k) {
+                double ba = 0.0;
+                for (int64_t j = 0; j < r; ++j) ba += B[i * r + j] * A[j * K + k];
+                R[i * K + k] = (float)((double)W[i * K + k] - gamma * ba);
+            }
+        orc_nf4_quantize(R, 0, n, codes, absmax);
+        orc_double_quantize(absmax, n1, q, c2, mean);
+        orc_nf4_dequantize(codes, q, c2, mean, n, Wd);
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            volatile float e = W[i] - Wd[i];
+            E[i] = (double)e;
+        }
+        orc_svd_topr(E, N, K, r, S, U, Vt);
+        const double g = 1.0 / sqrt(gamma);
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t j = 0; j < r; ++j) B[i * r + j] = U[i * r + j] * sqrt(S[j]) * g;
+        for (int64_t j = 0; j < r; ++j)
+            for (int64_t k = 0; k < K; ++k) A[j * K + k] = sqrt(S[j]) * Vt[j * K + k] * g;
+        double e2 = 0.0;
+#pragma omp parallel for schedule(static) reduction(+ : e2)
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t k = 0; k < K; ++k) {
+                double ba = 0.0;
+                for (int64_t j = 0; j < r; ++j) ba += B[i * r + j] * A[j * K + k];
+                const double d = E[i * K + k] - gamma * ba;
+                e2 += d * d;
+            }
+        err[t] = sqrt(e2);
+    }
+    free(R);
+    free(absmax);
+    free(Wd);
+    free(E);
+    free(S);
+    free(U);
+    free(Vt);
 }
 
 /* ------------------------------------------------------------------------ */
