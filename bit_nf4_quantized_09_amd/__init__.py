@@ -26,12 +26,14 @@ __all__ = [
     "nf4_profile_next_fused", "adamw_step", "adamw_step_paged", "PagedAdamW",
     "nf4_quantize_codebook", "nf4_codebook_stats", "qlora_linear_fwd_noalloc", "codebook_int4_symmetric", "codebook_uniform16",
     "lloyd_codebook", "NF4_OP_CODEBOOK_STATS",
-    "NF4_OP_DOUBLE_QUANTIZE", "NF4_OP_LINEAR_FWD", "NF4_OP_LINEAR_BWD",
+    "NF4_OP_DOUBLE_QUANTIZE", "NF4_OP_LINEAR_FWD", "NF4_OP_LINEAR_BWD", "NF4_OP_LOWRANK_SVD", "NF4_OP_LOFTQ",
+    "nf4_lowrank_svd", "loftq_init",
 ]
 
 NF4_OK, NF4_ERR_ARG, NF4_ERR_UNSUPPORTED, NF4_ERR_WORKSPACE, NF4_ERR_HIP = range(5)
 NF4_F32, NF4_BF16 = 0, 1
 NF4_OP_DOUBLE_QUANTIZE, NF4_OP_LINEAR_FWD, NF4_OP_LINEAR_BWD, NF4_OP_CODEBOOK_STATS = 1, 2, 3, 4
+NF4_OP_LOWRANK_SVD, NF4_OP_LOFTQ = 5, 6
 _STATUS = {1: "NF4_ERR_ARG", 2: "NF4_ERR_UNSUPPORTED", 3: "NF4_ERR_WORKSPACE", 4: "NF4_ERR_HIP"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -106,6 +108,11 @@ def load_library():
     L.nf4_adamw_step_paged.restype = ctypes.c_int
     L.nf4_adamw_step_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _f, _f, _f, _f, _f, _i64,
                                        _vp, _sz, _vp]
+    L.nf4_lowrank_svd.restype = ctypes.c_int
+    L.nf4_lowrank_svd.argtypes = [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.nf4_loftq_init.restype = ctypes.c_int
+    L.nf4_loftq_init.argtypes = [_vp, _i64, _i64, _i32, _f, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _sz, _vp]
     L.nf4_last_error.restype = ctypes.c_char_p
     L.nf4_last_error.argtypes = []
     _lib = L
@@ -607,3 +614,55 @@ def lloyd_codebook(w: torch.Tensor, levels, iters: int = 30):
             break
         lv = new
     return lv
+
+
+def nf4_lowrank_svd(E: torch.Tensor, r: int, omega: torch.Tensor, power_iters: int = 2):
+    """Rank-r truncated SVD of an fp32 matrix by randomized subspace iteration with the
+    K x l test matrix omega: (U [N, r], S [r], V [K, r]), E ~ U diag(S) V^T."""
+    L = load_library()
+    _dev(E, "E", torch.float32)
+    _dev(omega, "omega", torch.float32)
+    if E.dim() != 2 or omega.dim() != 2 or omega.shape[0] != E.shape[1]:
+        raise ValueError("E must be [N, K] and omega [K, l]")
+    _same_device(("E", E), ("omega", omega))
+    N, K = E.shape
+    l = omega.shape[1]
+    U = torch.empty((N, r), dtype=torch.float32, device=E.device)
+    S = torch.empty(r, dtype=torch.float32, device=E.device)
+    V = torch.empty((K, r), dtype=torch.float32, device=E.device)
+    wsb = L.nf4_workspace_bytes(NF4_OP_LOWRANK_SVD, l, N, K, r)
+    ws = _workspace(wsb, E.device)
+    _check(L.nf4_lowrank_svd(_ptr(E), N, K, r, l, power_iters, _ptr(omega), _ptr(U), _ptr(S), _ptr(V), _ptr(ws),
+                             wsb, _stream(E.device)))
+    return U, S, V
+
+
+def loftq_init(W: torch.Tensor, r: int, alpha: float, omega: torch.Tensor, iters: int = 5, power_iters: int = 2):
+    """LoftQ-style initialisation for a weight W (fp32 [N, K]): `iters` alternations of
+    quantizing the residual W - (alpha/r) B A and a rank-r truncated SVD of the quantization
+    error.  Returns (NF4Weight, A bf16 [r, K], B bf16 [N, r], err float64 [iters] on the
+    device: ||W - dequant(Q_t) - (alpha/r) B_t A_t||_F per alternation)."""
+    L = load_library()
+    _dev(W, "W", torch.float32)
+    _dev(omega, "omega", torch.float32)
+    if W.dim() != 2 or omega.dim() != 2 or omega.shape[0] != W.shape[1]:
+        raise ValueError("W must be [N, K] and omega [K, l]")
+    _same_device(("W", W), ("omega", omega))
+    N, K = W.shape
+    l = omega.shape[1]
+    n = N * K
+    n1 = (n + 63) // 64
+    dev = W.device
+    codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev)
+    q = torch.empty(n1, dtype=torch.uint8, device=dev)
+    c2 = torch.empty((n1 + 255) // 256, dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    A = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
+    B = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    err = torch.empty(iters, dtype=torch.float64, device=dev)
+    wsb = L.nf4_workspace_bytes(NF4_OP_LOFTQ, l, N, K, r)
+    ws = _workspace(wsb, dev)
+    _check(L.nf4_loftq_init(_ptr(W), N, K, r, float(alpha), iters, l, power_iters, _ptr(omega), _ptr(codes),
+                            _ptr(q), _ptr(c2), _ptr(mean), _ptr(A), _ptr(B), _ptr(err), _ptr(ws), wsb,
+                            _stream(dev)))
+    return NF4Weight(codes, q, c2, mean, (int(N), int(K))), A, B, err

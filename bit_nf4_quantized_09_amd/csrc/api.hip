@@ -263,6 +263,10 @@ size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t 
             return 2 * rank_buffer_bytes(M, r) + c1_buffer_bytes(op, M, N, K) + fwd_partial_bytes(M, N, K, r);
         case NF4_OP_LINEAR_BWD:
             return 2 * rank_buffer_bytes(M, r) + c1_buffer_bytes(op, M, N, K) + bwd_partial_bytes(M, N, K, r);
+        case NF4_OP_LOWRANK_SVD:   // M carries the sketch width l
+            return (N > 0 && K > 0 && M > 0 && M <= nf4::LR_MAX && r > 0) ? nf4::lowrank_ws_bytes(N, K, (int)M, r) : 0;
+        case NF4_OP_LOFTQ:
+            return (N > 0 && K > 0 && M > 0 && M <= nf4::LR_MAX && r > 0) ? nf4::loftq_ws_bytes(N, K, (int)M, r) : 0;
         default: return 0;
     }
 }
@@ -504,6 +508,67 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     e = nf4::launch_lora_gemm(g, true, Tb, true, v.rows, r, M, part, s, dB, true, false, nullptr,
                               0.0f, hs);
     return hip_status(e, "qlora_linear_bwd (dB)");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the rank-r SVD and the LoftQ initialisation (host only).
+nf4_status check_lowrank(const float* E, int64_t N, int64_t K, int32_t r, int32_t l, int32_t power_iters,
+                         const float* omega) {
+    if (!E || !omega) return fail(NF4_ERR_ARG, "matrix or omega is NULL");
+    if (N < 1 || K < 1) return fail(NF4_ERR_ARG, "N and K must be >= 1");
+    if (N >= ((int64_t)1 << 22) || K >= ((int64_t)1 << 22)) return fail(NF4_ERR_UNSUPPORTED, "N and K must be below 2^22");
+    if (N * K >= ((int64_t)1 << 32)) return fail(NF4_ERR_UNSUPPORTED, "N*K must be below 2^32");
+    if (r < 1 || l < r) return fail(NF4_ERR_ARG, "need 1 <= r <= l");
+    if (l > nf4::LR_MAX) return fail(NF4_ERR_UNSUPPORTED, "sketch width l must be at most 96");
+    if (l > N || l > K) return fail(NF4_ERR_ARG, "sketch width l must not exceed N or K");
+    if (power_iters < 0 || power_iters > 16) return fail(NF4_ERR_ARG, "power_iters must be in [0, 16]");
+    if (!aligned(E, 16) || !aligned(omega, 4)) return fail(NF4_ERR_ARG, "the matrix must be 16-byte aligned, omega 4-byte");
+    return NF4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nf4_status nf4_lowrank_svd(const float* E, int64_t N, int64_t K, int32_t r, int32_t l, int32_t power_iters,
+                           const float* omega, float* U, float* S, float* V, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    nf4_status st = check_lowrank(E, N, K, r, l, power_iters, omega);
+    if (st != NF4_OK) return st;
+    if (!U || !S || !V) return fail(NF4_ERR_ARG, "U, S or V is NULL");
+    if (!aligned(U, 4) || !aligned(S, 4) || !aligned(V, 4)) return fail(NF4_ERR_ARG, "misaligned U, S or V");
+    const size_t need = nf4::lowrank_ws_bytes(N, K, l, r);
+    if (!workspace || workspace_bytes < need)
+        return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LOWRANK_SVD)");
+    if (!aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
+    return hip_status(nf4::launch_lowrank_svd(E, N, K, r, l, power_iters, omega, U, S, V, workspace,
+                                              (hipStream_t)stream),
+                      "nf4_lowrank_svd");
+}
+
+nf4_status nf4_loftq_init(const float* W, int64_t N, int64_t K, int32_t r, float alpha, int32_t iters, int32_t l,
+                          int32_t power_iters, const float* omega, uint8_t* codes, uint8_t* q, float* c2,
+                          float* mean, void* A, void* B, double* err, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    nf4_status st = check_lowrank(W, N, K, r, l, power_iters, omega);
+    if (st != NF4_OK) return st;
+    if (!(alpha > 0.0f) || !isfinite(alpha)) return fail(NF4_ERR_ARG, "alpha must be positive and finite");
+    if (iters < 1 || iters > 64) return fail(NF4_ERR_ARG, "iters must be in [1, 64]");
+    if (!codes || !q || !c2 || !mean || !A || !B || !err) return fail(NF4_ERR_ARG, "an output is NULL");
+    if (!aligned(codes, 4) || !aligned(q, 4) || !aligned(c2, 4) || !aligned(mean, 4) || !aligned(A, 2) ||
+        !aligned(B, 2) || !aligned(err, 8))
+        return fail(NF4_ERR_ARG, "misaligned output");
+    const size_t need = nf4::loftq_ws_bytes(N, K, l, r);
+    if (!workspace || workspace_bytes < need)
+        return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LOFTQ)");
+    if (!aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
+    const float gamma = alpha / (float)r;
+    return hip_status(nf4::launch_loftq(W, N, K, r, gamma, iters, l, power_iters, omega, codes, q, c2, mean,
+                                        (uint16_t*)A, (uint16_t*)B, err, workspace, table(), (hipStream_t)stream),
+                      "nf4_loftq_init");
 }
 
 }  // extern "C"

@@ -108,4 +108,17 @@ struct AdamwScalars {
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* pbf, int64_t n,
                         const AdamwScalars& k, hipStream_t s);
 
+// ---- rank-r truncated SVD (randomized subspace iteration) and LoftQ initialisation ----
+constexpr int LR_MAX = 96;          // sketch width l at most (l >= r)
+constexpr int LR_MAX_SLICES = 16;   // contraction slices of a tall product at most
+size_t lowrank_ws_bytes(int64_t N, int64_t K, int l, int r);
+// E (N x K fp32) ~ U diag(S) V^T: U N x r, S r, V K x r (fp32), from the K x l Gaussian omega
+// and `power` subspace iterations
+hipError_t launch_lowrank_svd(const float* E, int64_t N, int64_t K, int r, int l, int power, const float* omega,
+                              float* U, float* S, float* V, void* ws, hipStream_t s);
+size_t loftq_ws_bytes(int64_t N, int64_t K, int l, int r);
+hipError_t launch_loftq(const float* W, int64_t N, int64_t K, int r, float gamma, int iters, int l, int power,
+                        const float* omega, uint8_t* codes, uint8_t* q, float* c2, float* mean, uint16_t* A,
+                        uint16_t* B, double* err, void* ws, const Nf4Table& tab, hipStream_t s);
+
 }  // namespace nf4

@@ -79,6 +79,8 @@ typedef struct nf4_weight {
 #define NF4_OP_LINEAR_FWD 2
 #define NF4_OP_LINEAR_BWD 3
 #define NF4_OP_CODEBOOK_STATS 4
+#define NF4_OP_LOWRANK_SVD 5     /* pass the sketch width l as M */
+#define NF4_OP_LOFTQ 6           /* pass the sketch width l as M */
 
 /* [BQ]+[NF]: blockwise absmax NF4 quantization (stub nf4_quantize(w, block=64)).
  * For each block of 64 consecutive values (the last may be partial):
@@ -278,6 +280,47 @@ void nf4_profile_next_fused(void* start_event, void* stop_event);
 
 /* Message for the last error returned on the calling thread ("" if none). */
 const char* nf4_last_error(void);
+
+/* Rank-r truncated SVD of an fp32 matrix, E ~ U diag(S) V^T, the step of the LoftQ
+ * initialisation below, exported for tests and reuse.  Randomized subspace iteration
+ * (Halko, Martinsson & Tropp, SIAM Review 2011): Y = orth(E Omega), `power_iters` rounds of
+ * Z = orth(E^T Y), Y = orth(E Z), then the eigen-decomposition of the l x l Gram matrix of
+ * E^T Y.  It approaches the exact truncated SVD as power_iters grows; the error of the
+ * approximation is what the test matrix and the gap between the r-th and (l+1)-th singular
+ * values allow.
+ *   E       fp32 N x K, row-major, 16-byte aligned (not modified); N, K < 2^22, N*K < 2^32
+ *   r, l    1 <= r <= l <= 96, l <= N, l <= K (l: sketch width, r plus oversampling)
+ *   power_iters  0 .. 16
+ *   omega   fp32 K x l test matrix (the caller draws it, e.g. i.i.d. N(0, 1))
+ *   U       out: fp32 N x r (orthonormal columns); S out: fp32 r, descending;
+ *   V       out: fp32 K x r (the right singular vectors as columns)
+ *   workspace  nf4_workspace_bytes(NF4_OP_LOWRANK_SVD, l, N, K, r) bytes, 256-byte aligned
+ * A column direction that E does not reach (rank below r) comes out as zero. */
+nf4_status nf4_lowrank_svd(const float* E, int64_t N, int64_t K, int32_t r, int32_t l, int32_t power_iters,
+                           const float* omega, float* U, float* S, float* V, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* [E2E] LoftQ-style initialisation of the adapter of a quantized base (closing remark of
+ * "Paged optimizers, and QLoRA end to end": start A and B so that dequant(W^NF4) + gamma B A
+ * is close to W, gamma = alpha / r).  The alternation of Li et al. (2023), from B A = 0,
+ * `iters` times: quantize the residual W - gamma B A with nf4_quantize and
+ * nf4_double_quantize; take the rank-r truncated SVD U S V^T of the quantization error
+ * E = W - dequant(Q) (nf4_lowrank_svd's method); B = U S^1/2 / sqrt(gamma),
+ * A = S^1/2 V^T / sqrt(gamma).
+ *   W       fp32 N x K (the full-precision weight), 16-byte aligned; N*K < 2^32
+ *   r, l, power_iters, omega   as for nf4_lowrank_svd (omega K x l)
+ *   alpha   > 0 (the layer's scale is alpha / r)
+ *   iters   1 .. 64
+ *   codes, q, c2, mean  out: the last quantization Q (the layer's frozen weight, as
+ *           nf4_quantize + nf4_double_quantize lay it out)
+ *   A       out: bf16 r x K;  B  out: bf16 N x r (round to nearest even of the fp32 factors)
+ *   err     out: device float64[iters], err[t] = ||W - dequant(Q_t) - gamma B_t A_t||_F with
+ *           the fp32 factors of alternation t (from ||E_t||_F^2 - sum S^2)
+ *   workspace  nf4_workspace_bytes(NF4_OP_LOFTQ, l, N, K, r) bytes, 256-byte aligned */
+nf4_status nf4_loftq_init(const float* W, int64_t N, int64_t K, int32_t r, float alpha, int32_t iters, int32_t l,
+                          int32_t power_iters, const float* omega, uint8_t* codes, uint8_t* q, float* c2,
+                          float* mean, void* A, void* B, double* err, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 #ifdef __cplusplus
 }

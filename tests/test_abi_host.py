@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
                             "nf4_workspace_bytes", "nf4_storage_bytes", "nf4_codebook",
                             "nf4_last_error", "nf4_profile_next_fused", "nf4_adamw_step",
                             "nf4_adamw_step_paged", "nf4_quantize_codebook", "nf4_codebook_stats",
-                            "qlora_linear_fwd_noalloc"])
+                            "qlora_linear_fwd_noalloc", "nf4_lowrank_svd", "nf4_loftq_init"])
     for name in names:
         assert hasattr(L, name), name
     # and the C symbols are unmangled (extern "C")
@@ -283,3 +283,25 @@ def test_binding_checks_tuple_sizes_before_the_device():
         nf4.nf4_codebook_stats(w, codes, torch.zeros(3), nf4.nf4_codebook())
     with pytest.raises(ValueError, match="c2 must hold 1"):
         nf4.nf4_double_dequantize(q, torch.zeros(0), mean)
+
+
+def test_lowrank_and_loftq_reject_bad_arguments():
+    L = nf4.load_library()
+    p = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(8192)
+    svd = L.nf4_lowrank_svd
+    big = 1 << 30
+    assert svd(None, 256, 192, 8, 24, 2, p, p, p, p, ws, big, None) == nf4.NF4_ERR_ARG
+    assert svd(p, 256, 192, 8, 4, 2, p, p, p, p, ws, big, None) == nf4.NF4_ERR_ARG          # l < r
+    assert svd(p, 256, 192, 8, 97, 2, p, p, p, p, ws, big, None) == nf4.NF4_ERR_UNSUPPORTED  # l > 96
+    assert svd(p, 16, 192, 8, 24, 2, p, p, p, p, ws, big, None) == nf4.NF4_ERR_ARG          # l > N
+    assert svd(p, 256, 192, 8, 24, 17, p, p, p, p, ws, big, None) == nf4.NF4_ERR_ARG        # power_iters
+    assert svd(p, 256, 192, 8, 24, 2, p, p, p, p, ws, 16, None) == nf4.NF4_ERR_WORKSPACE
+    assert svd(p, 1 << 22, 192, 8, 24, 2, p, p, p, p, ws, big, None) == nf4.NF4_ERR_UNSUPPORTED
+    lq = L.nf4_loftq_init
+    assert lq(p, 256, 192, 8, 16.0, 3, 24, 2, p, p, p, p, p, p, p, p, ws, 16, None) == nf4.NF4_ERR_WORKSPACE
+    assert lq(p, 256, 192, 8, 0.0, 3, 24, 2, p, p, p, p, p, p, p, p, ws, big, None) == nf4.NF4_ERR_ARG
+    assert lq(p, 256, 192, 8, 16.0, 0, 24, 2, p, p, p, p, p, p, p, p, ws, big, None) == nf4.NF4_ERR_ARG
+    assert lq(p, 256, 192, 8, 16.0, 3, 24, 2, p, p, p, p, p, None, p, p, ws, big, None) == nf4.NF4_ERR_ARG
+    assert L.nf4_workspace_bytes(nf4.NF4_OP_LOFTQ, 24, 256, 192, 8) > 256 * 192 * 4
+    assert L.nf4_workspace_bytes(nf4.NF4_OP_LOWRANK_SVD, 97, 256, 192, 8) == 0
