@@ -57,6 +57,8 @@ def _args():
                    help="per-shape kernel durations of a --gemv-sweep kernel trace, as a markdown table")
     p.add_argument("--codebooks-only", action="store_true",
                    help="the codebook comparison only (the 'codebooks' path figures), as a JSON line")
+    p.add_argument("--loftq-only", action="store_true",
+                   help="the LoftQ initialisation only (the 'loftq' path figures), as a JSON line")
     p.add_argument("--adamw-only", action="store_true",
                    help="the adapter optimizer step only (the 'adamw' path figures), as a JSON line "
                         "(for kernel traces and counter runs)")
@@ -570,6 +572,45 @@ def codebook_paths(dev, n=1 << 28, reps=5):
     return out
 
 
+def loftq_paths(dev, r=64, alpha=16.0, l=80, power=2, iters=5):
+    """LoftQ-style initialisation ("Paged optimizers, and QLoRA end to end", closing remark):
+    `iters` alternations of NF4 + double quantization of the residual and a rank-r randomized
+    SVD of the quantization error, on the LLaMA-65B q (8192 x 8192) and gate (22016 x 8192)
+    shapes (W ~ N(0, 0.02^2), seeded; sketch width l, `power` subspace iterations).  Reports
+    the time per alternation, the residual norm after the first and the last alternation
+    relative to plain NF4's ||W - dequant(Q)||_F, and the rate of the tall fp32 products
+    (2 N K l flops per pass, 2 + 2 power passes per alternation, over the whole alternation
+    time: a lower bound on the kernels' own rate)."""
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+    from workloads import Draw, seed_of
+
+    out = {"r": r, "alpha": alpha, "sketch_l": l, "power_iters": power, "alternations": iters}
+    for (name, N, K) in (("q65b", 8192, 8192), ("gate65b", 22016, 8192)):
+        W = Draw(seed_of(10, N, K), dev).normal((N, K), 0.02)
+        om = Draw(seed_of(11, K, l), dev).normal((K, l), 1.0)
+        nf4.loftq_init(W, r, alpha, om, iters=1, power_iters=power)
+        Wq0 = nf4.quantize_weight(W)
+        plain = float(torch.linalg.vector_norm(W - nf4.nf4_dequantize(Wq0, torch.float32)).item())
+        del Wq0
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        _, _, _, err = nf4.loftq_init(W, r, alpha, om, iters=iters, power_iters=power)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / iters
+        err = err.cpu().tolist()
+        tall_flops = (2 + 2 * power) * 2.0 * N * K * l
+        out[name] = dict(N=N, K=K, ms_per_alternation=ms, err_plain_nf4=plain,
+                         err_rel_first=err[0] / plain, err_rel_last=err[-1] / plain,
+                         tall_tflops_lower_bound=tall_flops / (ms / 1e3) / 1e12)
+        del W, om
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(layer, alpha, r, tokens):
     """The CPU oracle (float64, OpenMP) on `tokens` tokens through every projection."""
     import numpy as np
@@ -644,6 +685,9 @@ def main():
     if args.codebooks_only:
         print(json.dumps({"codebooks": codebook_paths(dev)}), flush=True)
         return
+    if args.loftq_only:
+        print(json.dumps({"loftq": loftq_paths(dev)}), flush=True)
+        return
     if args.adamw_only:
         from workloads import LLAMA65B, layer_projections
         shapes = [dict(N=N, K=K) for _, N, K in layer_projections(LLAMA65B["d"], LLAMA65B["ffn"])]
@@ -697,7 +741,8 @@ def main():
     if not args.no_paths and args.workload != "tiny":
         line["paths"] = {"codec": codec_paths(layer, dev), "gemv": gemv_paths(layer, dev, r, alpha),
                          "adamw": adamw_paths(layer, dev, r), "codebooks": codebook_paths(dev),
-                         "variants": variant_paths(layer, alpha, fwd_flops + bwd_flops)}
+                         "variants": variant_paths(layer, alpha, fwd_flops + bwd_flops),
+                         "loftq": loftq_paths(dev)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layer, alpha, r, min(args.cpu_tokens, M))
     print(json.dumps(line), flush=True)

@@ -111,14 +111,16 @@ const Nf4Table& table() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Limits of the linear products, checked before anything is enqueued.  The fused tiles
-// read 512 rows of an operand whose leading dimension is K (forward) or N (backward)
-// through one buffer descriptor, whose range the hardware caps at 2^31 - 1 bytes, so N
-// and K are at most nf4::FUSED_LD_LIMIT (2,101,255); the adapter products' and the
-// few-token forward's offsets are smaller.  A launch holds at most 2^24 workgroups of
-// 256 threads (2^32 work-items); the adapter products stack the token rows in 128-row
+// Limits of the linear products, checked before anything is enqueued.  Buffer descriptors
+// cap a range at 2^31 - 1 bytes and take 32-bit per-lane offsets: the adapter products
+// address up to 128 rows (direct operands) or 64 contraction rows (strided operands) of a
+// leading dimension N or K, 254 ld bytes at most, and the few-token forward 16 token rows
+// of K or 128 adapter rows; with N, K below 2^22 every offset stays below 2^31.  (The fused
+// products read their token operand through 64 KB fragment-order blocks and the packed
+// weight within N * K / 2 < 2^31 bytes.)  A launch holds at most 2^24 workgroups of 256
+// threads (2^32 work-items); the adapter products stack the token rows in 128-row
 // workgroups along the grid's second dimension.
-constexpr int64_t LINEAR_DIM_LIMIT = nf4::FUSED_LD_LIMIT;
+constexpr int64_t LINEAR_DIM_LIMIT = (int64_t)1 << 22;
 constexpr int64_t LINEAR_M_LIMIT = (int64_t)1 << 23;
 constexpr int64_t FUSED_GRID_LIMIT = (int64_t)1 << 24;
 
@@ -142,10 +144,8 @@ nf4_status check_weight(const nf4_weight* W, WeightView& v, bool linear) {
         if (W->rows == 0 || W->cols == 0) return fail(NF4_ERR_ARG, "empty weight");
         // the fused kernels address the packed weight through 32-bit buffer offsets
         if (n / 2 >= ((int64_t)1 << 31)) return fail(NF4_ERR_UNSUPPORTED, "weight larger than 2^32 values");
-        if (W->rows > LINEAR_DIM_LIMIT || W->cols > LINEAR_DIM_LIMIT)
-            return fail(NF4_ERR_UNSUPPORTED,
-                        "N (rows) and K (cols) must be at most 2101255 (512 operand rows within a "
-                        "2^31-byte buffer range)");
+        if (W->rows >= LINEAR_DIM_LIMIT || W->cols >= LINEAR_DIM_LIMIT)
+            return fail(NF4_ERR_UNSUPPORTED, "N (rows) and K (cols) must be below 2^22");
     }
     if (!aligned(W->codes, 16)) return fail(NF4_ERR_ARG, "codes must be 16-byte aligned");
     if (!plain && (!aligned(W->c2, 4) || !aligned(W->mean, 4))) return fail(NF4_ERR_ARG, "misaligned c2/mean");
@@ -180,9 +180,18 @@ size_t c1_buffer_bytes(int32_t op, int64_t M, int64_t N, int64_t K) {
     return fused ? align256((size_t)(N * (K / 64)) * 4) : 0;
 }
 
+// The fused products' A operand (X forward, dY backward) in fragment order: one 64 KB block
+// per (512-token tile, 64-value contraction step).
+size_t pack_bytes(int32_t op, int64_t M, int64_t N, int64_t K) {
+    const bool fused = op == NF4_OP_LINEAR_FWD ? M > GEMV_MAX_M : M > 0;
+    if (!fused) return 0;
+    const int64_t ld = op == NF4_OP_LINEAR_FWD ? K : N;
+    return (size_t)((M + nf4::FUSED_TM - 1) / nf4::FUSED_TM) * (size_t)((ld + 63) / 64) * nf4::A_BLOCK_BYTES;
+}
+
 // Workspace layouts (256-byte aligned pieces):
-//   forward : [s*T bf16 M x r][T bf16 M x r, when T_out is NULL][c1' fp32][fp32 partials]
-//   backward: [s*U bf16 M x r][T bf16 M x r, when T is NULL][c1' fp32][fp32 partials]
+//   forward : [s*T bf16 M x r][T bf16 M x r, when T_out is NULL][c1' fp32][fp32 partials][packed X]
+//   backward: [s*U bf16 M x r][T bf16 M x r, when T is NULL][c1' fp32][fp32 partials][packed dY]
 // The partials region serves, one after the other in stream order, the split-contraction
 // slices of the rank-r products and the fp32 partial tiles of the fused product's split
 // tail tiles.
@@ -260,9 +269,11 @@ size_t nf4_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t 
         case NF4_OP_DOUBLE_QUANTIZE: return nf4::double_quantize_ws_bytes(N);
         case NF4_OP_CODEBOOK_STATS: return N > 0 ? nf4::codebook_stats_ws_bytes(N) : 0;
         case NF4_OP_LINEAR_FWD:
-            return 2 * rank_buffer_bytes(M, r) + c1_buffer_bytes(op, M, N, K) + fwd_partial_bytes(M, N, K, r);
+            return 2 * rank_buffer_bytes(M, r) + c1_buffer_bytes(op, M, N, K) + fwd_partial_bytes(M, N, K, r) +
+                   pack_bytes(op, M, N, K);
         case NF4_OP_LINEAR_BWD:
-            return 2 * rank_buffer_bytes(M, r) + c1_buffer_bytes(op, M, N, K) + bwd_partial_bytes(M, N, K, r);
+            return 2 * rank_buffer_bytes(M, r) + c1_buffer_bytes(op, M, N, K) + bwd_partial_bytes(M, N, K, r) +
+                   pack_bytes(op, M, N, K);
         case NF4_OP_LOWRANK_SVD:   // M carries the sketch width l
             return (N > 0 && K > 0 && M > 0 && M <= nf4::LR_MAX && r > 0) ? nf4::lowrank_ws_bytes(N, K, (int)M, r) : 0;
         case NF4_OP_LOFTQ:
@@ -391,7 +402,8 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
         return fail(NF4_ERR_ARG, "X, Y and T_out must be 16-byte aligned");
     const size_t rb = rank_buffer_bytes(M, r);
     const size_t cb = c1_buffer_bytes(NF4_OP_LINEAR_FWD, M, v.rows, v.cols);
-    const size_t need = 2 * rb + cb + fwd_partial_bytes(M, v.rows, v.cols, r);
+    const size_t pb = fwd_partial_bytes(M, v.rows, v.cols, r);
+    const size_t need = 2 * rb + cb + pb + pack_bytes(NF4_OP_LINEAR_FWD, M, v.rows, v.cols);
     if (!workspace || workspace_bytes < need)
         return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LINEAR_FWD)");
     if (!aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
@@ -399,6 +411,7 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     uint16_t* Tb = T_out ? (uint16_t*)T_out : (uint16_t*)((char*)workspace + rb);
     float* c1 = (float*)((char*)workspace + 2 * rb);
     float* part = (float*)((char*)workspace + 2 * rb + cb);
+    uint16_t* xpk = (uint16_t*)((char*)workspace + 2 * rb + cb + pb);
     const float s = alpha / (float)r;
     hipStream_t hs = (hipStream_t)stream;
     const uint16_t* x = (const uint16_t*)X;
@@ -418,7 +431,9 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
         e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
         if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (constants)");
     }
-    e = nf4::launch_fused_fwd(v, c1, x, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, part, table(), hs);
+    e = nf4::launch_pack_a(x, M, v.cols, xpk, hs);
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (pack)");
+    e = nf4::launch_fused_fwd(v, c1, xpk, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, part, table(), hs);
     return hip_status(e, "qlora_linear_fwd (gemm)");
 }
 
@@ -462,7 +477,8 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
         return fail(NF4_ERR_ARG, "X, dY, T and dX must be 16-byte aligned");
     const size_t rb = rank_buffer_bytes(M, r);
     const size_t cb = c1_buffer_bytes(NF4_OP_LINEAR_BWD, M, v.rows, v.cols);
-    const size_t need = 2 * rb + cb + bwd_partial_bytes(M, v.rows, v.cols, r);
+    const size_t pb = bwd_partial_bytes(M, v.rows, v.cols, r);
+    const size_t need = 2 * rb + cb + pb + pack_bytes(NF4_OP_LINEAR_BWD, M, v.rows, v.cols);
     if (!workspace || workspace_bytes < need)
         return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_workspace_bytes(NF4_OP_LINEAR_BWD)");
     if (!aligned(workspace, 256)) return fail(NF4_ERR_ARG, "workspace must be 256-byte aligned");
@@ -476,6 +492,7 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     const uint16_t* Tb = (const uint16_t*)T;
     float* c1 = (float*)((char*)workspace + 2 * rb);
     float* part = (float*)((char*)workspace + 2 * rb + cb);
+    uint16_t* gpk = (uint16_t*)((char*)workspace + 2 * rb + cb + pb);
     hipError_t e;
     if (M > 0) {
         // Us = s dY B   (B stored N x r: contraction-strided)
@@ -496,7 +513,9 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
                 if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (constants)");
                 c1b = c1;
             }
-            e = nf4::launch_fused_bwd_dx(v, c1b, g, M, Us, al, r, (uint16_t*)dX, part, table(), hs);
+            e = nf4::launch_pack_a(g, M, v.rows, gpk, hs);
+            if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (pack)");
+            e = nf4::launch_fused_bwd_dx(v, c1b, gpk, M, Us, al, r, (uint16_t*)dX, part, table(), hs);
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dX)");
         }
     }

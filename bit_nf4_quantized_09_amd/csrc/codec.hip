@@ -177,23 +177,31 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, uint8_t* codes
 // ---------------------------------------------------------------------------
 constexpr int SUM_CHUNK = 2048;
 
+// Sum over the aligned pairwise tree of x[c0 .. c0 + 2048) (zeros past n), by the 256
+// threads of a workgroup; the result is in every thread.
+template <typename T>
+__device__ __forceinline__ double chunk_tree_sum(const T* __restrict__ x, int64_t n, int64_t c0) {
+    __shared__ double sw[4];
+    const int64_t i0 = c0 + threadIdx.x * 8;
+    double v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (i0 + e < n) ? (double)x[i0 + e] : 0.0;
+    double s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();                    // sw may still be read from a previous call
+    if (lane == 0) sw[wave] = s;
+    __syncthreads();
+    return (sw[0] + sw[1]) + (sw[2] + sw[3]);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_pairwise_chunks(const T* __restrict__ x, int64_t n,
                                                          double* __restrict__ out, int64_t mean_n1,
                                                          float* __restrict__ mean) {
-    const int64_t c0 = (int64_t)blockIdx.x * SUM_CHUNK + threadIdx.x * 8;
-    double v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (c0 + e < n) ? (double)x[c0 + e] : 0.0;
-    double s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
-    __shared__ double sw[4];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) sw[wave] = s;
-    __syncthreads();
+    const double r = chunk_tree_sum(x, n, (int64_t)blockIdx.x * SUM_CHUNK);
     if (threadIdx.x == 0) {
-        const double r = (sw[0] + sw[1]) + (sw[2] + sw[3]);
         if (mean_n1 >= 0) *mean = (mean_n1 > 0) ? (float)(r / (double)mean_n1) : 0.0f;
         else out[blockIdx.x] = r;
     }
@@ -204,6 +212,7 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t double_quantize_ws_bytes(int64_t n1) {
     size_t total = 0;
     int64_t len = ceil_div(n1, SUM_CHUNK);
+    if (len == 1) return sizeof(double);   // the single chunk sum
     while (len > 1) {
         total += (size_t)len;
         len = ceil_div(len, SUM_CHUNK);
@@ -249,10 +258,70 @@ __global__ __launch_bounds__(64) void k_dq_encode(const float* __restrict__ c1, 
     }
 }
 
+// Double-quantize encode with the mean formed in place: every workgroup sums the nchunk <=
+// 2048 chunk sums of k_pairwise_chunks over the same aligned tree (the exact float64 sum;
+// workgroup 0 stores the mean), then encodes DQ_BLOCKS_PER_WG blocks of 256 constants, one
+// wave per block, 4 constants per lane.  Two launches per tensor instead of a chain.
+constexpr int DQ_BLOCKS_PER_WG = 16;
+__global__ __launch_bounds__(256) void k_dq_encode_mean(const float* __restrict__ c1, int64_t n1,
+                                                        const double* __restrict__ chunk_sums, int64_t nchunk,
+                                                        float* __restrict__ mean_out, uint8_t* __restrict__ q,
+                                                        float* __restrict__ c2) {
+    const double S = chunk_tree_sum(chunk_sums, nchunk, 0);
+    const float mean = n1 > 0 ? (float)(S / (double)n1) : 0.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *mean_out = mean;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nblk = (n1 + 255) / 256;
+    for (int j = wave; j < DQ_BLOCKS_PER_WG; j += 4) {
+        const int64_t b = (int64_t)blockIdx.x * DQ_BLOCKS_PER_WG + j;
+        if (b >= nblk) break;
+        const int64_t base = b * 256 + lane * 4;
+        const bool full = (b * 256 + 256 <= n1);
+        float d[4];
+        if (full) {
+            const float4 c = *reinterpret_cast<const float4*>(c1 + base);
+            d[0] = c.x - mean; d[1] = c.y - mean; d[2] = c.z - mean; d[3] = c.w - mean;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = (base + e < n1) ? c1[base + e] - mean : 0.0f;
+        }
+        float m = fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3])));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if (lane == 0) c2[b] = m;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t code = (m == 0.0f) ? 0u : e4m3_from_unit(__fdiv_rn(d[e], m));
+            packed |= code << (8 * e);
+        }
+        if (full) {
+            *reinterpret_cast<uint32_t*>(q + base) = packed;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (base + e < n1) q[base + e] = (uint8_t)(packed >> (8 * e));
+        }
+    }
+}
+
 hipError_t launch_double_quantize(const float* c1, int64_t n1, uint8_t* q, float* c2, float* mean,
                                   double* ws, hipStream_t s) {
-    // mean: repeated chunk reductions until one chunk is left; that last pass writes the mean
     int64_t len = ceil_div(n1, SUM_CHUNK);
+    if (n1 > 0 && len <= SUM_CHUNK) {
+        // up to 2048^2 constants (2^28 weights): chunk sums, then the encode sums them itself
+        // (a single chunk's sum is the whole tree's; the encode re-sums that one value)
+        hipLaunchKernelGGL(k_pairwise_chunks<float>, dim3((unsigned)len), dim3(256), 0, s, c1, n1, ws,
+                           (int64_t)-1, (float*)nullptr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t nblk = ceil_div(n1, 256);
+        hipLaunchKernelGGL(k_dq_encode_mean, dim3((unsigned)ceil_div(nblk, DQ_BLOCKS_PER_WG)), dim3(256), 0, s, c1, n1,
+                           ws, len, mean, q, c2);
+        return hipGetLastError();
+    }
+    // larger tensors (and n1 = 0): repeated chunk reductions until one chunk is left; that
+    // last pass writes the mean; then the encode
     if (len <= 1) {
         hipLaunchKernelGGL(k_pairwise_chunks<float>, dim3(1), dim3(256), 0, s, c1, n1,
                            (double*)nullptr, n1, mean);

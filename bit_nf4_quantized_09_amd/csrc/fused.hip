@@ -10,60 +10,45 @@
 // Forward  Y  = X W'^T + s T B^T   (NT product, contraction over K)
 // Backward dX = dY W' + s U A      (NN product, contraction over N)
 //
-// Design for CDNA4: a TM x TN output tile per workgroup of 4 waves (each wave
-// 128 x 128 = 4 x 4 tiles of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per
-// lane), one NF4 block (64 values) of contraction per pipeline step, two LDS
-// stages.  The packed codes of one (row, 64-block) are owned by a pair of lanes (TN =
-// 128), which build the block's 16-entry bf16 table scaled by its decoded constant
-// together (each computes half and takes the other half from its partner); each lane
-// then expands its share of the codes with byte permutes before writing them to LDS;
-// every dequantized value is therefore computed once per workgroup and reused by TM
-// rows of the other operand.  The decode work per MFMA falls as TM grows: the
-// 512 x 128 tile (2 x 80 KB stages, the whole 160 KB LDS) decodes half as much per
-// MFMA as a 256 x 256 tile.
+// Design for CDNA4: a 512 x 128 output tile (tokens x features) per workgroup of 4 waves.
+// Wave w owns token rows 128 w .. 128 w + 127 of the tile and all 128 features: 4 x 4 tiles
+// of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane.  One NF4 block (64 values)
+// of contraction per pipeline step.
+//
+// The A operand (X forward, dY backward) is private to a wave, so it goes from global
+// memory straight into MFMA operand registers and never through LDS.  A pre-pass
+// (k_pack_a) lays the operand out in fragment order: for each 512-row token tile and
+// 64-value contraction step, 64 KB holding, per wave and MFMA fragment (row tile i,
+// substep s), the 16 bytes of each of the 64 lanes (row 128 w + 32 i + l % 32, contraction
+// values 16 s + 8 (l / 32) .. + 7) contiguously, so that every fragment load is one
+// coalesced kilobyte, with zeros past the last token row and past the contraction's end.
+// (Loaded from the row-major operand, each lane of a fragment load would touch its own
+// row: four times the cache lines per load instruction.)  Two register sets of A fragments
+// (steps of even and odd index) are reloaded two steps ahead, each fragment as soon as its
+// last MFMA of the step has issued.
+//
+// The W' tile is shared by the 4 waves and goes through LDS, decoded once per workgroup: the
+// packed codes of one (row, 64-block) are owned by a pair of lanes, which build the block's
+// 16-entry bf16 table scaled by its decoded constant together (each computes half and takes
+// the other half from its partner); each lane then expands its 32 codes with byte permutes
+// and writes them to one of two 16 KB LDS stages.  Every dequantized value is used by the
+// tile's 512 token rows.
 #include "bufio.h"
 #include "launch.h"
 
 namespace nf4 {
 
-// Tile geometry of k_fused<BWD, TM, TN>.
-template <int TM, int TN>
-struct FusedTile {
-    static_assert(TM * TN == TILE_FLOATS && TM % 128 == 0 && TN % 128 == 0, "tile");
-    static constexpr int WN = TN / 128;                  // waves across the tile (4 waves)
-    static constexpr int A_BYTES = TM * 128;             // A tile: TM tokens x 64 bf16
-    static constexpr int W_BYTES = TN * 128;             // W' tile: TN x 64 (fwd) or 64 x TN (bwd)
-    static constexpr int STAGE = A_BYTES + W_BYTES;
-    static constexpr int LDS = 2 * STAGE;
-    static constexpr int ACH = TM / 32;                  // A tile 16-byte chunks per lane per step
-    static constexpr int LPP = 256 / TN;                 // lanes per (row, 64-block) of W'
-    static constexpr int CPL = 64 / LPP;                 // codes per lane per step
-    static constexpr int NCH = CPL / 8;                  // 8-code chunks per lane per step
-    static constexpr int NW = CPL / 32;                  // 16-byte code words per lane
-    // A-tile register sets: two (8 chunks: loaded in step it for step it+2, written at the
-    // end of step it+1), or one (16 chunks: chunks 2r, 2r+1 written in region r of step
-    // it+1, reloaded for step it+2 two regions later)
-    static constexpr int DEPTH = ACH <= 8 ? 2 : 1;
-};
+// W' tiles: [128 rows][64 bf16] forward (128-byte rows, XOR-swizzled 16-byte chunks) or
+// [64 rows][128 bf16] backward (256-byte rows, read transposed); two stages.
+constexpr int W_STAGE_BYTES = 16384;
+constexpr int FUSED_LDS_BYTES = 2 * W_STAGE_BYTES;
 
 // [rows][64 bf16] tile with 128-byte rows: 16-byte chunk c of row r sits at chunk
 // position c ^ g(r), g(r) = (r ^ (r >> 3)) & 7.  Any 16 consecutive rows reading the
-// same chunk (one b128 pass of 16 lanes) then cover all 64 banks exactly once, and so
-// do 8 consecutive rows (32-bank view).
+// same chunk (one b128 pass of 16 lanes) then cover all 64 banks exactly once.
 __device__ __forceinline__ int tile_off(int row, int chunk) {
     return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
 }
-
-// Stage layout of the 160 KB of LDS (512 x 128 tiles): the A tiles [512 rows][128 B] of the
-// two stages are interleaved by halves (rows 0-255 of stages 0 and 1 at 0 and 32 KB, rows
-// 256-511 at 64 and 96 KB), then the W' tiles of stages 0 and 1 (16 KB each) at 128 and
-// 144 KB.  Every stage offset (32 KB, 16 KB) then fits the 16-bit immediate of a DS
-// instruction, so with the stage known at compile time each address is a loop-invariant
-// per-lane base plus an immediate.
-constexpr int A_STAGE_OFF = 32768;
-constexpr int W_REGION = 131072;
-constexpr int W_STAGE_OFF = 16384;
-__device__ __forceinline__ int a_off(int row, int chunk) { return tile_off(row, chunk) + ((row >> 8) << 15); }
 
 // Backward W' tile [64 n][TN k] with 2 TN-byte rows, read by ds_read_b64_tr_b16:
 // 32-byte segment u (16 k values) of row r sits at u ^ 2(r & 3), so the 4 rows x 2
@@ -90,7 +75,7 @@ struct FusedArgs {
     const uint8_t* codes;
     const float* c1;          // decoded first-level constant of every 64-block (N * K/64)
     int64_t N, K;             // frozen weight rows (out features) and columns (in features)
-    const uint16_t* A;        // X [M x K] (forward) or dY [M x N] (backward)
+    const uint16_t* A;        // X [M x K] (forward) or dY [M x N] (backward), packed by k_pack_a
     int64_t M;
     const uint16_t* Rk;       // forward: s*T [M x r]; backward: s*U [M x r]
     const uint16_t* Lr;       // forward: B [N x r];   backward: A [r x K]
@@ -102,128 +87,111 @@ struct FusedArgs {
     float* spart;             // fp32 partial tiles, 65536 floats per (tail tile, piece)
 };
 
-// One lane's 16-byte chunks of an A tile (indexed with constants only, so that they
-// stay in registers).
-template <int N>
-struct XRegs {
-    uint4 r[N];
+// One step's A fragments of a lane: [row tile i][substep s], 8 bf16 each (indexed with
+// constants only, so that they stay in registers).
+struct AFrags {
+    uint4 f[4][4];
 };
 
 // This lane's packed codes of one (row, 64-block) and its decoded constant (zero past
 // the last row).
-template <int NW>
 struct BlockCodes {
-    uint4 w[NW];
+    uint4 w;
     float c1;
 };
 
-template <bool BWD, int TM, int TN>
+template <bool BWD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fused(FusedArgs a, Nf4Table tab) {
-    using G = FusedTile<TM, TN>;
-    static_assert(G::A_BYTES == 2 * A_STAGE_OFF && G::W_BYTES == W_STAGE_OFF && G::LDS == W_REGION + 2 * W_STAGE_OFF,
-                  "stage layout");
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int TM = FUSED_TM, TN = FUSED_TN;
+    static_assert(TM == 512 && TN == 128 && TM * TN == TILE_FLOATS, "tile");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[FUSED_LDS_BYTES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int h = lane >> 5, rl = lane & 31;
     // forward tiles (tokens, out features); backward tiles (tokens, in features)
     Unit u;
     if (!unit_of(blockIdx.x, (a.M + TM - 1) / TM, ((BWD ? a.K : a.N) + TN - 1) / TN, a.S, u)) return;
     const int64_t c0 = u.tn * TN, m0 = u.tm * TM;
     const int64_t KB = a.K >> 6;
-    const int64_t ldA = BWD ? a.N : a.K;                 // row length of the A operand
     const int64_t all_steps = BWD ? (a.N + 63) >> 6 : KB;   // 64-deep contraction steps
-    int64_t sb, steps;                                    // this unit's steps sb .. sb + steps - 1
-    unit_steps(all_steps, a.chunk, u.split, sb, steps);
+    int64_t sb64, steps64;                                // this unit's steps sb .. sb + steps - 1
+    unit_steps(all_steps, a.chunk, u.split, sb64, steps64);
+    // 32-bit and wave-uniform (said so), so that the step arithmetic, the buffer offsets and
+    // the descriptors stay in scalar registers (steps < 2^16: N, K < 2^22)
+    const int sb = __builtin_amdgcn_readfirstlane((int)sb64);
+    const int steps = __builtin_amdgcn_readfirstlane((int)steps64);
 
-    // ---- this lane's share of the packed weight: CPL codes of one (row, 64-block) per step ----
-    // pair = tid / LPP, part = tid % LPP (codes part*CPL .. of the block).
-    // forward: row c0 + pair, block = step; backward: row 64*step + pair / (TN/64), block
-    // c0/64 + pair % (TN/64).  Rows past N fall outside the buffers' range and read zero
+    // ---- this lane's share of the packed weight: 32 codes of one (row, 64-block) per step ----
+    // pair = tid / 2, part = tid % 2 (codes 32 part .. of the block).
+    // forward: row c0 + pair, block = step; backward: row 64*step + pair / 2, block
+    // c0/64 + pair % 2.  Rows past N fall outside the buffers' range and read zero
     // codes and a zero constant, so their dequantized values are zero.  The forward
     // advances by a wave-uniform offset inside the row; the backward moves the
     // descriptors down by 64 rows per step.
-    const int pair = tid / G::LPP, part = tid % G::LPP;
-    const int nl = BWD ? pair / (TN / 64) : pair;         // row of the W' tile (bwd: of 64)
-    const int jb = BWD ? pair % (TN / 64) : 0;            // block of the tile (bwd)
+    const int pair = tid >> 1, part = tid & 1;
+    const int nl = BWD ? pair >> 1 : pair;                // row of the W' tile (bwd: of 64)
+    const int jb = BWD ? pair & 1 : 0;                    // block of the tile (bwd)
     const int64_t kblk_b = (c0 >> 6) + jb < KB ? (c0 >> 6) + jb : KB - 1;
     const int64_t my_row0 = BWD ? nl : c0 + pair;         // row at step 0
-    const uint32_t code_voff = (uint32_t)(my_row0 * (a.K >> 1) + (BWD ? kblk_b * 32 : 0) + part * (G::CPL / 2));
+    const uint32_t code_voff = (uint32_t)(my_row0 * (a.K >> 1) + (BWD ? kblk_b * 32 : 0) + part * 16);
     const uint32_t c1_voff = (uint32_t)((my_row0 * KB + (BWD ? kblk_b : 0)) * 4);
-    // The constant is requested first: it is needed first (scaled table), then the
-    // codes, then the A tile (LDS write at the end of the step).
-    auto load_codes = [&](int64_t lstep) {
-        const int64_t step = sb + lstep;
-        BlockCodes<G::NW> bc;
+    // The constant is requested first: it is needed first (scaled table), then the codes.
+    auto load_codes = [&](int lstep) {
+        const int step = sb + lstep;
+        BlockCodes bc;
         if constexpr (BWD) {
-            const int64_t r0 = step * 64;                  // first weight row of the step
+            const int64_t r0 = (int64_t)step * 64;         // first weight row of the step
             const __amdgpu_buffer_rsrc_t rs_c1 = make_rsrc(a.c1 + r0 * KB, (a.N - r0) * KB * 4);
             const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes + r0 * (a.K >> 1), (a.N - r0) * (a.K >> 1));
             bc.c1 = buf_loadf(rs_c1, c1_voff, 0);
-#pragma unroll
-            for (int i = 0; i < G::NW; ++i) bc.w[i] = buf_load16(rs_codes, code_voff + 16 * i, 0);
+            bc.w = buf_load16(rs_codes, code_voff, 0);
         } else {
             const __amdgpu_buffer_rsrc_t rs_c1 = make_rsrc(a.c1, a.N * KB * 4);
             const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(a.codes, a.N * (a.K >> 1));
             bc.c1 = buf_loadf(rs_c1, c1_voff, (uint32_t)(step * 4));
-#pragma unroll
-            for (int i = 0; i < G::NW; ++i) bc.w[i] = buf_load16(rs_codes, code_voff + 16 * i, (uint32_t)(step * 32));
+            bc.w = buf_load16(rs_codes, code_voff, (uint32_t)(step * 32));
         }
         return bc;
     };
-    // LDS position of this lane's decoded chunk c (8 codes)
+    // LDS position (in a stage) of this lane's decoded chunk c (8 codes)
     auto w_off = [&](int c) {
-        if constexpr (BWD) return wt_off<TN>(nl, jb * 64 + part * G::CPL + c * 8);
-        else return tile_off(pair, part * G::NCH + c);
+        if constexpr (BWD) return wt_off<TN>(nl, jb * 64 + part * 32 + c * 8);
+        else return tile_off(pair, part * 4 + c);
     };
-    auto word = [&](const BlockCodes<G::NW>& bc, int c) {
-        const uint4 v = bc.w[c >> 2];
-        return (c & 3) == 0 ? v.x : (c & 3) == 1 ? v.y : (c & 3) == 2 ? v.z : v.w;
+    auto word = [&](const BlockCodes& bc, int c) {
+        return c == 0 ? bc.w.x : c == 1 ? bc.w.y : c == 2 ? bc.w.z : bc.w.w;
     };
     // the two lanes of a (row, 64-block) pair (tid 2i, 2i+1) build its scaled table together:
     // lane `part` computes entries 8 part .. 8 part + 7, and its codes are flipped to match
-    static_assert(G::LPP == 2, "pair lanes");
     float lvh[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) lvh[i] = part ? tab.lv[8 + i] : tab.lv[i];
     const uint32_t flip = pair_code_flip(part);
-    auto half_table = [&](float c) { return make_pair_table(lvh, c); };
-    auto dequant_store = [&](uint8_t* sW, const BlockCodes<G::NW>& bc) {
-        const ScaledTable st = half_table(bc.c1);
-#pragma unroll
-        for (int c = 0; c < G::NCH; ++c) {
-            uint32_t o[4];
-            decode8(st, word(bc, c) ^ flip, o);
-            *reinterpret_cast<uint4*>(sW + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
+    auto decode_chunk = [&](uint8_t* sW, const ScaledTable& st, const BlockCodes& bc, int c) {
+        uint32_t o[4];
+        decode8(st, word(bc, c) ^ flip, o);
+        *reinterpret_cast<uint4*>(sW + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
     };
 
-    // ---- A operand tile: TM tokens x 64 contraction values, ACH chunks per lane ----
-    // chunk i of this lane: tile row (tid >> 3) + 32 i, contraction chunk (tid & 7).  The
-    // descriptor of a step starts at the step's first contraction value of the tile's
-    // first row and ends with the tile's last row, so rows past M, and columns of the
-    // last row past its end, read zero.  Backward columns past N of the other rows read
-    // finite data of the next row and meet zeroed W' rows.
-    // (the ABI bounds ldA so that every offset, a_chunk_offset(tid, i, ldA) + 16 bytes,
-    // stays inside the descriptor's 2^31 - 1 byte range)
-    static_assert(TM == FUSED_TM && G::ACH == A_CHUNKS, "A-tile offsets of tile_map.h");
-    const int achunk = tid & 7;
-    const int64_t arows = a.M - m0 < TM ? a.M - m0 : TM;
-    const uint32_t a_voff0 = (uint32_t)a_chunk_offset(tid, 0, ldA);
-    const uint32_t a_rstride = (uint32_t)(a_chunk_offset(tid, 1, ldA) - a_chunk_offset(tid, 0, ldA));
-    auto a_rsrc = [&](int64_t lstep) {
-        const int64_t step = sb + lstep;
-        return make_rsrc(a.A + m0 * ldA + step * 64, arows * ldA * 2 - step * 128);
-    };
-    auto load_a = [&](XRegs<G::ACH>& X, int64_t lstep) {
-        const __amdgpu_buffer_rsrc_t rs_a = a_rsrc(lstep);
+    // ---- A operand: 16 fragments per lane and step, from the packed operand ----
+    // The step's 64 KB block of this token tile: wave w's fragment (i, s) is the kilobyte at
+    // 16 KB w + 1 KB (4 i + s), lane l's 16 bytes at 16 l of it.
+    uint32_t a_voff[4];
 #pragma unroll
-        for (int i = 0; i < G::ACH; ++i) X.r[i] = buf_load16(rs_a, a_voff0 + i * a_rstride, 0);
+    for (int i = 0; i < 4; ++i) a_voff[i] = (uint32_t)(wave * 16384 + 4096 * i + lane * 16);
+    const uint16_t* a_tile = a.A + u.tm * all_steps * (int64_t)(A_BLOCK_BYTES / 2);
+    auto a_rsrc = [&](int lstep) {
+        return make_rsrc(a_tile + (int64_t)(sb + lstep) * (A_BLOCK_BYTES / 2), A_BLOCK_BYTES);
     };
-    auto store_a = [&](const XRegs<G::ACH>& X, uint8_t* sA) {
+    auto load_frag = [&](__amdgpu_buffer_rsrc_t rs, int i, int s) {
+        return buf_load16(rs, a_voff[i] + 1024 * s, 0);
+    };
+    auto load_all = [&](AFrags& F, int lstep) {
+        const __amdgpu_buffer_rsrc_t rs = a_rsrc(lstep);
 #pragma unroll
-        for (int i = 0; i < G::ACH; ++i)
-            *reinterpret_cast<uint4*>(sA + a_off((tid >> 3) + 32 * i, achunk)) = X.r[i];
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) F.f[i][s] = load_frag(rs, i, s);
     };
 
     f32x16 acc[4][4];
@@ -232,219 +200,131 @@ void k_fused(FusedArgs a, Nf4Table tab) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    // B fragment of MFMA column tile j, substep sub (16 contraction values).  Backward: the
-    // swizzle of wt_off depends on row & 3 only, so rows 16 sub + r and r + 4 sit at fixed
-    // distances from row r: one per-lane base per column tile, the rest immediates.
-    // (the bases hold the W' region's offset, which exceeds an immediate; the stage, substep
-    // and second-read offsets do not)
+    // W' fragment of MFMA column tile j, substep s, from stage `st` (contraction values
+    // 16 s + 8 h .. + 7 of the step).  Forward: row 32 j + rl, chunk 2 s + h.  Backward: the
+    // swizzle of wt_off depends on row & 3 only, so rows 16 s + 8 h + r and r + 4 sit at fixed
+    // distances from row 8 h + r: one per-lane base per column tile, the rest immediates.
     int bt_abs[4] = {0, 0, 0, 0};
     if constexpr (BWD) {
         const int g = lane >> 4, jl = lane & 15;
         const int row0 = 8 * (g >> 1) + (jl >> 2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bt_abs[j] = W_REGION + wt_off<TN>(row0, wn * 128 + j * 32 + 16 * (g & 1) + 4 * (jl & 3));
+        for (int j = 0; j < 4; ++j) bt_abs[j] = wt_off<TN>(row0, j * 32 + 16 * (g & 1) + 4 * (jl & 3));
     }
-    auto read_b = [&](const uint8_t* sB, int j, int sub) -> bf16x8 {
+    auto read_b = [&](int st, int j, int s) -> bf16x8 {
         if constexpr (BWD) {
-            const int soff = (int)(sB - (lds + W_REGION));      // the stage's offset (0 or 16 KB)
-            const uint8_t* p = lds + bt_abs[j] + (soff + sub * 16 * (2 * TN));
+            const uint8_t* p = lds + st * W_STAGE_BYTES + bt_abs[j] + s * 16 * (2 * TN);
             const uint2 lo = ds_read_tr16(p);
             const uint2 hi = ds_read_tr16(p + 4 * (2 * TN));
             return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         } else {
-            const int rb = wn * 128 + j * 32 + (lane & 31);
-            return *reinterpret_cast<const bf16x8*>(sB + tile_off(rb, 2 * sub + (lane >> 5)));
+            return *reinterpret_cast<const bf16x8*>(lds + st * W_STAGE_BYTES + tile_off(j * 32 + rl, 2 * s + h));
         }
     };
-    auto mfma_step = [&](const uint8_t* sA, const uint8_t* sB, int nsub) {
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            if (sub < nsub) {
-                const int ch = 2 * sub + (lane >> 5);
-                bf16x8 fa[4], fb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    fa[i] = *reinterpret_cast<const bf16x8*>(sA + a_off(wm * 128 + i * 32 + (lane & 31), ch));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) fb[j] = read_b(sB, j, sub);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-            }
-        }
+    auto mfma = [&](int i, int j, uint4 af, bf16x8 bf) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af), bf, acc[i][j], 0, 0, 0);
     };
 
     // ---- main loop: the MFMAs of step `it` overlap the dequantization of step it+1 ----
-    // The body is laid out by hand as 8 regions fenced by sched_barrier: region r
-    // issues MFMAs 8r..8r+7 of this step (substep r/2), one slice of the
-    // dequantization of the next step (region 0: block constant and scaled table;
-    // region r > 0: chunk r-1 of this lane's codes and its LDS write), half of the
-    // fragment reads of the following substep and a share of the A tile traffic.  Inside
-    // a region, each MFMA is followed by a few VALU instructions, so the VALU work
-    // executes while the matrix core is busy.
-    // step `it` (stage it & 1): xn receives the A tile of step it+2 and xw holds that of
-    // step it+1, to be written to the other stage.  Two sets: one chunk loaded per region,
-    // xw written at the end.  One set (xn == xw): region r writes chunks 2r, 2r+1 and
-    // reloads chunks 2r-4, 2r-3; chunks 12-15 are reloaded after the last region, so
-    // every chunk has six regions to arrive.  With one set the decode of the next W'
-    // tile runs in regions 3-7, away from the A-tile writes of the first regions.
-    BlockCodes<G::NW> wcur;
-    // (stage_tag: the stage of step `it`, it & 1, as a compile-time constant)
-    auto step_body = [&](auto stage_tag, int64_t it, XRegs<G::ACH>& xn, const XRegs<G::ACH>& xw) {
+    // The body is laid out by hand as 8 regions fenced by sched_barrier: region r issues
+    // MFMAs 8r..8r+7 of this step (substep r/2, row tiles 2(r%2), 2(r%2)+1), then reloads the
+    // two A fragments they consumed for step it+2, reads the next substep's W' fragments
+    // (even regions) and carries one slice of the decode of the next step's W' tile (region
+    // 0: block constant and scaled table; regions 1-4: one 8-code chunk each, decoded and
+    // written to the other stage).  The last region's MFMAs run after the step's barrier,
+    // behind the first W' reads of the next step, so that those reads' latency is hidden.
+    BlockCodes wcur;
+    bf16x8 fb[2][4];
+    // (stage_tag: the stage of step `it`, it & 1, as a compile-time constant; `cur` holds the
+    // A fragments of step it and receives those of step it + 2)
+    auto step_body = [&](auto stage_tag, int it, AFrags& cur) {
         constexpr int st = decltype(stage_tag)::value;
-        const int64_t n2 = it + 2 < steps ? it + 2 : steps - 1;
-        const BlockCodes<G::NW> wnxt = load_codes(n2);
+        const int n2 = it + 2 < steps ? it + 2 : steps - 1;
+        const BlockCodes wnxt = load_codes(n2);
         const __amdgpu_buffer_rsrc_t rs_an = a_rsrc(n2);
-        const uint8_t* sA = lds + st * A_STAGE_OFF;
-        uint8_t* sAn = lds + (st ^ 1) * A_STAGE_OFF;
-        const uint8_t* sB = lds + W_REGION + st * W_STAGE_OFF;
-        uint8_t* sWn = lds + W_REGION + (st ^ 1) * W_STAGE_OFF;
-
-        bf16x8 fa[2][4], fb[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[0][i] = *reinterpret_cast<const bf16x8*>(sA + a_off(wm * 128 + i * 32 + (lane & 31), (lane >> 5)));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[0][j] = read_b(sB, j, 0);
-        __builtin_amdgcn_sched_barrier(0);
-
+        uint8_t* sWn = lds + (st ^ 1) * W_STAGE_BYTES;
         ScaledTable tbl;
 #pragma unroll
-        for (int rg = 0; rg < 8; ++rg) {
-            const int sub = rg >> 1, half = rg & 1, fc = sub & 1;
-            // next-substep fragments: region 2s loads A, region 2s+1 loads B
-            if (sub < 3) {
-                const int ch = 2 * (sub + 1) + (lane >> 5);
-                if (half == 0) {
+        for (int rg = 0; rg < 7; ++rg) {
+            const int s = rg >> 1, half = rg & 1, fc = s & 1;
+            if (half == 0 && s < 3) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        fa[fc ^ 1][i] = *reinterpret_cast<const bf16x8*>(sA + a_off(wm * 128 + i * 32 + (lane & 31), ch));
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) fb[fc ^ 1][j] = read_b(sB, j, sub + 1);
-                }
+                for (int j = 0; j < 4; ++j) fb[fc ^ 1][j] = read_b(st, j, s + 1);
             }
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int i = (half * 8 + t) >> 2, j = t & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fc][i], fb[fc][j], acc[i][j], 0, 0, 0);
-            }
-            // A tile chunks, spread over the regions: a burst of wide loads at the top of
-            // the step would stall the wave at the texture unit
-            if constexpr (G::DEPTH == 2) {
-                xn.r[rg] = buf_load16(rs_an, a_voff0 + rg * a_rstride, 0);
-            } else {
-                // region r writes chunks 2r, 2r+1 and (r >= 2) reloads chunks 2r-4, 2r-3
+            for (int t = 0; t < 8; ++t) mfma(2 * half + (t >> 2), t & 3, cur.f[2 * half + (t >> 2)][s], fb[fc][t & 3]);
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int i = 2 * rg + q;
-                    *reinterpret_cast<uint4*>(sAn + a_off((tid >> 3) + 32 * i, achunk)) = xw.r[i];
-                }
-                if (rg >= 2) {
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int i = 2 * rg - 4 + q;
-                        xn.r[i] = buf_load16(rs_an, a_voff0 + i * a_rstride, 0);
-                    }
-                }
-            }
-            // decode window: regions 0.. (two register sets) or 3.. (one set: the first
-            // half carries the A tile writes)
-            constexpr int D0 = G::DEPTH == 2 ? 0 : 3;
-            if (rg == D0) {
-                tbl = half_table(wcur.c1);
-            } else if (rg > D0 && rg - D0 - 1 < G::NCH && rg - D0 - 1 < 7 - D0) {
-                const int c = rg - D0 - 1;
-                uint32_t o[4];
-                decode8(tbl, word(wcur, c) ^ flip, o);
-                *reinterpret_cast<uint4*>(sWn + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
+            for (int q = 0; q < 2; ++q) cur.f[2 * half + q][s] = load_frag(rs_an, 2 * half + q, s);
+            if (rg == 0) {
+                tbl = make_pair_table(lvh, wcur.c1);
+            } else if (rg <= 4) {
+                decode_chunk(sWn, tbl, wcur, rg - 1);
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);     // VALU
-                if (t < (BWD && half ? 8 : 4) && sub < 3)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
-                if (G::DEPTH == 2 ? t == 2 : (rg >= 2 && (t == 2 || t == 6)))
+                if (rg <= 4) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                else __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+                if (half == 0 && s < 3 && t < 4)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // DS read
+                if (t == 2 || t == 5 || (rg == 0 && (t == 0 || t == 1)))
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-                if (G::DEPTH == 1 && (t == 4 || t == 7))
+                if (rg >= 1 && rg <= 4 && t == 6)
                     __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int c = (G::DEPTH == 2 ? 7 : 4); c < G::NCH; ++c) {
-            uint32_t o[4];
-            decode8(tbl, word(wcur, c) ^ flip, o);
-            *reinterpret_cast<uint4*>(sWn + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-        if constexpr (G::DEPTH == 2) {
-            store_a(xw, sAn);
-        } else {
-            // the last four chunks of the A tile of step it+2
-#pragma unroll
-            for (int i = 12; i < 16; ++i) xn.r[i] = buf_load16(rs_an, a_voff0 + i * a_rstride, 0);
-        }
         wcur = wnxt;
         __syncthreads();
+        // the next step's first W' fragments, then the last 8 MFMAs of this step behind them
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[0][j] = read_b(st ^ 1, j, 0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) mfma(2 + (t >> 2), t & 3, cur.f[2 + (t >> 2)][3], fb[1][t & 3]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) cur.f[2 + q][3] = load_frag(rs_an, 2 + q, 3);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+            if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // DS read
+            if (t == 2 || t == 5) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- prologue: stage 0 <- step 0; codes of step 1 (and, DEPTH 2, the A tile of step 1) ----
-    XRegs<G::ACH> xa, xb;
+    // ---- prologue: stage 0 <- W' of step 0; A fragments of steps 0 and 1; codes of step 1 ----
+    AFrags fa0, fa1;
     {
-        load_a(xa, 0);
-        const BlockCodes<G::NW> b0 = load_codes(0);
-        store_a(xa, lds);
-        dequant_store(lds + W_REGION, b0);
-    }
-    if constexpr (G::DEPTH == 2) {
-        load_a(xb, steps > 1 ? 1 : 0);
+        const BlockCodes b0 = load_codes(0);
         wcur = load_codes(steps > 1 ? 1 : 0);
-    } else {
-        // the loop's own request order (codes of a step, then the A tile of the step
-        // before it), so that its waits need no slack for a different order
-        wcur = load_codes(steps > 1 ? 1 : 0);
-        load_a(xa, steps > 1 ? 1 : 0);
+        load_all(fa0, 0);
+        load_all(fa1, steps > 1 ? 1 : 0);
+        const ScaledTable t0 = make_pair_table(lvh, b0.c1);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) decode_chunk(lds, t0, b0, c);
     }
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[0][j] = read_b(0, j, 0);
 
-    if constexpr (G::DEPTH == 2) {
-        int64_t it = 0;
+    {
+        int it = 0;
         for (; it + 1 < steps; it += 2) {
-            step_body(std::integral_constant<int, 0>{}, it, xa, xb);
-            step_body(std::integral_constant<int, 1>{}, it + 1, xb, xa);
+            step_body(std::integral_constant<int, 0>{}, it, fa0);
+            step_body(std::integral_constant<int, 1>{}, it + 1, fa1);
         }
-        if (it < steps) step_body(std::integral_constant<int, 0>{}, it, xa, xb);
-    } else {
-        int64_t it = 0;
-        for (; it + 1 < steps; it += 2) {
-            step_body(std::integral_constant<int, 0>{}, it, xa, xa);
-            step_body(std::integral_constant<int, 1>{}, it + 1, xa, xa);
-        }
-        if (it < steps) step_body(std::integral_constant<int, 0>{}, it, xa, xa);
+        if (it < steps) step_body(std::integral_constant<int, 0>{}, it, fa0);
     }
 
-    // ---- rank-r adapter term, staged through stage 0 in rank chunks of 64 ----
-    //   forward : acc += (s T) B^T   (A operand s*T [M x r], B operand rows of B [N x r])
-    //   backward: acc += (s U) A     (A operand s*U [M x r], B operand A [r x K], transposed read)
-    // (piece 0 only, for a split tile)
+    // ---- rank-r adapter term, in rank chunks of 64 (piece 0 only, for a split tile) ----
+    //   forward : acc += (s T) B^T   (A operand s*T [M x r], W' stage: rows of B [N x r])
+    //   backward: acc += (s U) A     (A operand s*U [M x r], W' stage: A [r x K], read transposed)
+    // The A operand comes straight from global memory (it is small: M x r), rank values past r
+    // zeroed on both sides.
     const int rr = u.split <= 0 ? a.r : 0;
+    const int64_t arows = a.M - m0 < TM ? a.M - m0 : TM;
     for (int rc = 0; rc < rr; rc += 64) {
-        uint8_t* sR = lds;                 // stage 0 of the layout above
-        uint8_t* sL = lds + W_REGION;
-#pragma unroll
-        for (int i = 0; i < TM * 8 / 256; ++i) {
-            const int qi = tid + 256 * i;
-            const int row = qi >> 3, c = qi & 7;
-            const int col = rc + 8 * c;
-            const int64_t gm = m0 + row;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (col < a.r && gm < a.M) v = *reinterpret_cast<const uint4*>(a.Rk + gm * a.r + col);
-            *reinterpret_cast<uint4*>(sR + a_off(row, c)) = v;
-        }
+        __syncthreads();                    // every wave is done with the stages
 #pragma unroll
         for (int i = 0; i < TN * 8 / 256; ++i) {
             const int qi = tid + 256 * i;
@@ -453,20 +333,40 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 const int64_t gk = c0 + 8 * c;
                 uint4 v = make_uint4(0, 0, 0, 0);
                 if (rc + j < a.r && gk < a.K) v = *reinterpret_cast<const uint4*>(a.Lr + (int64_t)(rc + j) * a.K + gk);
-                *reinterpret_cast<uint4*>(sL + wt_off<TN>(j, 8 * c)) = v;
+                *reinterpret_cast<uint4*>(lds + wt_off<TN>(j, 8 * c)) = v;
             } else {
                 const int row = qi >> 3, c = qi & 7;
                 const int col = rc + 8 * c;
                 const int64_t gn = c0 + row;
                 uint4 v = make_uint4(0, 0, 0, 0);
                 if (col < a.r && gn < a.N) v = *reinterpret_cast<const uint4*>(a.Lr + gn * a.r + col);
-                *reinterpret_cast<uint4*>(sL + tile_off(row, c)) = v;
+                *reinterpret_cast<uint4*>(lds + tile_off(row, c)) = v;
+            }
+        }
+        AFrags R;
+        {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.Rk + m0 * a.r + rc, arows * a.r * 2 - rc * 2);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bool live = rc + 16 * s + 8 * h < a.r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t off = (uint32_t)((128 * wave + 32 * i + rl) * a.r * 2 + 32 * s + 16 * h);
+                    R.f[i][s] = buf_load16(rs, live ? off : 0x80000000u, 0);
+                }
             }
         }
         __syncthreads();
-        const int left = a.r - rc;
-        mfma_step(sR, sL, left >= 64 ? 4 : (left + 15) / 16);
-        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 b[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = read_b(0, j, s);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mfma(i, j, R.f[i][s], b[j]);
+        }
     }
 
     // ---- piece of a split tile: fp32 partial tile, row-major TM x TN, summed later ----
@@ -476,10 +376,10 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int col = wn * 128 + j * 32 + (lane & 31);
+                const int col = j * 32 + rl;
 #pragma unroll
                 for (int reg = 0; reg < 16; ++reg) {
-                    const int row = wm * 128 + i * 32 + 8 * (reg >> 2) + 4 * (lane >> 5) + (reg & 3);
+                    const int row = wave * 128 + i * 32 + 8 * (reg >> 2) + 4 * h + (reg & 3);
                     slot[row * TN + col] = acc[i][j][reg];
                 }
             }
@@ -492,13 +392,59 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t col = c0 + wn * 128 + j * 32 + (lane & 31);
+            const int64_t col = c0 + j * 32 + rl;
 #pragma unroll
             for (int reg = 0; reg < 16; ++reg) {
-                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (reg >> 2) + 4 * (lane >> 5) + (reg & 3);
+                const int64_t row = m0 + wave * 128 + i * 32 + 8 * (reg >> 2) + 4 * h + (reg & 3);
                 if (row < a.M && col < ncols) a.out[row * ncols + col] = f32_to_bf16(acc[i][j][reg]);
             }
         }
+}
+
+// ---------------------------------------------------------------------------
+// Fragment-order packing of the fused products' A operand (X forward, dY backward: M x ld
+// bf16, row-major, ld % 8 == 0).  Block (tm, st), at (tm steps + st) * 64 KB of dst, holds
+// token rows 512 tm .. + 511 and contraction values 64 st .. + 63: chunk q (16 bytes) =
+// a_pack_chunk(row, c) for the 16-byte chunk c of the tile's row, zeros past M and past ld.
+// One workgroup per block: the tile is read row-major (coalesced) into LDS with XOR-swizzled
+// chunks, then written out in chunk order (coalesced); every LDS pass is free of bank
+// conflicts (16 consecutive rows read one chunk position; a write covers 2 rows x 8 chunks).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pack_a(const uint16_t* __restrict__ src, int64_t M, int64_t ld,
+                                                int64_t steps, uint16_t* __restrict__ dst) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t ptile[];   // 512 rows x 128 bytes
+    const int64_t blk = blockIdx.x, tm = blk / steps, st = blk % steps;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int row = (tid >> 3) + 32 * j, c = tid & 7;
+        const int64_t gm = tm * FUSED_TM + row, gk = st * 64 + 8 * c;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (gm < M && gk < ld) v = *reinterpret_cast<const uint4*>(src + gm * ld + gk);
+        *reinterpret_cast<uint4*>(ptile + tile_off(row, c)) = v;
+    }
+    __syncthreads();
+    uint4* out = reinterpret_cast<uint4*>(dst + blk * (A_BLOCK_BYTES / 2));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int q = tid + 256 * j;
+        out[q] = *reinterpret_cast<const uint4*>(ptile + tile_off(a_pack_row(q), a_pack_col(q)));
+    }
+}
+
+hipError_t launch_pack_a(const uint16_t* src, int64_t M, int64_t ld, uint16_t* dst, hipStream_t st) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_pack_a, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           A_BLOCK_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t steps = (ld + 63) / 64, tiles = (M + FUSED_TM - 1) / FUSED_TM;
+    if (steps * tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pack_a, dim3((unsigned)(steps * tiles)), dim3(256), A_BLOCK_BYTES, st, src, M, ld, steps,
+                       dst);
+    return hipGetLastError();
 }
 
 FusedEvents& fused_events() {
@@ -546,14 +492,6 @@ template <bool BWD>
 static hipError_t launch_fused(FusedArgs fa, int64_t ncols, int64_t steps, void* split_ws,
                                const Nf4Table& tab, hipStream_t st) {
     constexpr int TM = FUSED_TM, TN = FUSED_TN;
-    using G = FusedTile<TM, TN>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_fused<BWD, TM, TN>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     const FusedPlan p = fused_plan(fa.M, ncols, steps);
     fa.S = p.S;
     fa.chunk = p.chunk;
@@ -561,7 +499,7 @@ static hipError_t launch_fused(FusedArgs fa, int64_t ncols, int64_t steps, void*
     if (p.S > 1 && !split_ws) return hipErrorInvalidValue;
     // the profiling events cover the product and, for split tail tiles, their sum
     return with_events(st, [&] {
-        hipLaunchKernelGGL((k_fused<BWD, TM, TN>), dim3((unsigned)p.grid), dim3(256), G::LDS, st, fa, tab);
+        hipLaunchKernelGGL((k_fused<BWD>), dim3((unsigned)p.grid), dim3(256), 0, st, fa, tab);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.S == 1) return e;
         hipLaunchKernelGGL(k_split_reduce<TN>, dim3((unsigned)(p.tails * 32)), dim3(256), 0, st, fa.spart, p.S,
@@ -570,19 +508,19 @@ static hipError_t launch_fused(FusedArgs fa, int64_t ncols, int64_t steps, void*
     });
 }
 
-hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* X, int64_t M, const uint16_t* Ts,
+hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* Xpk, int64_t M, const uint16_t* Ts,
                             const uint16_t* Bl, int r, uint16_t* Y, void* split_ws, const Nf4Table& tab,
                             hipStream_t st) {
     if (M == 0 || W.rows == 0) return hipSuccess;
-    FusedArgs fa{W.codes, c1, W.rows, W.cols, X, M, Ts, Bl, r, Y, 1, 0, nullptr};
+    FusedArgs fa{W.codes, c1, W.rows, W.cols, Xpk, M, Ts, Bl, r, Y, 1, 0, nullptr};
     return launch_fused<false>(fa, W.rows, W.cols >> 6, split_ws, tab, st);
 }
 
-hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint16_t* dY, int64_t M, const uint16_t* Us,
+hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint16_t* dYpk, int64_t M, const uint16_t* Us,
                                const uint16_t* Al, int r, uint16_t* dX, void* split_ws, const Nf4Table& tab,
                                hipStream_t st) {
     if (M == 0 || W.cols == 0) return hipSuccess;
-    FusedArgs fa{W.codes, c1, W.rows, W.cols, dY, M, Us, Al, r, dX, 1, 0, nullptr};
+    FusedArgs fa{W.codes, c1, W.rows, W.cols, dYpk, M, Us, Al, r, dX, 1, 0, nullptr};
     return launch_fused<true>(fa, W.cols, (W.rows + 63) >> 6, split_ws, tab, st);
 }
 

@@ -68,9 +68,12 @@ inline hipError_t with_events(hipStream_t st, F&& fn) {
 }
 
 // ---- fused dequant products -------------------------------------------------
+// The A operand (X forward, dY backward; M x ld bf16, ld % 8 == 0) in fragment order, the
+// layout of tile_map.h, ceil(M/512) * ceil(ld/64) * A_BLOCK_BYTES bytes at dst.
+hipError_t launch_pack_a(const uint16_t* src, int64_t M, int64_t ld, uint16_t* dst, hipStream_t st);
 // Y = X W'^T + Ts B^T, Ts = s T   (MFMA GEMM, dequantization fused into the W operand load).
 // c1: the decoded first-level constants of W (launch_double_dequantize), one per 64-block.
-hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* X, int64_t M, const uint16_t* Ts,
+hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* Xpk, int64_t M, const uint16_t* Ts,
                             const uint16_t* Bl, int r, uint16_t* Y, void* split_ws, const Nf4Table& tab,
                             hipStream_t st);
 // Whole forward for M <= 16 tokens (HBM-bound dequant-GEMV): Y = X W'^T + s (X A^T) B^T and
@@ -81,7 +84,7 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
                              const uint16_t* Bl, int r, float s, uint16_t* Y, uint16_t* T, float* part,
                              const Nf4Table& tab, hipStream_t st);
 // dX = dY W' + Us A, Us = s U   (contraction over N, W' used transposed)
-hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint16_t* dY, int64_t M, const uint16_t* Us,
+hipError_t launch_fused_bwd_dx(const WeightView& W, const float* c1, const uint16_t* dYpk, int64_t M, const uint16_t* Us,
                                const uint16_t* Al, int r, uint16_t* dX, void* split_ws, const Nf4Table& tab,
                                hipStream_t st);
 

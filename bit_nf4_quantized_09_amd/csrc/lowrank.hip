@@ -153,8 +153,9 @@ __global__ __launch_bounds__(256) void k_gram_part(const float* __restrict__ Xm,
 //   SMALL_CHOL: G = L L^T (a column whose pivot falls to 1e-12 of the largest diagonal entry
 //     or below is dropped: its L column is zero); writes Minv = L^-T (l x l, fp32), whose
 //     dropped rows are zero, so that X Minv has orthonormal columns (zero where dropped).
-//   SMALL_EIG: cyclic Jacobi (round-robin order, n/2 disjoint rotations per round, sweeps
-//     until the off-diagonal mass falls below 1e-28 of the total, at most 40); sorts the
+//   SMALL_EIG: cyclic Jacobi (round-robin order, n/2 disjoint rotations per round, a pair
+//     skipped once its entry is below 1e-16 of the geometric mean of its diagonal entries;
+//     sweeps until the off-diagonal mass falls below 1e-22 of the total, at most 40); sorts the
 //     eigenvalues descending; sigma = sqrt(max(lambda, 0)); writes S[0..r) (fp32),
 //     Mb = V_r diag(g sigma^eb) and Ma = V_r diag(g sigma^ea) (l x r, fp32; a zero sigma
 //     gives a zero column when its exponent is negative) and, when err != null,
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
                 if (tid < st) s_red[tid] += s_red[tid + st];
                 __syncthreads();
             }
-            if (tid == 0) s_flag = !(s_red[0] > 1e-28 * total);
+            if (tid == 0) s_flag = !(s_red[0] > 1e-22 * total);
             if (tid <= n) s_slot[tid] = tid;
             __syncthreads();
             if (s_flag) break;
@@ -279,7 +280,8 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
                     double c = 1.0, s = 0.0;
                     if (q < l) {
                         const double gpq = G[p * LD + q];
-                        if (gpq != 0.0) {
+                        // a pair already orthogonal to working precision is left as it is
+                        if (fabs(gpq) > 1e-16 * sqrt(fabs(G[p * LD + p] * G[q * LD + q]))) {
                             const double tau = (G[q * LD + q] - G[p * LD + p]) / (2.0 * gpq);
                             const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
                             c = 1.0 / sqrt(1.0 + t * t);

@@ -20,21 +20,17 @@ constexpr int XCDS = 8;                 // accelerator complex dies, each with i
 constexpr int XCD_CUS = 32;             // compute units per XCD (256 / 8)
 constexpr int GROUP_M = 4;              // token tiles per group of the tile order
 constexpr int MAX_SPLIT = 4;            // pieces per tail tile at most
-// The A operand of a fused tile (X forward, dY backward: TM rows of ldA bf16 values) is
-// read through a buffer descriptor whose range the hardware caps at 2^31 - 1 bytes, with
-// 32-bit per-lane offsets from the step's first column of the tile's first row.  A lane's
-// 16-byte chunk i of a step sits at row a_chunk_row(tid, i), byte a_chunk_byte(tid) of
-// the step's 128 (64 bf16), so the furthest chunk ends at (TM - 1) 2 ldA + 128 bytes:
-// the leading dimension of an operand a fused product reads (K forward, N backward) is
-// at most FUSED_LD_LIMIT.
-constexpr int A_CHUNKS = FUSED_TM / 32;  // 16-byte chunks per lane per step
-__host__ __device__ __forceinline__ int a_chunk_row(int tid, int i) { return (tid >> 3) + 32 * i; }
-__host__ __device__ __forceinline__ int a_chunk_byte(int tid) { return (tid & 7) * 16; }
-__host__ __device__ __forceinline__ int64_t a_chunk_offset(int tid, int i, int64_t ldA) {
-    return (int64_t)a_chunk_row(tid, i) * ldA * 2 + a_chunk_byte(tid);
+// Fragment-order layout of the fused products' A operand (X forward, dY backward), written
+// by k_pack_a and read by k_fused: one 64 KB block per (512-row token tile, 64-value step),
+// 4096 chunks of 16 bytes.  Chunk q = 1024 w + 64 (4 i + s) + l is the 16 bytes lane l of
+// wave w loads for MFMA fragment (row tile i, substep s): tile row 128 w + 32 i + l % 32,
+// 16-byte column 2 s + l / 32 of the step's 128 bytes (contraction values 16 s + 8 (l / 32)
+// .. + 7, the v_mfma_f32_32x32x16_bf16 A-operand layout).
+constexpr int A_BLOCK_BYTES = 65536;
+__host__ __device__ __forceinline__ int a_pack_row(int q) {
+    return 128 * (q >> 10) + 32 * ((q >> 8) & 3) + (q & 31);
 }
-constexpr int64_t DESC_RANGE_MAX = 0x7FFFFFFF;
-constexpr int64_t FUSED_LD_LIMIT = (DESC_RANGE_MAX - 128) / (2 * (FUSED_TM - 1));   // 2,101,255
+__host__ __device__ __forceinline__ int a_pack_col(int q) { return 2 * ((q >> 6) & 3) + ((q >> 5) & 1); }
 
 // Split of a launch's tail tiles along the contraction (S == 1: none).  A launch with
 // S > 1 needs `bytes` of split workspace: `tails` x S fp32 partial tiles, summed by a

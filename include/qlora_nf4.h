@@ -167,9 +167,7 @@ nf4_status nf4_dequantize(const nf4_weight* W, void* out, nf4_dtype out_dtype, v
  *   Y = X W'^T + s (X A^T) B^T,  s = alpha / r,  W' = dequant(W) rounded to bf16
  * with the dequantization fused into the matrix multiply.
  *   W       N x K weight, K a multiple of 64, N a multiple of 8, N*K < 2^32,
- *           N and K at most 2,101,255 (the fused products read 512 rows of an
- *           operand whose row length is K forward and N backward within one
- *           buffer range of at most 2^31 - 1 bytes)
+ *           N and K below 2^22 (the kernels' 32-bit buffer offsets)
  *   X       bf16 M x K;  0 <= M < 2^23 (M == 0 enqueues nothing); for M > 16 the
  *           product runs as ceil(M/512) * ceil(N/128) output tiles (plus split
  *           pieces), which must stay below 2^24 (backward: ceil(M/512) * ceil(K/128))

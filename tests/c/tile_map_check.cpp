@@ -5,9 +5,8 @@
 // contraction ranges partition all steps; that the pieces of a tile run on one XCD
 // after that XCD's whole tiles and own S partial slots inside the planned workspace;
 // that the summing kernel's slot -> tile lookup inverts the map (and rejects unused
-// slots); and that tail waves fit the XCD.  It also checks that the lanes' A-tile chunks
-// cover the step's TM rows once each and, at the leading-dimension limit the library
-// enforces, end inside the 2^31 - 1 byte descriptor range.  Prints "<shapes> <failures>".
+// slots); and that tail waves fit the XCD.  It also checks that the fragment-order packing
+// of the A operand is a bijection onto the MFMA operand layout.  Prints "<shapes> <failures>".
 #include <cstdio>
 #include <map>
 #include <set>
@@ -114,31 +113,21 @@ int main() {
                 if (bad < 10) std::printf("# tiles=%lld steps=%lld code %d\n", (long long)T, (long long)S, e);
             }
         }
-    // A-tile offsets: at the ABI's leading-dimension limit every 16-byte chunk of every lane
-    // ends inside the descriptor's 2^31 - 1 byte range; one element further and the last
-    // rows' chunks would not (the limit is the largest that fits)
-    for (int64_t ld : {(int64_t)64, (int64_t)65600, FUSED_LD_LIMIT - 63, FUSED_LD_LIMIT, FUSED_LD_LIMIT + 1}) {
-        int64_t far = 0;
-        for (int tid = 0; tid < 256; ++tid)
-            for (int i = 0; i < A_CHUNKS; ++i) {
-                const int row = a_chunk_row(tid, i), byte = a_chunk_byte(tid);
-                if (row < 0 || row >= FUSED_TM || byte < 0 || byte + 16 > 128) { ++bad; continue; }
-                const int64_t end = a_chunk_offset(tid, i, ld) + 16;
-                if (end > far) far = end;
-            }
-        ++shapes;
-        const bool fits = far <= DESC_RANGE_MAX;
-        if (fits != (ld <= FUSED_LD_LIMIT)) {
-            ++bad;
-            std::printf("# ldA=%lld furthest chunk end %lld\n", (long long)ld, (long long)far);
-        }
-    }
-    // every (row, chunk) of the TM x 128-byte step is covered by exactly one (lane, chunk)
+    // fragment-order packing: the 4096 chunks of a block cover the 512 rows x 8 chunk columns
+    // of a step once each, and chunk q of the block is what lane q % 64 of wave q / 1024
+    // loads for fragment (i, s) = ((q / 256) % 4, (q / 64) % 4): row 128 w + 32 i + l % 32,
+    // column 2 s + l / 32 (the 32x32x16 bf16 MFMA A-operand layout)
     {
         std::vector<int> seen(FUSED_TM * 8, 0);
-        for (int tid = 0; tid < 256; ++tid)
-            for (int i = 0; i < A_CHUNKS; ++i) seen[a_chunk_row(tid, i) * 8 + a_chunk_byte(tid) / 16]++;
         ++shapes;
+        for (int q = 0; q < A_BLOCK_BYTES / 16; ++q) {
+            const int row = a_pack_row(q), col = a_pack_col(q);
+            if (row < 0 || row >= FUSED_TM || col < 0 || col >= 8) { ++bad; break; }
+            seen[row * 8 + col]++;
+            const int w = q >> 10, l = q & 63, frag = (q >> 6) & 15, i = frag >> 2, s = frag & 3;
+            if (16 * q != w * 16384 + 4096 * i + 1024 * s + 16 * l) ++bad;
+            if (row != 128 * w + 32 * i + (l & 31) || col != 2 * s + (l >> 5)) ++bad;
+        }
         for (int v : seen)
             if (v != 1) { ++bad; break; }
     }

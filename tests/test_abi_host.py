@@ -72,7 +72,9 @@ def test_storage_accounting_closed_forms():
 
 
 def test_workspace_sizes():
-    assert nf4.nf4_workspace_bytes(nf4.NF4_OP_DOUBLE_QUANTIZE, 0, 2048, 0, 0) == 0
+    # double quantization keeps one float64 sum per 2048-constant chunk of the mean's tree
+    assert nf4.nf4_workspace_bytes(nf4.NF4_OP_DOUBLE_QUANTIZE, 0, 0, 0, 0) == 0
+    assert nf4.nf4_workspace_bytes(nf4.NF4_OP_DOUBLE_QUANTIZE, 0, 2048, 0, 0) == 8
     assert nf4.nf4_workspace_bytes(nf4.NF4_OP_DOUBLE_QUANTIZE, 0, 2049, 0, 0) == 2 * 8
     fwd = nf4.nf4_workspace_bytes(nf4.NF4_OP_LINEAR_FWD, 4096, 8192, 8192, 64)
     bwd = nf4.nf4_workspace_bytes(nf4.NF4_OP_LINEAR_BWD, 4096, 8192, 8192, 64)
@@ -106,7 +108,8 @@ def test_double_quantize_rejects_bad_arguments():
     p = ctypes.c_void_p(4096)
     assert L.nf4_double_quantize(p, 100, 128, p, p, p, None, 0, None) == nf4.NF4_ERR_UNSUPPORTED
     assert L.nf4_double_quantize(p, 100, 256, p, p, None, None, 0, None) == nf4.NF4_ERR_ARG
-    # n1 > 2048 needs a workspace
+    # n1 > 0 needs a workspace (one float64 per 2048 constants)
+    assert L.nf4_double_quantize(p, 100, 256, p, p, p, None, 0, None) == nf4.NF4_ERR_WORKSPACE
     assert L.nf4_double_quantize(p, 5000, 256, p, p, p, None, 0, None) == nf4.NF4_ERR_WORKSPACE
     assert L.nf4_double_quantize(p, 5000, 256, p, p, p, p, 8, None) == nf4.NF4_ERR_WORKSPACE
     assert L.nf4_double_dequantize(p, p, p, 10, 64, p, None) == nf4.NF4_ERR_UNSUPPORTED
@@ -141,19 +144,13 @@ def test_linear_rejects_bad_arguments():
     assert fwd(ctypes.byref(good), p, 0, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_OK  # M = 0
     # size limits (32-bit operand offsets, launch grid), before any device call
     assert fwd(ctypes.byref(_w(1 << 22, 64)), p, 16, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_ERR_UNSUPPORTED
-    assert b"at most 2101255" in L.nf4_last_error()
+    assert b"below 2^22" in L.nf4_last_error()
     assert fwd(ctypes.byref(_w(64, 1 << 22)), p, 16, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_ERR_UNSUPPORTED
-    # the fused tiles read 512 operand rows of length K (forward) or N (backward) inside one
-    # 2^31 - 1 byte buffer range, so N, K <= 2,101,255: K = 2,101,312 (the next multiple of
-    # 64 past the limit) and N = 2,101,256 (the next multiple of 8) are rejected, before any
-    # device call, for every token count; K = N = 2,101,248 pass the shape checks (they fail
+    # the largest accepted N and K pass the shape checks, for every token count (they fail
     # later, on the workspace size, which this call gives as 16 bytes)
     for M in (1, 16, 17, 4096):
-        assert fwd(ctypes.byref(_w(8, 2101312)), p, M, p, p, 8, 16.0, p, p, ws, 16, None) == nf4.NF4_ERR_UNSUPPORTED
-        assert fwd(ctypes.byref(_w(8, 2101248)), p, M, p, p, 8, 16.0, p, p, ws, 16, None) == nf4.NF4_ERR_WORKSPACE
-        assert L.qlora_linear_bwd(ctypes.byref(_w(2101256, 64)), p, p, M, p, p, 8, 16.0, p, p, p, p, ws, 16,
-                                  None) == nf4.NF4_ERR_UNSUPPORTED
-        assert L.qlora_linear_bwd(ctypes.byref(_w(2101248, 64)), p, p, M, p, p, 8, 16.0, p, p, p, p, ws, 16,
+        assert fwd(ctypes.byref(_w(8, (1 << 22) - 64)), p, M, p, p, 8, 16.0, p, p, ws, 16, None) == nf4.NF4_ERR_WORKSPACE
+        assert L.qlora_linear_bwd(ctypes.byref(_w((1 << 22) - 8, 64)), p, p, M, p, p, 8, 16.0, p, p, p, p, ws, 16,
                                   None) == nf4.NF4_ERR_WORKSPACE
     assert fwd(ctypes.byref(good), p, 1 << 23, p, p, 8, 16.0, p, p, ws, 1 << 20, None) == nf4.NF4_ERR_UNSUPPORTED
     wide = _w(1025 * 128, 64)       # (2^14 - 1) token tiles x 1025 feature tiles >= 2^24

@@ -217,13 +217,13 @@ def test_llama65b_layer_chain_sampled():
             p[k] = None
 
 
-@pytest.mark.parametrize("N,K", [(8, 2101248), (2101248, 64)])
-def test_operand_rows_at_the_descriptor_limit(N, K):
-    # The fused tiles read 512 rows of X (row length K, forward) or dY (row length N,
-    # backward) through one buffer descriptor of at most 2^31 - 1 bytes; the ABI accepts
-    # N and K up to 2,101,255.  At the largest accepted multiples the last rows of the
-    # 512-row tile (rows 358-511 would have read as zero past 2^31 bytes) must carry their
-    # products: eight rows of every wave are compared
+@pytest.mark.parametrize("N,K", [(8, (1 << 22) - 64), ((1 << 22) - 8, 64)])
+def test_longest_operand_rows(N, K):
+    # The largest N and K the ABI accepts (below 2^22): X rows of length K (forward) and dY
+    # rows of length N (backward) as long as they get, with every byte offset of every kernel
+    # below 2^31 (an earlier form of the fused product read its token operand through one
+    # 2^31-byte range, and the last rows of its 512-row tiles lost their products past it);
+    # eight rows of every wave of the 512-row tile are compared
     M = 512
     W, X, A, B, dY = linear_inputs(N, K, M, 8, seed=seed_of(24, N, K), device=DEV)
     _run(W, X, A, B, dY, alpha=16.0, rows=_sampled_rows(M, 8, 3, band=128))
