@@ -27,15 +27,16 @@
 
 namespace nf4 {
 
-constexpr int LR_TM = 64;       // rows of a tall-product tile
+constexpr int LR_TM = 128;      // rows of a tall-product tile
 constexpr int LR_TP = 32;       // contraction values per staged chunk
 
 // ---------------------------------------------------------------------------
 // C = op(E) X: E is M x P row-major (TRANS false) or P x M row-major (TRANS true), X is
-// P x l row-major, C is M x l.  Workgroup (row tile, contraction slice z): 64 rows x all
+// P x l row-major, C is M x l.  Workgroup (row tile, contraction slice z): 128 rows x all
 // l <= LR_MAX columns over contraction values [z pchunk, (z+1) pchunk); thread (ty, tx)
-// owns rows 4 ty .. 4 ty + 3 and columns tx + 16 j.  Sums over p in ascending order (fp32
-// FMA); the slice's sums go to part[z] (M x l), or straight to C when there is one slice.
+// owns rows 8 ty .. 8 ty + 7 and columns tx + 16 j (48 accumulators, 6 FMAs per LDS read).
+// Sums over p in ascending order (fp32 FMA); the slice's sums go to part[z] (M x l), or
+// straight to C when there is one slice.
 // ---------------------------------------------------------------------------
 template <bool TRANS>
 __global__ __launch_bounds__(256) void k_tall(const float* __restrict__ E, int64_t M, int64_t P,
@@ -47,9 +48,9 @@ __global__ __launch_bounds__(256) void k_tall(const float* __restrict__ E, int64
     const int64_t m0 = (int64_t)blockIdx.x * LR_TM;
     const int64_t p0 = (int64_t)blockIdx.y * pchunk;
     const int64_t p1 = p0 + pchunk < P ? p0 + pchunk : P;
-    float acc[4][LR_MAX / 16];
+    float acc[8][LR_MAX / 16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < LR_MAX / 16; ++j) acc[i][j] = 0.0f;
     for (int64_t pc = p0; pc < p1; pc += LR_TP) {
@@ -72,21 +73,22 @@ __global__ __launch_bounds__(256) void k_tall(const float* __restrict__ E, int64
         __syncthreads();
 #pragma unroll 4
         for (int pp = 0; pp < LR_TP; ++pp) {
-            const float4 a = *reinterpret_cast<const float4*>(&sA[pp][4 * ty]);
-            const float av[4] = {a.x, a.y, a.z, a.w};
+            const float4 a0 = *reinterpret_cast<const float4*>(&sA[pp][8 * ty]);
+            const float4 a1 = *reinterpret_cast<const float4*>(&sA[pp][8 * ty + 4]);
+            const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
             for (int j = 0; j < LR_MAX / 16; ++j) {
                 const float b = sB[pp][tx + 16 * j];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][j] = __fmaf_rn(av[i], b, acc[i][j]);
+                for (int i = 0; i < 8; ++i) acc[i][j] = __fmaf_rn(av[i], b, acc[i][j]);
             }
         }
         __syncthreads();
     }
     float* out = part + (int64_t)blockIdx.y * M * l;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + 4 * ty + i;
+    for (int i = 0; i < 8; ++i) {
+        const int64_t m = m0 + 8 * ty + i;
 #pragma unroll
         for (int j = 0; j < LR_MAX / 16; ++j) {
             const int c = tx + 16 * j;
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void k_slices_sum(const float* __restrict__ pa
 // (fp64 products of the fp32 values, rows ascending).  Workgroup b covers LR_GROWS rows;
 // thread t owns entries e = t + 256 k of the l x l matrix.
 // ---------------------------------------------------------------------------
-constexpr int LR_GROWS = 256;
+constexpr int LR_GROWS = 64;
 __global__ __launch_bounds__(256) void k_gram_part(const float* __restrict__ Xm, int64_t rows, int l,
                                                    double* __restrict__ gpart) {
     constexpr int EPT = LR_MAX * LR_MAX / 256;   // entries per thread
@@ -147,13 +149,23 @@ __global__ __launch_bounds__(256) void k_gram_part(const float* __restrict__ Xm,
         if (ea[k] < l && ec[k] < l) out[ea[k] * l + ec[k]] = acc[k];
 }
 
+// G[e] = sum over the nparts Gram partials of gpart[z][e], z ascending (one entry per thread).
+__global__ __launch_bounds__(256) void k_gram_sum(const double* __restrict__ gpart, int nparts, int64_t n,
+                                                  double* __restrict__ G) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    double s = 0.0;
+    for (int z = 0; z < nparts; ++z) s += gpart[(int64_t)z * n + e];
+    G[e] = s;
+}
+
 // ---------------------------------------------------------------------------
 // The l x l problems, one workgroup, fp64 in LDS (dynamic: 2 LR_MAX (LR_MAX + 1) doubles).
-// G = sum of the nparts Gram partials, in order.
+// G: the Gram matrix (summed by k_gram_sum).
 //   SMALL_CHOL: G = L L^T (a column whose pivot falls to 1e-12 of the largest diagonal entry
 //     or below is dropped: its L column is zero); writes Minv = L^-T (l x l, fp32), whose
 //     dropped rows are zero, so that X Minv has orthonormal columns (zero where dropped).
-//   SMALL_EIG: cyclic Jacobi (round-robin order, n/2 disjoint rotations per round, a pair
+//   SMALL_EIG: cyclic Jacobi (circle-method order, n/2 disjoint rotations per round, a pair
 //     skipped once its entry is below 1e-16 of the geometric mean of its diagonal entries;
 //     sweeps until the off-diagonal mass falls below 1e-22 of the total, at most 40); sorts the
 //     eigenvalues descending; sigma = sqrt(max(lambda, 0)); writes S[0..r) (fp32),
@@ -186,15 +198,10 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
     __shared__ double s_red[256];
     __shared__ double s_c[LR_MAX / 2], s_s[LR_MAX / 2];
     __shared__ int s_p[LR_MAX / 2], s_q[LR_MAX / 2];
-    __shared__ int s_slot[LR_MAX + 1];
     __shared__ int s_order[LR_MAX];
     __shared__ int s_flag;
     const int tid = threadIdx.x, l = a.l;
-    for (int e = tid; e < l * l; e += 256) {
-        double s = 0.0;
-        for (int z = 0; z < a.nparts; ++z) s += a.gpart[(int64_t)z * l * l + e];
-        G[(e / l) * LD + e % l] = s;
-    }
+    for (int e = tid; e < l * l; e += 256) G[(e / l) * LD + e % l] = a.gpart[e];   // the summed Gram matrix
     __syncthreads();
     // symmetrize (the partial sums of (a, c) and (c, a) are the same products, in the same
     // order, so this only guards the algorithms below against any asymmetry)
@@ -255,6 +262,15 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
         for (int i = 0; i < l; ++i)
             for (int j = 0; j < l; ++j) total += G[i * LD + j] * G[i * LD + j];
         __syncthreads();
+        // this thread's (pair, index) work items of a round: e = tid + 256 m < np * l
+        constexpr int WI = (LR_MAX / 2 * LR_MAX + 255) / 256;
+        int wk[WI], wc[WI];
+#pragma unroll
+        for (int m = 0; m < WI; ++m) {
+            const int e = tid + 256 * m;
+            wk[m] = e < np * l ? e / l : -1;
+            wc[m] = e < np * l ? e % l : 0;
+        }
         for (int sweep = 0; sweep < 40; ++sweep) {
             // off-diagonal mass
             double off = 0.0;
@@ -269,13 +285,14 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
                 __syncthreads();
             }
             if (tid == 0) s_flag = !(s_red[0] > 1e-22 * total);
-            if (tid <= n) s_slot[tid] = tid;
             __syncthreads();
             if (s_flag) break;
             for (int round = 0; round < n - 1; ++round) {
-                // this round's pairs and rotations
+                // this round's pairs (circle method: index n - 1 meets `round`, the others
+                // meet across the circle of n - 1) and rotations
                 if (tid < np) {
-                    int p = s_slot[tid], q = s_slot[n - 1 - tid];
+                    int p = tid == 0 ? n - 1 : (round + tid) % (n - 1);
+                    int q = tid == 0 ? round : (round - tid + (n - 1)) % (n - 1);
                     if (p > q) { const int t = p; p = q; q = t; }
                     double c = 1.0, s = 0.0;
                     if (q < l) {
@@ -295,8 +312,11 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
                 }
                 __syncthreads();
                 // G <- J^T G (rows p, q of every pair)
-                for (int e = tid; e < np * l; e += 256) {
-                    const int k = e / l, col = e % l, p = s_p[k], q = s_q[k];
+#pragma unroll
+                for (int m = 0; m < WI; ++m) {
+                    const int k = wk[m], col = wc[m];
+                    if (k < 0) continue;
+                    const int p = s_p[k], q = s_q[k];
                     if (q >= l) continue;
                     const double c = s_c[k], s = s_s[k];
                     const double gp = G[p * LD + col], gq = G[q * LD + col];
@@ -305,8 +325,11 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
                 }
                 __syncthreads();
                 // G <- G J and V <- V J (columns p, q of every pair)
-                for (int e = tid; e < np * l; e += 256) {
-                    const int k = e / l, row = e % l, p = s_p[k], q = s_q[k];
+#pragma unroll
+                for (int m = 0; m < WI; ++m) {
+                    const int k = wk[m], row = wc[m];
+                    if (k < 0) continue;
+                    const int p = s_p[k], q = s_q[k];
                     if (q >= l) continue;
                     const double c = s_c[k], s = s_s[k];
                     const double gp = G[row * LD + p], gq = G[row * LD + q];
@@ -315,13 +338,6 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
                     const double vp = V[row * LD + p], vq = V[row * LD + q];
                     V[row * LD + p] = c * vp - s * vq;
                     V[row * LD + q] = s * vp + c * vq;
-                }
-                __syncthreads();
-                // round-robin: slot 0 stays, the others move by one
-                if (tid == 0) {
-                    const int last = s_slot[n - 1];
-                    for (int j = n - 1; j > 1; --j) s_slot[j] = s_slot[j - 1];
-                    s_slot[1] = last;
                 }
                 __syncthreads();
             }
@@ -346,12 +362,22 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
             a.Ma[row * a.r + t] = (float)(V[row * LD + j] * fa * (double)a.g);
         }
         if (tid < a.r) a.S[tid] = (float)sqrt(fmax(G[s_order[tid] * LD + s_order[tid]], 0.0));
-        if (tid == 0 && a.err) {
+        if (a.err) {
+            // ||E||^2: the nnorm <= 1024 partials, 4 per thread in order, then a fixed tree
             double e2 = 0.0;
-            for (int z = 0; z < a.nnorm; ++z) e2 += a.norm2[z];
-            double cap = 0.0;
-            for (int t = 0; t < a.r; ++t) cap += fmax(G[s_order[t] * LD + s_order[t]], 0.0);
-            *a.err = sqrt(fmax(e2 - cap, 0.0));
+            for (int z = 4 * tid; z < 4 * tid + 4; ++z) e2 += z < a.nnorm ? a.norm2[z] : 0.0;
+            __syncthreads();
+            s_red[tid] = e2;
+            __syncthreads();
+            for (int st = 128; st > 0; st >>= 1) {
+                if (tid < st) s_red[tid] += s_red[tid + st];
+                __syncthreads();
+            }
+            if (tid == 0) {
+                double cap = 0.0;
+                for (int t = 0; t < a.r; ++t) cap += fmax(G[s_order[t] * LD + s_order[t]], 0.0);
+                *a.err = sqrt(fmax(s_red[0] - cap, 0.0));
+            }
         }
     }
 }
@@ -482,6 +508,7 @@ size_t lowrank_ws_bytes(int64_t N, int64_t K, int l, int r) {
     b += 2 * al256((size_t)K * l * 4);                       // Z, Z2
     b += al256((size_t)LR_MAX_SLICES * big * l * 4);          // tall-product slices
     b += al256((size_t)cdiv(big, LR_GROWS) * l * l * 8);      // Gram partials
+    b += al256((size_t)l * l * 8);                           // their sum
     b += al256((size_t)l * l * 4);                           // Minv
     b += 2 * al256((size_t)l * r * 4);                       // Mb, Ma
     return b;
@@ -490,6 +517,7 @@ size_t lowrank_ws_bytes(int64_t N, int64_t K, int l, int r) {
 struct LowrankWs {
     float *Y, *Y2, *Z, *Z2, *part;
     double* gpart;
+    double* gsum;
     float *Minv, *Mb, *Ma;
 };
 
@@ -504,6 +532,7 @@ static LowrankWs carve(void* ws, int64_t N, int64_t K, int l, int r) {
     w.Z2 = (float*)take((size_t)K * l * 4);
     w.part = (float*)take((size_t)LR_MAX_SLICES * big * l * 4);
     w.gpart = (double*)take((size_t)cdiv(big, LR_GROWS) * l * l * 8);
+    w.gsum = (double*)take((size_t)l * l * 8);
     w.Minv = (float*)take((size_t)l * l * 4);
     w.Mb = (float*)take((size_t)l * r * 4);
     w.Ma = (float*)take((size_t)l * r * 4);
@@ -540,9 +569,15 @@ static hipError_t tall(bool trans, const float* E, int64_t M, int64_t P, const f
     return hipGetLastError();
 }
 
-static hipError_t gram(const float* Xm, int64_t rows, int l, double* gpart, int* nparts, hipStream_t s) {
-    *nparts = (int)cdiv(rows, LR_GROWS);
-    hipLaunchKernelGGL(k_gram_part, dim3((unsigned)*nparts), dim3(256), 0, s, Xm, rows, l, gpart);
+// G (l x l fp64, at gsum) = Xm^T Xm over `rows` rows: partial sums per 64 rows, then their
+// fixed-order sum
+static hipError_t gram(const float* Xm, int64_t rows, int l, double* gpart, double* gsum, hipStream_t s) {
+    const int nparts = (int)cdiv(rows, LR_GROWS);
+    hipLaunchKernelGGL(k_gram_part, dim3((unsigned)nparts), dim3(256), 0, s, Xm, rows, l, gpart);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gram_sum, dim3((unsigned)cdiv((int64_t)l * l, 256)), dim3(256), 0, s, gpart, nparts,
+                       (int64_t)l * l, gsum);
     return hipGetLastError();
 }
 
@@ -551,12 +586,11 @@ static hipError_t orth(float* X, float* tmp, int64_t rows, int l, LowrankWs& w, 
     float* src = X;
     float* dst = tmp;
     for (int pass = 0; pass < 2; ++pass) {
-        int np = 0;
-        hipError_t e = gram(src, rows, l, w.gpart, &np, s);
+        hipError_t e = gram(src, rows, l, w.gpart, w.gsum, s);
         if (e != hipSuccess) return e;
         SmallArgs a{};
-        a.gpart = w.gpart;
-        a.nparts = np;
+        a.gpart = w.gsum;
+        a.nparts = 1;
         a.l = l;
         a.Minv = w.Minv;
         hipLaunchKernelGGL(k_small<SMALL_CHOL>, dim3(1), dim3(256), small_lds(), s, a);
@@ -593,12 +627,11 @@ static hipError_t lowrank_factors(const float* E, int64_t N, int64_t K, int r, i
     if (e != hipSuccess) return e;
     // Z = E^T Y, its Gram matrix, the eigen-decomposition and the factor matrices
     e = tall(true, E, K, N, w.Y, l, w.Z, w.part, s);
-    int np = 0;
-    if (e == hipSuccess) e = gram(w.Z, K, l, w.gpart, &np, s);
+    if (e == hipSuccess) e = gram(w.Z, K, l, w.gpart, w.gsum, s);
     if (e != hipSuccess) return e;
     SmallArgs a{};
-    a.gpart = w.gpart;
-    a.nparts = np;
+    a.gpart = w.gsum;
+    a.nparts = 1;
     a.l = l;
     a.r = r;
     a.S = S;
