@@ -34,6 +34,31 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 NF4_BYTES_PER_PARAM = 0.5 + 1.0 / 64 + 4.0 / (64 * 256)
 
 
+def rocminfo_peaks():
+    """The GPU agent's compute-unit count and maximum engine clock as rocminfo reports them,
+    and the dense bf16 MFMA peak they give (4096 flops per clock per CU: four matrix cores
+    of 1024); None where rocminfo is missing or reports no GPU agent."""
+    import re
+    import subprocess
+
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in out.split("*******")[1:]:
+        kind = re.search(r"Device Type:\s+(\w+)", agent)
+        if not kind or kind.group(1) != "GPU":
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        name = re.search(r"Name:\s+(gfx\w+)", agent)
+        if cu and mhz:
+            cus, clk = int(cu.group(1)), int(mhz.group(1))
+            return {"agent": name.group(1) if name else None, "cus": cus, "max_sclk_mhz": clk,
+                    "bf16_tflops_at_max_sclk": round(cus * clk * 1e6 * 4096 / 1e12, 1)}
+    return None
+
+
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -48,6 +73,16 @@ def _args():
                    help="one step of the workload, then a plain 512 MiB device copy (for counter runs)")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 counter CSVs (FETCH_SIZE, WRITE_SIZE) into the traffic summary")
+    p.add_argument("--summarize-mfma", nargs=3, metavar=("COUNTER_CSV", "TRACE_CSV", "COMMAND"),
+                   help="matrix-core utilisation and clock of the fused products from a GRBM_COUNT / "
+                        "SQ_VALU_MFMA_BUSY_CYCLES counter pass with its kernel trace")
+    p.add_argument("--pmc-codec-workload", action="store_true",
+                   help="one pass of each codec and few-token kernel over the 65B layer, then a plain "
+                        "512 MiB device copy (for counter runs)")
+    p.add_argument("--summarize-pmc-codec", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="per-kernel traffic table of two counter runs over --pmc-codec-workload")
+    p.add_argument("--hbm-ceiling", action="store_true",
+                   help="read / write / copy streaming probes over 4 GiB, as a markdown table")
     p.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "COMMAND"),
                    help="turn a rocprofv3 kernel-stats CSV into a short summary naming its command")
     p.add_argument("--gemv-sweep", action="store_true",
@@ -57,8 +92,12 @@ def _args():
                    help="per-shape kernel durations of a --gemv-sweep kernel trace, as a markdown table")
     p.add_argument("--codebooks-only", action="store_true",
                    help="the codebook comparison only (the 'codebooks' path figures), as a JSON line")
+    p.add_argument("--gemv-only", action="store_true",
+                   help="the few-token forward only (the 'gemv' path figures over the 65B layer), as a JSON line")
     p.add_argument("--loftq-only", action="store_true",
                    help="the LoftQ initialisation only (the 'loftq' path figures), as a JSON line")
+    p.add_argument("--bulk-codec-only", action="store_true",
+                   help="the bulk codec round trip over 32 LLaMA-7B-shaped layers only, as a JSON line")
     p.add_argument("--adamw-only", action="store_true",
                    help="the adapter optimizer step only (the 'adamw' path figures), as a JSON line "
                         "(for kernel traces and counter runs)")
@@ -159,10 +198,12 @@ KERNEL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_09_amd", "csrc", f)
 COPY_BYTES = 512 << 20
 
 
-def kernel_source_hash():
+def kernel_source_hash(names=None):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    files = KERNEL_SOURCES if names is None else [os.path.join(ROOT, "bit_nf4_quantized_09_amd", "csrc", f)
+                                                  for f in names]
+    for f in files:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -237,6 +278,55 @@ def summarize_trace(stats_csv, command):
         out.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
             name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
             100.0 * float(r["TotalDurationNs"]) / total))
+    print("\n".join(out))
+
+
+def summarize_mfma(counter_csv, trace_csv, command):
+    """Clock and matrix-core utilisation of the fused products from one counter pass
+    (GRBM_COUNT, SQ_VALU_MFMA_BUSY_CYCLES, summed over the 8 XCDs) with a kernel trace of the
+    same run (durations): clock = (GRBM_COUNT / 8) / duration; MFMA work = algorithmic flops /
+    1024 SIMD-cycles (a v_mfma_f32_32x32x16_bf16, 32768 flops, occupies a SIMD's matrix core
+    for 32 cycles); utilisation = MFMA work / (1024 SIMDs x cycles of the launch).  The shape
+    of each launch is read back from the workload's launch order (7 forwards q..down, then 7
+    backwards down..q)."""
+    import csv
+    from workloads import LLAMA65B, layer_projections
+
+    dur = {}
+    for r in csv.DictReader(open(trace_csv)):
+        if "k_fused" in r["Kernel_Name"]:
+            dur[r["Dispatch_Id"]] = (r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    cnt = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if r["Dispatch_Id"] in dur:
+            cnt.setdefault(r["Dispatch_Id"], {}).setdefault(r["Counter_Name"], 0.0)
+            cnt[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+    projs = layer_projections(LLAMA65B["d"], LLAMA65B["ffn"])
+    M, rr = 4096, 64
+    order = [("forward", N, K) for _, N, K in projs] + [("dX", N, K) for _, N, K in reversed(projs)]
+    ids = sorted(dur, key=int)
+    out = ["# MFMA utilisation and clock of the fused products (LLaMA-65B layer, 4096 tokens)", "",
+           "Command (GPU, repository root; one counter pass with the kernel trace for the durations):", "",
+           "    " + command, "",
+           "    python bench.py --summarize-mfma <dir>/run_counter_collection.csv <dir>/run_kernel_trace.csv '<command>'", "",
+           "`--pmc-workload` runs one step of the layer (7 forwards, then 7 backwards) and a plain copy.",
+           "Counter values are summed over the 8 XCDs; per launch: clock = (`GRBM_COUNT` / 8) / duration;",
+           "MFMA work = algorithmic flops / 1024 SIMD-cycles; `SQ_VALU_MFMA_BUSY_CYCLES` / MFMA work",
+           "checks that the kernel issues exactly the algorithmic MFMA work; utilisation = MFMA work /",
+           "(1024 SIMDs x clock cycles of the launch).", "",
+           "| product | N x K | duration | clock | MFMA busy / work | MFMA utilisation at that clock | TFLOP/s |",
+           "|---|---|---|---|---|---|---|"]
+    for i, d in enumerate(ids[:len(order)]):
+        kind, N, K = order[i]
+        name, t = dur[d]
+        c = cnt.get(d, {})
+        flops = 2 * M * N * K + (2 * M * N * rr if kind == "forward" else 2 * M * K * rr)
+        work = flops / 1024.0
+        clock = c.get("GRBM_COUNT", 0.0) / 8.0 / t
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        util = work / (1024.0 * clock * t) if clock > 0 else 0.0
+        out.append("| %s | %d x %d | %.1f us | %.2f GHz | %.3f | %.3f | %.0f |" % (
+            kind, N, K, t * 1e6, clock / 1e9, busy / work if work else 0.0, util, flops / t / 1e12))
     print("\n".join(out))
 
 
@@ -428,6 +518,73 @@ def codec_paths(layer, dev, reps=3):
         v["frac_hbm"] = v["GBps"] / PEAK_HBM_GBS
     res["params"] = n_total
     return res
+
+
+def bulk_codec_paths(dev):
+    """The bulk round trip over every weight of 32 LLaMA-7B-shaped decoder layers
+    (6,476,005,376 values, N(0, 0.02) with 1% of the entries scaled by 10), in fp32
+    and in bf16: NF4 quantize of every tensor, double quantization of every absmax
+    vector, then dequantize back to the input's dtype.  Inputs, codes and outputs stay
+    resident (6.5e9 values at fresh addresses, far beyond the Infinity Cache).  One
+    untimed pass first fills the allocator's cache, so that the timed pass allocates
+    nothing; the timed pass is queued behind a sleeping kernel and timed with events
+    between its phases, so the figures are GPU time (host_bound says whether the host
+    still had calls to submit when the sleep ended)."""
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+    from workloads import LLAMA7B, Draw, layer_projections, seed_of
+
+    projs = layer_projections(LLAMA7B["d"], LLAMA7B["ffn"])
+    out = {}
+
+    def round_trip(ws, dtype, ev=None):
+        if ev is not None:
+            ev[0].record()
+        qs = [nf4.nf4_quantize(w) for w in ws]
+        if ev is not None:
+            ev[1].record()
+        dqs = [nf4.nf4_double_quantize(a) for _, a in qs]
+        if ev is not None:
+            ev[2].record()
+        wts = [nf4.NF4Weight(c, q, c2, m, (int(w.shape[0]), int(w.shape[1])))
+               for w, (c, _), (q, c2, m) in zip(ws, qs, dqs)]
+        outs = [nf4.nf4_dequantize(wt, dtype) for wt in wts]
+        if ev is not None:
+            ev[3].record()
+        return qs, dqs, outs
+
+    for dtype, tag, nbytes in ((torch.float32, "fp32", 4), (torch.bfloat16, "bf16", 2)):
+        ws = []
+        for layer in range(LLAMA7B["layers"]):
+            for pi, (name, N, K) in enumerate(projs):
+                ws.append(Draw(seed_of(20, layer, pi), dev).normal((N, K), 0.02, outlier_frac=0.01).to(dtype))
+        n = sum(w.numel() for w in ws)
+        res = round_trip(ws, dtype)                 # untimed: fills the allocator's cache
+        torch.cuda.synchronize()
+        del res
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        gate = torch.cuda.Event()
+        torch.cuda._sleep(int(2e8))               # holds the queue while the calls are submitted
+        gate.record()
+        res = round_trip(ws, dtype, ev)
+        host_bound = gate.query()
+        torch.cuda.synchronize()
+        del res
+        t = [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(3)]
+        b = [n * (nbytes + 0.5 + 4 / 64), n * (4 / 64 + 1 / 64 + 4 / (64 * 256)),
+             n * (NF4_BYTES_PER_PARAM + nbytes)]
+        rec = {}
+        for key, ti, bi in zip(("quantize", "double_quantize", "dequantize"), t, b):
+            rec[key] = dict(GBps=bi / ti / 1e9, ms=ti * 1e3, bytes=bi, frac_hbm=bi / ti / 1e9 / PEAK_HBM_GBS)
+        rec["round_trip"] = dict(GBps=sum(b) / sum(t) / 1e9, ms=sum(t) * 1e3, bytes=sum(b),
+                                 frac_hbm=sum(b) / sum(t) / 1e9 / PEAK_HBM_GBS)
+        rec["params"] = n
+        rec["tensors"] = len(ws)
+        rec["host_bound"] = bool(host_bound)
+        out[tag] = rec
+        del ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def gemv_paths(layer, dev, r, alpha, reps=5):
@@ -639,6 +796,171 @@ def cpu_baseline(layer, alpha, r, tokens):
                        "float64 oracle)" % (tokens, len(layer)))
 
 
+def hbm_ceiling(reps=10):
+    """The streaming ceilings of this GPU's HBM, for context: a linear read, a linear
+    write and a copy over 4 GiB buffers (16-byte accesses, grid-stride, plain and
+    nontemporal, several grid sizes), each timed over `reps` back-to-back launches
+    with one event pair on the current stream.  Prints a markdown table."""
+    import ctypes
+    import torch
+    from bit_nf4_quantized_09_amd.build import PROBE_LIB
+
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit("the probe library is not built (python bit_nf4_quantized_09_amd/build.py)")
+    L = ctypes.CDLL(PROBE_LIB)
+    L.nf4probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.nf4probe_stream.restype = ctypes.c_int
+    nbytes = 4 << 30
+    src = torch.arange(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    names = {0: "read", 1: "write", 2: "copy"}
+    rows = ["| pattern | nontemporal | workgroups | GB/s | % of 8 TB/s |", "|---|---|---|---|---|"]
+    best = {}
+    for kind in (0, 1, 2):
+        for nt in (0, 1):
+            for grid in (1024, 2048, 4096, 8192, 16384):
+                args = (kind, src.data_ptr(), sink.data_ptr() if kind == 0 else dst.data_ptr(), nbytes, grid, nt,
+                        stream)
+                if L.nf4probe_stream(*args) != 0:
+                    raise SystemExit("probe launch failed")
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                t0.record()
+                for _ in range(reps):
+                    L.nf4probe_stream(*args)
+                t1.record()
+                torch.cuda.synchronize()
+                moved = nbytes * (2 if kind == 2 else 1)
+                gbs = moved / (t0.elapsed_time(t1) / 1e3 / reps) / 1e9
+                best[names[kind]] = max(best.get(names[kind], 0.0), gbs)
+                rows.append("| %s | %s | %d | %.0f | %.1f%% |" % (names[kind], "yes" if nt else "no", grid, gbs,
+                                                                   100.0 * gbs / PEAK_HBM_GBS))
+            print("hbm ceiling: %s nontemporal=%d done" % (names[kind], nt), file=sys.stderr, flush=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes / (t0.elapsed_time(t1) / 1e3 / reps) / 1e9
+    rows.append("| copy (torch copy_) | - | - | %.0f | %.1f%% |" % (gbs, 100.0 * gbs / PEAK_HBM_GBS))
+    rows += ["", "best: " + ", ".join("%s %.0f GB/s" % kv for kv in best.items())]
+    print("\n".join(rows), flush=True)
+
+
+def pmc_codec_workload():
+    """For counter runs: one pass of each HBM-bound kernel over the LLaMA-65B layer's
+    seven weights (fp32 and bf16 quantize, double quantization, fp32- and bf16-out
+    dequantize, the few-token forward at M = 1, 4, 16), then a plain copy of COPY_BYTES."""
+    import torch
+    import bit_nf4_quantized_09_amd as nf4
+
+    layer, projs, M, r, alpha = build_layer("llama65b_layer", "cuda:0")
+    absmax = [nf4.nf4_quantize(p["W"])[1] for p in layer]
+    wb = [p["W"].to(torch.bfloat16) for p in layer]
+    torch.cuda.synchronize()
+    for w in wb:
+        nf4.nf4_quantize(w)
+    del wb
+    for a in absmax:
+        nf4.nf4_double_quantize(a)
+    for dt in (torch.float32, torch.bfloat16):
+        for p in layer:
+            nf4.nf4_dequantize(p["Wq"], dt)
+    for m in (1, 4, 16):
+        for p in layer:
+            nf4.qlora_linear_fwd(p["Wq"], p["X"][:m].contiguous(), p["A"], p["B"], alpha)
+    torch.cuda.synchronize()
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("pmc codec workload done", flush=True)
+
+
+def summarize_pmc_codec(fetch_csv, write_csv):
+    """Per-kernel HBM traffic of the counter runs over --pmc-codec-workload, next to the
+    algorithmic bytes of the same dispatches."""
+    from workloads import LLAMA65B, layer_projections
+
+    fetch = _read_counters(fetch_csv, "FETCH_SIZE")
+    write = _read_counters(write_csv, "WRITE_SIZE")
+    is_copy = lambda k: "copy" in k.lower()
+    fc = [v for (d, k), v in fetch.items() if is_copy(k or "")]
+    wc = [v for (d, k), v in write.items() if is_copy(k or "")]
+    if not (fc and wc):
+        raise SystemExit("counter files lack the copy kernel")
+    kf = (COPY_BYTES / 1024.0) / max(fc)
+    kw = (COPY_BYTES / 1024.0) / max(wc)
+    projs = layer_projections(LLAMA65B["d"], LLAMA65B["ffn"])
+    n = sum(N * K for _, N, K in projs)
+    nk = [(N, K) for _, N, K in projs]
+    n1 = n / 64
+    # algorithmic bytes over the workload's dispatches of each kernel (all 7 weights)
+    fams = [
+        ("quantize, fp32 in", lambda k: "k_quantize<unsigned int>" in k, 7, n * (4 + 0.5 + 4 / 64)),
+        ("quantize, bf16 in", lambda k: "k_quantize<unsigned short>" in k, 7, n * (2 + 0.5 + 4 / 64)),
+        ("double quantization: chunk sums", lambda k: "k_pairwise_chunks" in k, 7, n1 * 4),
+        ("double quantization: mean + 8-bit encode", lambda k: "k_dq_encode_mean" in k, 7,
+         n1 * (4 + 1) + n1 / 256 * 4),
+        ("dequantize, fp32 out", lambda k: "k_dequantize<false, false>" in k, 7, n * (NF4_BYTES_PER_PARAM + 4)),
+        ("dequantize, bf16 out", lambda k: "k_dequantize<true, false>" in k, 7, n * (NF4_BYTES_PER_PARAM + 2)),
+        ("few-token forward: part (M = 1, 4, 16)", lambda k: "k_gemv_part" in k, 21,
+         sum(NF4_BYTES_PER_PARAM * N * K + 2 * 64 * (N + K) + 2 * m * K for (N, K) in nk for m in (1, 4, 16))),
+    ]
+    lines = [
+        "# HBM traffic of the codec and few-token kernels, LLaMA-65B layer weights",
+        "",
+        "Commands (GPU, from the repository root; one counter per run):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE -d pmc_fetch -o run --output-format csv -- python bench.py --pmc-codec-workload",
+        "    rocprofv3 --pmc WRITE_SIZE -d pmc_write -o run --output-format csv -- python bench.py --pmc-codec-workload",
+        "    python bench.py --summarize-pmc-codec <pmc_fetch>/run_counter_collection.csv "
+        "<pmc_write>/run_counter_collection.csv",
+        "",
+        "The workload makes one pass of each kernel over the seven weights (%.4g values); the "
+        "few-token forward runs once per weight at M = 1, 4 and 16. Calibration: a plain device "
+        "copy of %d MiB in the same run reads %.1f KiB by FETCH_SIZE and writes %.1f KiB by "
+        "WRITE_SIZE, factors %.4f (fetch) and %.4f (write)." % (n, COPY_BYTES >> 20, max(fc), max(wc), kf, kw),
+        "",
+        "| kernel | dispatches | fetched bytes | written bytes | traffic | algorithmic bytes | traffic / algorithmic |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    def last(table, pred, count):
+        # the workload's own dispatches are the last `count` of each kernel (the layer's
+        # set-up quantizes the weights first)
+        v = sorted((int(d), x) for (d, k), x in table.items() if pred(k or ""))
+        return [x for _, x in v[-count:]]
+
+    for label, pred, expect, alg in fams:
+        fv = last(fetch, pred, expect)
+        wv = last(write, pred, expect)
+        if not fv or not wv:
+            lines.append("| %s | 0 | - | - | - | %.4g | - |" % (label, alg))
+            continue
+        fb = sum(fv) * 1024.0 * kf
+        wb_ = sum(wv) * 1024.0 * kw
+        lines.append("| %s | %d | %.4g | %.4g | %.4g | %.4g | %.3f |" % (
+            label, len(fv), fb, wb_, fb + wb_, alg, (fb + wb_) / alg))
+        if len(fv) != expect:
+            lines.append("| (%s: %d dispatches found, %d expected) | | | | | | |" % (label, len(fv), expect))
+    red_f = last(fetch, lambda k: "k_gemv_reduce" in k, 21)
+    red_w = last(write, lambda k: "k_gemv_reduce" in k, 21)
+    if red_f and red_w:
+        lines.append("| few-token forward: slice reduce | %d | %.4g | %.4g | %.4g | - | - |" % (
+            len(red_f), sum(red_f) * 1024.0 * kf, sum(red_w) * 1024.0 * kw,
+            sum(red_f) * 1024.0 * kf + sum(red_w) * 1024.0 * kw))
+    lines += ["", "kernel_source_sha256 (codec.hip, gemv.hip, nf4_common.h, bufio.h) = %s"
+              % kernel_source_hash(["codec.hip", "gemv.hip", "nf4_common.h", "bufio.h"])]
+    print("\n".join(lines))
+
+
 def pmc_workload(args):
     """One untimed step of the workload, then a plain device copy of COPY_BYTES."""
     import torch
@@ -659,8 +981,14 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
+        return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_pmc_codec:
+        summarize_pmc_codec(*args.summarize_pmc_codec)
         return
     if args.summarize_gemv_trace:
         summarize_gemv_trace(args.summarize_gemv_trace)
@@ -682,11 +1010,24 @@ def main():
     if args.pmc_workload:
         pmc_workload(args)
         return
+    if args.pmc_codec_workload:
+        pmc_codec_workload()
+        return
+    if args.hbm_ceiling:
+        hbm_ceiling()
+        return
     if args.codebooks_only:
         print(json.dumps({"codebooks": codebook_paths(dev)}), flush=True)
         return
+    if args.gemv_only:
+        layer, projs, M, r, alpha = build_layer(args.workload, dev)
+        print(json.dumps({"gemv": gemv_paths(layer, dev, r, alpha)}), flush=True)
+        return
     if args.loftq_only:
         print(json.dumps({"loftq": loftq_paths(dev)}), flush=True)
+        return
+    if args.bulk_codec_only:
+        print(json.dumps({"codec_llama7b_32_layers": bulk_codec_paths(dev)}), flush=True)
         return
     if args.adamw_only:
         from workloads import LLAMA65B, layer_projections
@@ -738,8 +1079,11 @@ def main():
                                        "frac": round(kb["achieved"] / PEAK_BF16_TFLOPS, 4),
                                        "avg_us": round(kb["avg_us"], 2)}},
     }
+    line["peaks"] = {"bf16_tflops_used": PEAK_BF16_TFLOPS, "hbm_gbps_used": PEAK_HBM_GBS,
+                     "source": "MI355X published dense figures", "rocminfo": rocminfo_peaks()}
     if not args.no_paths and args.workload != "tiny":
-        line["paths"] = {"codec": codec_paths(layer, dev), "gemv": gemv_paths(layer, dev, r, alpha),
+        line["paths"] = {"codec": codec_paths(layer, dev), "codec_llama7b_32_layers": bulk_codec_paths(dev),
+                         "gemv": gemv_paths(layer, dev, r, alpha),
                          "adamw": adamw_paths(layer, dev, r), "codebooks": codebook_paths(dev),
                          "variants": variant_paths(layer, alpha, fwd_flops + bwd_flops),
                          "loftq": loftq_paths(dev)}

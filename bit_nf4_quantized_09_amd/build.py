@@ -9,6 +9,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libqlora_nf4.so")
+PROBE_SOURCE = "hbm_probe.hip"      # the HBM ceiling probes: a library of their own
+PROBE_LIB = os.path.join(OUT_DIR, "libnf4_hbm_probe.so")
 SOURCES = ["api.hip", "codec.hip", "lora.hip", "fused.hip", "gemv.hip", "adamw.hip", "codebook.hip", "lowrank.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -35,8 +37,12 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
+    probe_obj = objs.pop()
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", probe_obj, "-o", tmp], check=True)
+    os.replace(tmp, PROBE_LIB)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:
