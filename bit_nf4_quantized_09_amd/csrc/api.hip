@@ -421,9 +421,10 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
                                    Tb, part, table(), hs);
         return hip_status(e, "qlora_linear_fwd (gemv)");
     }
-    // T = X A^T (kept for the backward) and s*T for the epilogue of the fused product
+    // T = X A^T (kept for the backward) and s*T for the epilogue of the fused product; the
+    // same pass writes X in the fused product's fragment order
     e = nf4::launch_lora_gemm(x, false, (const uint16_t*)A, false, M, r, v.cols, part, 1.0f, Tb,
-                              false, false, Ts, s, hs);
+                              false, false, Ts, s, hs, xpk, true);
     if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
     if (v.absmax) {
         c1 = (float*)v.absmax;            // plain constants: read as they are
@@ -431,8 +432,6 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
         e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
         if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (constants)");
     }
-    e = nf4::launch_pack_a(x, M, v.cols, xpk, hs);
-    if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (pack)");
     e = nf4::launch_fused_fwd(v, c1, xpk, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, part, table(), hs);
     return hip_status(e, "qlora_linear_fwd (gemm)");
 }
@@ -495,9 +494,10 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     uint16_t* gpk = (uint16_t*)((char*)workspace + 2 * rb + cb + pb);
     hipError_t e;
     if (M > 0) {
-        // Us = s dY B   (B stored N x r: contraction-strided)
+        // Us = s dY B   (B stored N x r: contraction-strided); with dX wanted, the same pass
+        // writes dY in the fused product's fragment order
         e = nf4::launch_lora_gemm(g, false, bl, true, M, r, v.rows, part, s, Us, false, false,
-                                  nullptr, 0.0f, hs);
+                                  nullptr, 0.0f, hs, dX ? gpk : nullptr);
         if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (U)");
         if (!Tb) {
             uint16_t* Tw = (uint16_t*)((char*)workspace + rb);
@@ -513,8 +513,6 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
                 if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (constants)");
                 c1b = c1;
             }
-            e = nf4::launch_pack_a(g, M, v.rows, gpk, hs);
-            if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (pack)");
             e = nf4::launch_fused_bwd_dx(v, c1b, gpk, M, Us, al, r, (uint16_t*)dX, part, table(), hs);
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dX)");
         }

@@ -16,12 +16,16 @@
 // of contraction per pipeline step.
 //
 // The A operand (X forward, dY backward) is private to a wave, so it goes from global
-// memory straight into MFMA operand registers and never through LDS.  A pre-pass
-// (k_pack_a) lays the operand out in fragment order: for each 512-row token tile and
+// memory straight into MFMA operand registers and never through LDS.  The rank-r product
+// that reads the operand anyway (T = X A^T forward, U = dY B backward: k_skinny in
+// lora.hip) also writes it in fragment order: for each 512-row token tile and
 // 64-value contraction step, 64 KB holding, per wave and MFMA fragment (row tile i,
 // substep s), the 16 bytes of each of the 64 lanes (row 128 w + 32 i + l % 32, contraction
 // values 16 s + 8 (l / 32) .. + 7) contiguously, so that every fragment load is one
 // coalesced kilobyte, with zeros past the last token row and past the contraction's end.
+// In the forward, every 16-byte piece (8 contraction values) holds its values in the order
+// 0, 2, 4, 6, 1, 3, 5, 7, the order in which the W' decode produces them without its last
+// four byte permutes (decode8<true>); a contraction is blind to the order its pairs come in.
 // (Loaded from the row-major operand, each lane of a fragment load would touch its own
 // row: four times the cache lines per load instruction.)  Two register sets of A fragments
 // (steps of even and odd index) are reloaded two steps ahead, each fragment as soon as its
@@ -75,7 +79,7 @@ struct FusedArgs {
     const uint8_t* codes;
     const float* c1;          // decoded first-level constant of every 64-block (N * K/64)
     int64_t N, K;             // frozen weight rows (out features) and columns (in features)
-    const uint16_t* A;        // X [M x K] (forward) or dY [M x N] (backward), packed by k_pack_a
+    const uint16_t* A;        // X [M x K] (forward) or dY [M x N] (backward), in fragment order
     int64_t M;
     const uint16_t* Rk;       // forward: s*T [M x r]; backward: s*U [M x r]
     const uint16_t* Lr;       // forward: B [N x r];   backward: A [r x K]
@@ -169,7 +173,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     const uint32_t flip = pair_code_flip(part);
     auto decode_chunk = [&](uint8_t* sW, const ScaledTable& st, const BlockCodes& bc, int c) {
         uint32_t o[4];
-        decode8(st, word(bc, c) ^ flip, o);
+        decode8<!BWD>(st, word(bc, c) ^ flip, o);
         *reinterpret_cast<uint4*>(sW + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
     };
 
@@ -402,51 +406,6 @@ void k_fused(FusedArgs a, Nf4Table tab) {
 }
 
 // ---------------------------------------------------------------------------
-// Fragment-order packing of the fused products' A operand (X forward, dY backward: M x ld
-// bf16, row-major, ld % 8 == 0).  Block (tm, st), at (tm steps + st) * 64 KB of dst, holds
-// token rows 512 tm .. + 511 and contraction values 64 st .. + 63: chunk q (16 bytes) =
-// a_pack_chunk(row, c) for the 16-byte chunk c of the tile's row, zeros past M and past ld.
-// One workgroup per block: the tile is read row-major (coalesced) into LDS with XOR-swizzled
-// chunks, then written out in chunk order (coalesced); every LDS pass is free of bank
-// conflicts (16 consecutive rows read one chunk position; a write covers 2 rows x 8 chunks).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_pack_a(const uint16_t* __restrict__ src, int64_t M, int64_t ld,
-                                                int64_t steps, uint16_t* __restrict__ dst) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t ptile[];   // 512 rows x 128 bytes
-    const int64_t blk = blockIdx.x, tm = blk / steps, st = blk % steps;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int row = (tid >> 3) + 32 * j, c = tid & 7;
-        const int64_t gm = tm * FUSED_TM + row, gk = st * 64 + 8 * c;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (gm < M && gk < ld) v = *reinterpret_cast<const uint4*>(src + gm * ld + gk);
-        *reinterpret_cast<uint4*>(ptile + tile_off(row, c)) = v;
-    }
-    __syncthreads();
-    uint4* out = reinterpret_cast<uint4*>(dst + blk * (A_BLOCK_BYTES / 2));
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int q = tid + 256 * j;
-        out[q] = *reinterpret_cast<const uint4*>(ptile + tile_off(a_pack_row(q), a_pack_col(q)));
-    }
-}
-
-hipError_t launch_pack_a(const uint16_t* src, int64_t M, int64_t ld, uint16_t* dst, hipStream_t st) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_pack_a, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           A_BLOCK_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const int64_t steps = (ld + 63) / 64, tiles = (M + FUSED_TM - 1) / FUSED_TM;
-    if (steps * tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_pack_a, dim3((unsigned)(steps * tiles)), dim3(256), A_BLOCK_BYTES, st, src, M, ld, steps,
-                       dst);
-    return hipGetLastError();
-}
-
 FusedEvents& fused_events() {
     static thread_local FusedEvents ev;
     return ev;

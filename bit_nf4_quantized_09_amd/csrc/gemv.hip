@@ -107,8 +107,8 @@ constexpr int gv_lds_bytes(int MT) { return MT * (GV_RB * 128 + 16); }
 // about as many bytes as a weight workgroup.  Straight-line code from the first
 // request to the last wait, so that every wait names exactly the requests it needs.
 template <int RB, int MT, bool ADAPTER, bool PLAIN>
-__device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& tab, int64_t group,
-                                               uint32_t* s_pair, float* s_e4m3) {
+__device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& tab, int64_t slice,
+                                               int64_t group, uint32_t* s_pair, float* s_e4m3) {
     constexpr int CP = GV_CP;
     extern __shared__ __attribute__((aligned(16))) uint8_t gv_lds[];
     constexpr int NT = 64 * GV_WV;                     // threads
@@ -121,7 +121,6 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t KB = a.K >> 6;
-    const int64_t slice = blockIdx.x;
     const int64_t b0 = slice * RB;                      // first block of the slice
     const int nb = KB - b0 < RB ? (int)(KB - b0) : RB;  // blocks of the slice inside the row
     const int nl = lane & 15, g = lane >> 4;
@@ -326,17 +325,21 @@ __device__ __forceinline__ void gemv_part_body(const GvArgs& a, const Nf4Table& 
     }
 }
 
-// grid (slice, row group): the slices of one row group are dispatched together, so the
-// workgroups in flight read whole rows of codes (long runs within one DRAM page);
-// the adapter row groups come first.
+// grid: one dimension, workgroup b = (row group) x slices + slice; the slices of one row
+// group are dispatched together, so the workgroups in flight read whole rows of codes
+// (long runs within one DRAM page); the adapter row groups come first.  (One dimension
+// holds the 2^22 / 64 row groups of the longest weight, which the second grid dimension
+// of a launch could not.)
 template <int RB, int MT, bool PLAIN>
 __global__ __launch_bounds__(64 * GV_WV) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void k_gemv_part(GvArgs a, Nf4Table tab) {
     __shared__ __attribute__((aligned(16))) uint32_t s_pair[256 * GV_CP];   // code byte -> two bf16 levels
     __shared__ float s_e4m3[256];                      // 8-bit constant -> E4M3 value
     const int64_t nag = (a.r + GV_AROWS - 1) / GV_AROWS;
-    if ((int64_t)blockIdx.y < nag) gemv_part_body<RB, MT, true, PLAIN>(a, tab, blockIdx.y, s_pair, s_e4m3);
-    else gemv_part_body<RB, MT, false, PLAIN>(a, tab, (int64_t)blockIdx.y - nag, s_pair, s_e4m3);
+    const int64_t nsl = ((a.K >> 6) + RB - 1) / RB;      // slices of a row (gemv_slices)
+    const int64_t b = blockIdx.x, slice = b % nsl, group = b / nsl;
+    if (group < nag) gemv_part_body<RB, MT, true, PLAIN>(a, tab, slice, group, s_pair, s_e4m3);
+    else gemv_part_body<RB, MT, false, PLAIN>(a, tab, slice, group - nag, s_pair, s_e4m3);
 }
 
 // k_gemv_reduce<ROWS, NO, NT>: workgroup of ROWS weight rows; thread (row n = n0 + tid %
@@ -445,13 +448,13 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
     GvArgs ga{W.codes, W.q, W.c2, W.mean, W.rows, W.cols, X, (int)M, Al, Bl, r, s, part, Y, T, W.absmax};
     const bool small = M <= 4;
     const int64_t wrows = small ? gv_rows(4) : gv_rows(16);
-    dim3 g1((unsigned)slices, (unsigned)((r + GV_AROWS - 1) / GV_AROWS + (W.rows + wrows - 1) / wrows));
+    dim3 g1((unsigned)(slices * ((r + GV_AROWS - 1) / GV_AROWS + (W.rows + wrows - 1) / wrows)));
     // reduce: 32 rows x 8 token groups (one output per thread) for up to 4 tokens,
     // 64 rows x 4 token groups (four outputs) above
     const int64_t rrows = small ? 32 : 64;
     dim3 g2((unsigned)((W.rows + rrows - 1) / rrows > 0 ? (W.rows + rrows - 1) / rrows : 1));
     return with_events(st, [&] {
-        if (g1.x > 0 && g1.y > 0) {
+        if (g1.x > 0) {
             const bool plain = W.absmax != nullptr;
             hipError_t e = small ? (plain ? launch_gemv_part<4, true>(g1, ga, tab, st)
                                           : launch_gemv_part<4, false>(g1, ga, tab, st))

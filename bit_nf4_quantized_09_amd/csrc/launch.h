@@ -38,11 +38,16 @@ hipError_t launch_dequantize(const WeightView& W, void* out, bool out_bf16, cons
 // b_trans == false: Bop^T is row-major [Nc x P] (ldb = P); true: Bop stored [P x Nc] (ldb = Nc).
 // C is bf16 or fp32, stored [Mc x Nc] or (c_trans) [Nc x Mc]; C2, if given, receives
 // bf16(scale2 * sum) in the same layout.  `part` is fp32 workspace of
-// skinny_partial_bytes(Mc, Nc, P) bytes for the split-contraction slices.
+// skinny_partial_bytes(Mc, Nc, P) bytes for the split-contraction slices.  `pack`, if given
+// (A direct only), receives A in the fused product's fragment order (tile_map.h:
+// 512-row token tiles x 64-value steps, ld = P), written from the tiles the product stages
+// anyway; with pack_even_odd each 16-byte piece holds its 8 values in the order 0, 2, 4, 6,
+// 1, 3, 5, 7 (the order of the forward product's decoded weights).
 size_t skinny_partial_bytes(int64_t Mc, int64_t Nc, int64_t P);
 hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, bool b_trans,
                             int64_t Mc, int64_t Nc, int64_t P, float* part, float scale, void* C,
-                            bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s);
+                            bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s,
+                            uint16_t* pack = nullptr, bool pack_even_odd = false);
 
 // ---- profiling hook: events around the next fused launch on this thread ----
 struct FusedEvents {
@@ -68,9 +73,6 @@ inline hipError_t with_events(hipStream_t st, F&& fn) {
 }
 
 // ---- fused dequant products -------------------------------------------------
-// The A operand (X forward, dY backward; M x ld bf16, ld % 8 == 0) in fragment order, the
-// layout of tile_map.h, ceil(M/512) * ceil(ld/64) * A_BLOCK_BYTES bytes at dst.
-hipError_t launch_pack_a(const uint16_t* src, int64_t M, int64_t ld, uint16_t* dst, hipStream_t st);
 // Y = X W'^T + Ts B^T, Ts = s T   (MFMA GEMM, dequantization fused into the W operand load).
 // c1: the decoded first-level constants of W (launch_double_dequantize), one per 64-block.
 hipError_t launch_fused_fwd(const WeightView& W, const float* c1, const uint16_t* Xpk, int64_t M, const uint16_t* Ts,

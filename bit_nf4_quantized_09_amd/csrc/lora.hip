@@ -80,7 +80,8 @@ template <bool ATR, bool BTR>
 __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ A,
                                                 const uint16_t* __restrict__ B, int64_t Mc,
                                                 int64_t Nc, int64_t P, int64_t chunks_per_slice,
-                                                float* __restrict__ part) {
+                                                float* __restrict__ part, uint16_t* __restrict__ pack,
+                                                bool pack_even_odd) {
     using St = SkStage<ATR, BTR>;
     constexpr int NR = St::NR;
     constexpr bool DD = !ATR && !BTR;
@@ -181,6 +182,24 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ A,
             acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
         }
     };
+    // The A tile of a chunk, staged in LDS, in the fused product's fragment order (tile_map.h):
+    // sub-block (token tile i0 / 512, contraction step c, row quarter (i0 / 128) % 4), whose
+    // 1024 16-byte pieces this workgroup writes contiguously, each piece's 8 values in the
+    // even/odd order of the forward product's decoded weights when pack_even_odd is set.
+    // Only the first column tile writes it; rows past Mc and contraction values past P are
+    // the zeros staged for them.
+    uint16_t* const pk = (ATR || blockIdx.x != 0) ? nullptr : pack;
+    auto write_pack = [&](int stage, int64_t c) {
+        const uint8_t* sA = lds + stage * SK_STAGE;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(pk) + ((i0 >> 9) * nchunks + c) * (int64_t)A_BLOCK_BYTES +
+                       ((i0 >> 7) & 3) * (A_BLOCK_BYTES / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + 256 * i;
+            const uint4 v = *reinterpret_cast<const uint4*>(sA + lds_off(a_pack_row(q), a_pack_col(q)));
+            *reinterpret_cast<uint4*>(dst + 16 * q) = pack_even_odd ? even_odd8(v) : v;
+        }
+    };
     St s0, s1, s2;
     // step k (chunk c0 + k) with register sets cur (chunk k's, already in LDS) and nx (chunk
     // k+1's): write nx to the free stage, request chunk k+3 into cur, multiply stage k & 1
@@ -188,6 +207,7 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ A,
         store(nx, (int)((k + 1) & 1));
         load(cur, c0 + k + 3);
         compute((int)(k & 1));
+        if (pk) write_pack((int)(k & 1), c0 + k);
         __syncthreads();
     };
 
@@ -280,8 +300,10 @@ size_t skinny_partial_bytes(int64_t Mc, int64_t Nc, int64_t P) {
 
 hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, bool b_trans,
                             int64_t Mc, int64_t Nc, int64_t P, float* part, float scale, void* C,
-                            bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s) {
+                            bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s,
+                            uint16_t* pack, bool pack_even_odd) {
     if (Mc == 0 || Nc == 0) return hipSuccess;
+    if (pack && a_trans) return hipErrorInvalidValue;
     // per-lane buffer offsets are 32-bit: a direct operand spans 128 rows of its leading
     // dimension P, a transposed one 64 contraction rows of its leading dimension
     if ((!a_trans || !b_trans) && P >= ((int64_t)1 << 22)) return hipErrorInvalidValue;
@@ -290,15 +312,18 @@ hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, 
     int S;
     int64_t cps;
     skinny_plan(Mc, Nc, P, &S, &cps);
-    dim3 grid((unsigned)((Nc + SK_BN - 1) / SK_BN), (unsigned)((Mc + SK_BM - 1) / SK_BM), (unsigned)S);
+    // with a packed copy of A to write, the row tiles cover whole 512-row token tiles, so
+    // that the rows past Mc are written too (as zeros)
+    const int64_t row_tiles = pack ? ((Mc + 511) / 512) * (512 / SK_BM) : (Mc + SK_BM - 1) / SK_BM;
+    dim3 grid((unsigned)((Nc + SK_BN - 1) / SK_BN), (unsigned)row_tiles, (unsigned)S);
     if (!a_trans && !b_trans)
-        hipLaunchKernelGGL((k_skinny<false, false>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part);
+        hipLaunchKernelGGL((k_skinny<false, false>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part, pack, pack_even_odd);
     else if (!a_trans && b_trans)
-        hipLaunchKernelGGL((k_skinny<false, true>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part);
+        hipLaunchKernelGGL((k_skinny<false, true>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part, pack, pack_even_odd);
     else if (a_trans && b_trans)
-        hipLaunchKernelGGL((k_skinny<true, true>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part);
+        hipLaunchKernelGGL((k_skinny<true, true>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part, nullptr, false);
     else
-        hipLaunchKernelGGL((k_skinny<true, false>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part);
+        hipLaunchKernelGGL((k_skinny<true, false>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part, nullptr, false);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = Mc * Nc;

@@ -219,35 +219,44 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
         double dmax = 0.0;
         for (int i = 0; i < l; ++i) dmax = fmax(dmax, G[i * LD + i]);
         const double tol = 1e-12 * dmax;
-        // left-looking Cholesky, column by column; L overwrites the lower triangle of G
+        // Cholesky, right-looking: at step j the pivot, then column j, then the rank-1
+        // update of the trailing lower triangle; every entry receives its products in
+        // ascending step order, as in the column-by-column form.  L overwrites the lower
+        // triangle of G.
         for (int j = 0; j < l; ++j) {
             if (tid == 0) {
-                double d = G[j * LD + j];
-                for (int k = 0; k < j; ++k) d -= G[j * LD + k] * G[j * LD + k];
-                s_red[0] = d > tol && d > 0.0 ? sqrt(d) : 0.0;
+                const double d = G[j * LD + j];
+                const double ljj = d > tol && d > 0.0 ? sqrt(d) : 0.0;
+                G[j * LD + j] = ljj;
+                s_red[0] = ljj;
             }
             __syncthreads();
             const double ljj = s_red[0];
-            for (int i = j + 1 + tid; i < l; i += 256) {
-                double v = G[i * LD + j];
-                for (int k = 0; k < j; ++k) v -= G[i * LD + k] * G[j * LD + k];
-                G[i * LD + j] = ljj > 0.0 ? v / ljj : 0.0;
+            for (int i = j + 1 + tid; i < l; i += 256) G[i * LD + j] = ljj > 0.0 ? G[i * LD + j] / ljj : 0.0;
+            __syncthreads();
+            const int t = l - j - 1;
+            for (int e = tid; e < t * t; e += 256) {
+                const int i = j + 1 + e / t, k = j + 1 + e % t;
+                if (k <= i) G[i * LD + k] -= G[i * LD + j] * G[k * LD + j];
             }
             __syncthreads();
-            if (tid == 0) G[j * LD + j] = ljj;
-            __syncthreads();
         }
-        // Linv (lower) column by column by forward substitution, into V: thread c solves
-        // L x = e_c (rows with a zero pivot give x = 0)
-        for (int c = tid; c < l; c += 256) {
-            for (int i = 0; i < l; ++i) {
-                double v = (i == c) ? 1.0 : 0.0;
-                for (int k = c; k < i; ++k) v -= G[i * LD + k] * V[k * LD + c];
-                const double lii = G[i * LD + i];
-                V[i * LD + c] = (i < c || lii == 0.0) ? 0.0 : v / lii;
-            }
-        }
+        // Linv = L^-1 (lower) into V, by rows: at step j row j is divided by its pivot
+        // (a zero pivot gives a zero row), then eliminated from the rows below; each entry
+        // receives its products in ascending order of j, then its one division
+        for (int e = tid; e < l * l; e += 256) V[(e / l) * LD + e % l] = (e / l == e % l) ? 1.0 : 0.0;
         __syncthreads();
+        for (int j = 0; j < l; ++j) {
+            const double ljj = G[j * LD + j];
+            for (int c = tid; c < l; c += 256) V[j * LD + c] = (j < c || ljj == 0.0) ? 0.0 : V[j * LD + c] / ljj;
+            __syncthreads();
+            const int t = l - j - 1, w = j + 1;
+            for (int e = tid; e < t * w; e += 256) {
+                const int i = j + 1 + e / w, c = e % w;
+                V[i * LD + c] -= G[i * LD + j] * V[j * LD + c];
+            }
+            __syncthreads();
+        }
         // Minv = Linv^T
         for (int e = tid; e < l * l; e += 256) {
             const int i = e / l, j = e % l;

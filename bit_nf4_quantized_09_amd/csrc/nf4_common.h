@@ -174,7 +174,10 @@ __device__ __forceinline__ void lookup4(const ScaledTable& s, uint32_t sel, uint
 // spreads one bit per byte lane into a full byte mask in a single instruction.
 constexpr uint32_t SIGN_SPREAD = 0x090B080Au;
 
-// 8 codes (nibble i = element i) -> 8 bf16 in element order (4 registers).
+// 8 codes (nibble i = element i) -> 8 bf16 in element order (4 registers), or with
+// EVEN_ODD in the order 0, 2, 4, 6, 1, 3, 5, 7 (a product whose other operand is permuted
+// the same way within every 8-value chunk contracts to the same sum).
+template <bool EVEN_ODD>
 __device__ __forceinline__ void decode8(const ScaledTable& s, uint32_t w, uint32_t out[4]) {
     const uint32_t ev = w & 0x0F0F0F0Fu;           // elements 0,2,4,6
     const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;    // elements 1,3,5,7
@@ -189,10 +192,25 @@ __device__ __forceinline__ void decode8(const ScaledTable& s, uint32_t w, uint32
     const uint32_t e23 = __builtin_amdgcn_perm(ehi, elo, 0x07030602u);
     const uint32_t o01 = __builtin_amdgcn_perm(ohi, olo, 0x05010400u);
     const uint32_t o23 = __builtin_amdgcn_perm(ohi, olo, 0x07030602u);
-    out[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);   // elements 0,1
-    out[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);   // 2,3
-    out[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);   // 4,5
-    out[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);   // 6,7
+    if constexpr (EVEN_ODD) {
+        // elements in the order 0, 2, 4, 6, 1, 3, 5, 7 (four byte permutes fewer)
+        out[0] = e01;
+        out[1] = e23;
+        out[2] = o01;
+        out[3] = o23;
+    } else {
+        out[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);   // elements 0,1
+        out[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);   // 2,3
+        out[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);   // 4,5
+        out[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);   // 6,7
+    }
+}
+
+// The within-chunk order of decode8<true>, applied to 8 bf16 values (16 bytes, element
+// order): the even elements, then the odd ones.
+__device__ __forceinline__ uint4 even_odd8(uint4 v) {
+    return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                      __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
 }
 
 }  // namespace nf4

@@ -21,7 +21,7 @@ constexpr int XCD_CUS = 32;             // compute units per XCD (256 / 8)
 constexpr int GROUP_M = 4;              // token tiles per group of the tile order
 constexpr int MAX_SPLIT = 4;            // pieces per tail tile at most
 // Fragment-order layout of the fused products' A operand (X forward, dY backward), written
-// by k_pack_a and read by k_fused: one 64 KB block per (512-row token tile, 64-value step),
+// by k_skinny (lora.hip) and read by k_fused: one 64 KB block per (512-row token tile, 64-value step),
 // 4096 chunks of 16 bytes.  Chunk q = 1024 w + 64 (4 i + s) + l is the 16 bytes lane l of
 // wave w loads for MFMA fragment (row tile i, substep s): tile row 128 w + 32 i + l % 32,
 // 16-byte column 2 s + l / 32 of the step's 128 bytes (contraction values 16 s + 8 (l / 32)

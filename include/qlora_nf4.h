@@ -37,6 +37,12 @@
  *     X, A, B, dY, Y, T, dX, out) must be 16-byte aligned.
  *   - Concurrency: calls are reentrant; concurrent calls on different
  *     streams must not share output buffers or workspaces.
+ *   - Narrowed from a broader interface sketch: the block sizes are fixed at
+ *     64 (first level) and 256 (second level), the values QLoRA uses, so
+ *     nf4_weight carries no block-size fields; it carries absmax instead, for
+ *     the variant without double quantization; and four error statuses
+ *     (argument, unsupported, workspace, HIP) stand for finer per-cause codes,
+ *     the cause being spelled out by nf4_last_error().
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H

@@ -85,6 +85,32 @@ def test_gemv_ranks_and_long_rows(M, N, K, r):
     _run(W, X, A, B, dY, alpha=16.0)
 
 
+@pytest.mark.parametrize("M", [1, 5])
+def test_gemv_second_level_groups(M):
+    # an odd number of blocks per row (17) puts block pairs across the boundaries of the
+    # 256-block groups of second-level constants; rows scaled over four decades give the
+    # groups different constants, and every output row is held to the tolerance on its
+    # own, so a block decoded with its neighbouring group's constant shows
+    N, K, r = 256, 1088, 16
+    W, X, A, B, dY = (t.to(DEV) for t in linear_inputs(N, K, M, r, seed=seed_of(14, M)))
+    g = torch.Generator().manual_seed(seed_of(15, M))
+    scale = (10.0 ** (4.0 * torch.rand(N, 1, generator=g) - 2.0)).to(DEV)
+    W = W * scale
+    B = (B.float() * 1e-2).to(torch.bfloat16)      # keep the rank-r term below the smallest rows
+    print("gemv groups", N, K, M, flush=True)
+    ref = oracle_weight(W.cpu())
+    Wq = nf4.quantize_weight(W)
+    Y, T = nf4.qlora_linear_fwd(Wq, X, A, B, 16.0)
+    torch.cuda.synchronize()
+    Yr, Tr = oracle.qlora_linear_fwd(ref["Wd"], host_f32(X), host_f32(A), host_f32(B), 16.0)
+    err = np.abs(to_np(Y) - Yr).max(axis=0)
+    # the natural size of output row n: the norm of its dequantized weight row (X ~ N(0, 1))
+    row_norm = np.linalg.norm(ref["Wd"], axis=1)
+    worst = int(np.argmax(err / row_norm))
+    assert err[worst] <= 2e-2 * row_norm[worst], "row %d: error %.3e, row norm %.3e" % (
+        worst, err[worst], row_norm[worst])
+
+
 def test_gemv_and_gemm_paths_agree():
     # 16 tokens run through the dequant-GEMV; the same 16 plus one more run through the GEMM
     N, K, r = 520, 1024, 64
@@ -227,6 +253,23 @@ def test_longest_operand_rows(N, K):
     M = 512
     W, X, A, B, dY = linear_inputs(N, K, M, 8, seed=seed_of(24, N, K), device=DEV)
     _run(W, X, A, B, dY, alpha=16.0, rows=_sampled_rows(M, 8, 3, band=128))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("N,K", [(8, (1 << 22) - 64), ((1 << 22) - 8, 64)])
+def test_gemv_longest_rows(M, N, K):
+    # the few-token forward at the largest N and K the ABI accepts: token rows of 2^22 - 64
+    # values (every byte offset below 2^31), and rows of a single block (one block pair
+    # whose second block lies past the row); every output compared
+    W, X, A, B, dY = linear_inputs(N, K, M, 8, seed=seed_of(25, N, K, M), device=DEV)
+    print("gemv longest", N, K, M, flush=True)
+    ref = oracle_weight(W.cpu())
+    Wq = nf4.quantize_weight(W)
+    Y, T = nf4.qlora_linear_fwd(Wq, X, A, B, 16.0)
+    torch.cuda.synchronize()
+    Yr, Tr = oracle.qlora_linear_fwd(ref["Wd"], host_f32(X), host_f32(A), host_f32(B), 16.0)
+    assert_close("Y", to_np(Y), Yr)
+    assert_close("T", to_np(T), Tr)
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
