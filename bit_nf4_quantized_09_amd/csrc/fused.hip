@@ -23,9 +23,12 @@
 // substep s), the 16 bytes of each of the 64 lanes (row 128 w + 32 i + l % 32, contraction
 // values 16 s + 8 (l / 32) .. + 7) contiguously, so that every fragment load is one
 // coalesced kilobyte, with zeros past the last token row and past the contraction's end.
-// In the forward, every 16-byte piece (8 contraction values) holds its values in the order
-// 0, 2, 4, 6, 1, 3, 5, 7, the order in which the W' decode produces them without its last
-// four byte permutes (decode8<true>); a contraction is blind to the order its pairs come in.
+// The W' decode leaves each 8-value chunk in the order 0, 2, 4, 6, 1, 3, 5, 7, which saves
+// its last four byte permutes (decode8<true>).  In the forward the chunk runs along the
+// contraction, and every 16-byte piece of the packed X holds its 8 values in the same order (a
+// contraction is blind to the order its pairs come in).  In the backward it runs along the
+// output features: the rank-r operand A is staged in the same order, and the stores put each
+// accumulator column back at its feature.
 // (Loaded from the row-major operand, each lane of a fragment load would touch its own
 // row: four times the cache lines per load instruction.)  Two register sets of A fragments
 // (steps of even and odd index) are reloaded two steps ahead, each fragment as soon as its
@@ -173,7 +176,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     const uint32_t flip = pair_code_flip(part);
     auto decode_chunk = [&](uint8_t* sW, const ScaledTable& st, const BlockCodes& bc, int c) {
         uint32_t o[4];
-        decode8<!BWD>(st, word(bc, c) ^ flip, o);
+        decode8<true>(st, word(bc, c) ^ flip, o);
         *reinterpret_cast<uint4*>(sW + w_off(c)) = make_uint4(o[0], o[1], o[2], o[3]);
     };
 
@@ -336,7 +339,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 const int j = qi / (TN / 8), c = qi % (TN / 8);   // rank row j, 8 features per chunk
                 const int64_t gk = c0 + 8 * c;
                 uint4 v = make_uint4(0, 0, 0, 0);
-                if (rc + j < a.r && gk < a.K) v = *reinterpret_cast<const uint4*>(a.Lr + (int64_t)(rc + j) * a.K + gk);
+                if (rc + j < a.r && gk < a.K) v = even_odd8(*reinterpret_cast<const uint4*>(a.Lr + (int64_t)(rc + j) * a.K + gk));
                 *reinterpret_cast<uint4*>(lds + wt_off<TN>(j, 8 * c)) = v;
             } else {
                 const int row = qi >> 3, c = qi & 7;
@@ -373,6 +376,11 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         }
     }
 
+    // The output column of accumulator column rl: forward, the feature itself; backward, the
+    // W' tile holds each 8-feature chunk in even/odd order (decode8<true>; the rank-r operand A
+    // is staged the same way), so position p of a chunk is feature 2p (p < 4) or 2p - 7.
+    const int rl_col = BWD ? (rl & ~7) | ((rl & 7) < 4 ? 2 * (rl & 7) : 2 * (rl & 7) - 7) : rl;
+
     // ---- piece of a split tile: fp32 partial tile, row-major TM x TN, summed later ----
     if (u.split >= 0) {
         float* slot = a.spart + (u.tail * a.S + u.split) * (int64_t)TILE_FLOATS;
@@ -380,7 +388,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int col = j * 32 + rl;
+                const int col = j * 32 + rl_col;
 #pragma unroll
                 for (int reg = 0; reg < 16; ++reg) {
                     const int row = wave * 128 + i * 32 + 8 * (reg >> 2) + 4 * h + (reg & 3);
@@ -396,7 +404,7 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t col = c0 + j * 32 + rl;
+            const int64_t col = c0 + j * 32 + rl_col;
 #pragma unroll
             for (int reg = 0; reg < 16; ++reg) {
                 const int64_t row = m0 + wave * 128 + i * 32 + 8 * (reg >> 2) + 4 * h + (reg & 3);
