@@ -88,6 +88,8 @@ def _args():
     p.add_argument("--gemv-sweep", action="store_true",
                    help="few-token forward only: 10 queued calls for each LLaMA-65B shape and M in "
                         "{1, 4, 16} (for a kernel trace; see --summarize-gemv-trace)")
+    p.add_argument("--summarize-gemv-pmc", nargs=2, metavar=("COUNTER_CSV", "COMMAND"),
+                   help="per-shape counters of k_gemv_part from a --gemv-sweep counter run, as a markdown table")
     p.add_argument("--summarize-gemv-trace", metavar="KERNEL_TRACE_CSV",
                    help="per-shape kernel durations of a --gemv-sweep kernel trace, as a markdown table")
     p.add_argument("--codebooks-only", action="store_true",
@@ -114,23 +116,60 @@ GEMV_SWEEP_CALLS = 10
 
 def gemv_sweep():
     """The few-token forward alone: for each shape and token count, GEMV_SWEEP_CALLS calls
-    queued behind a sleeping kernel, so that they run back to back."""
+    queued behind a sleeping kernel, so that they run back to back.  The calls rotate
+    through copies of the packed weight at different addresses, together more than twice
+    the 256 MB Infinity Cache, so that every call streams its weight from HBM."""
     import torch
     import bit_nf4_quantized_09_amd as nf4
     from workloads import linear_inputs, seed_of
 
     for (N, K) in GEMV_SWEEP_SHAPES:
         W, X, A, B, _ = linear_inputs(N, K, 16, 64, seed=seed_of(3, N, K), device="cuda", with_dy=False)
-        Wq = nf4.quantize_weight(W)
+        copies = []
+        while sum(c.nbytes() for c in copies) < (512 << 20):
+            copies.append(nf4.quantize_weight(W))
         del W
         for M in GEMV_SWEEP_M:
             x = X[:M].contiguous()
             torch.cuda.synchronize()
             torch.cuda._sleep(int(2e7))
-            for _ in range(GEMV_SWEEP_CALLS):
-                nf4.qlora_linear_fwd(Wq, x, A, B, 16.0)
+            for i in range(GEMV_SWEEP_CALLS):
+                nf4.qlora_linear_fwd(copies[i % len(copies)], x, A, B, 16.0)
             torch.cuda.synchronize()
-            print("gemv sweep N=%d K=%d M=%d done" % (N, K, M), file=sys.stderr, flush=True)
+            print("gemv sweep N=%d K=%d M=%d done (%d weight copies)" % (N, K, M, len(copies)),
+                  file=sys.stderr, flush=True)
+        del copies
+        torch.cuda.empty_cache()
+
+
+def summarize_gemv_pmc(counter_csv, command):
+    """Per-dispatch counters of k_gemv_part in a --gemv-sweep counter run, medians per
+    (shape, tokens), as a markdown table."""
+    import csv
+
+    per = {}
+    for row in csv.DictReader(open(counter_csv)):
+        k = row.get("Kernel_Name") or ""
+        if "k_gemv_part" not in k:
+            continue
+        d = int(row["Dispatch_Id"])
+        per.setdefault(d, {})
+        per[d][row["Counter_Name"]] = per[d].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    disp = [per[d] for d in sorted(per)]
+    names = sorted({c for v in disp for c in v})
+    out = ["# k_gemv_part counters per launch, LLaMA-65B shapes", "", "Command (GPU, repository root):", "",
+           "    " + command, "",
+           "Medians over the %d calls of each (shape, tokens) row of `bench.py --gemv-sweep` (each call "
+           "streams its weight from HBM: the calls rotate through copies of it)." % GEMV_SWEEP_CALLS, "",
+           "| N x K | M | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+    i = 0
+    for (N, K) in GEMV_SWEEP_SHAPES:
+        for M in GEMV_SWEEP_M:
+            grp = disp[i:i + GEMV_SWEEP_CALLS]
+            i += GEMV_SWEEP_CALLS
+            med = lambda c: sorted(v.get(c, 0.0) for v in grp)[len(grp) // 2] if grp else float("nan")
+            out.append("| %d x %d | %d | " % (N, K, M) + " | ".join("%.4g" % med(c) for c in names) + " |")
+    print("\n".join(out))
 
 
 def summarize_gemv_trace(trace_csv):
@@ -234,9 +273,14 @@ def summarize_pmc(fetch_csv, write_csv):
     ff, wf = pick(fetch, is_fused), pick(write, is_fused)
     if not (fc and wc and ff and wf):
         raise SystemExit("counter files lack the copy or the fused kernel")
-    # the copy of COPY_BYTES: largest dispatch of each kind
-    kf = (COPY_BYTES / 1024.0) / max(fc)
-    kw = (COPY_BYTES / 1024.0) / max(wc)
+    # the copy of COPY_BYTES: largest dispatch of each kind; the pure read and pure write
+    # of the same size, where the run has them, calibrate each counter on its own
+    kf_copy = (COPY_BYTES / 1024.0) / max(fc)
+    kw_copy = (COPY_BYTES / 1024.0) / max(wc)
+    pr = [v for (d, k), v in fetch.items() if "k_probe_read" in (k or "")]
+    pw = [v for (d, k), v in write.items() if "k_probe_write" in (k or "")]
+    kf = (COPY_BYTES / 1024.0) / pr[0] if pr else kf_copy
+    kw = (COPY_BYTES / 1024.0) / pw[0] if pw else kw_copy
     fetch_b = sum(ff) / len(ff) * 1024.0 * kf
     write_b = sum(wf) / len(wf) * 1024.0 * kw
     lines = [
@@ -249,8 +293,11 @@ def summarize_pmc(fetch_csv, write_csv):
         "    python bench.py --summarize-pmc <pmc_fetch>/run_counter_collection.csv <pmc_write>/run_counter_collection.csv",
         "",
         "Calibration: a plain device copy of %d MiB in the same run reads %.1f KiB by FETCH_SIZE and writes "
-        "%.1f KiB by WRITE_SIZE; the factors that map them to %d KiB are %.4f (fetch) and %.4f (write)."
-        % (COPY_BYTES >> 20, max(fc), max(wc), COPY_BYTES >> 10, kf, kw),
+        "%.1f KiB by WRITE_SIZE (factors %.4f and %.4f to %d KiB); a pure read of the same size fetches %s KiB "
+        "and a pure write writes %s KiB. The table uses %.4f (fetch) and %.4f (write)%s."
+        % (COPY_BYTES >> 20, max(fc), max(wc), kf_copy, kw_copy, COPY_BYTES >> 10,
+           "%.1f" % pr[0] if pr else "-", "%.1f" % pw[0] if pw else "-", kf, kw,
+           ", from the pure read and write" if pr and pw else ", from the copy"),
         "",
         "| launches | FETCH_SIZE KiB (avg) | WRITE_SIZE KiB (avg) | fetch bytes | write bytes |",
         "|---|---|---|---|---|",
@@ -881,7 +928,30 @@ def pmc_codec_workload():
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
+    calibration_probes()
     print("pmc codec workload done", flush=True)
+
+
+def calibration_probes():
+    """A pure read and a pure write of COPY_BYTES (the ceiling probes), each touching a
+    buffer no kernel has touched before, for calibrating FETCH_SIZE and WRITE_SIZE."""
+    import ctypes
+    import torch
+    from bit_nf4_quantized_09_amd.build import PROBE_LIB
+
+    L = ctypes.CDLL(PROBE_LIB)
+    L.nf4probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.nf4probe_stream.restype = ctypes.c_int
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    if (L.nf4probe_stream(0, src.data_ptr(), sink.data_ptr(), COPY_BYTES, 8192, 0, stream) != 0 or
+            L.nf4probe_stream(1, None, dst.data_ptr(), COPY_BYTES, 8192, 0, stream) != 0):
+        raise SystemExit("probe launch failed")
+    torch.cuda.synchronize()
 
 
 def summarize_pmc_codec(fetch_csv, write_csv):
@@ -896,8 +966,13 @@ def summarize_pmc_codec(fetch_csv, write_csv):
     wc = [v for (d, k), v in write.items() if is_copy(k or "")]
     if not (fc and wc):
         raise SystemExit("counter files lack the copy kernel")
-    kf = (COPY_BYTES / 1024.0) / max(fc)
-    kw = (COPY_BYTES / 1024.0) / max(wc)
+    kf_copy = (COPY_BYTES / 1024.0) / max(fc)
+    kw_copy = (COPY_BYTES / 1024.0) / max(wc)
+    pr = [v for (d, k), v in fetch.items() if "k_probe_read" in (k or "")]
+    pw = [v for (d, k), v in write.items() if "k_probe_write" in (k or "")]
+    # the pure read and pure write of the same size calibrate each counter on its own
+    kf = (COPY_BYTES / 1024.0) / pr[0] if pr else kf_copy
+    kw = (COPY_BYTES / 1024.0) / pw[0] if pw else kw_copy
     projs = layer_projections(LLAMA65B["d"], LLAMA65B["ffn"])
     n = sum(N * K for _, N, K in projs)
     nk = [(N, K) for _, N, K in projs]
@@ -927,7 +1002,11 @@ def summarize_pmc_codec(fetch_csv, write_csv):
         "The workload makes one pass of each kernel over the seven weights (%.4g values); the "
         "few-token forward runs once per weight at M = 1, 4 and 16. Calibration: a plain device "
         "copy of %d MiB in the same run reads %.1f KiB by FETCH_SIZE and writes %.1f KiB by "
-        "WRITE_SIZE, factors %.4f (fetch) and %.4f (write)." % (n, COPY_BYTES >> 20, max(fc), max(wc), kf, kw),
+        "WRITE_SIZE (factors %.4f and %.4f); a pure read of the same size (the read probe) "
+        "fetches %s KiB and a pure write writes %s KiB. The table uses the factors %.4f (fetch) "
+        "and %.4f (write)%s." % (n, COPY_BYTES >> 20, max(fc), max(wc), kf_copy, kw_copy,
+                                 "%.1f" % pr[0] if pr else "-", "%.1f" % pw[0] if pw else "-", kf, kw,
+                                 ", from the pure read and write" if pr and pw else ", from the copy"),
         "",
         "| kernel | dispatches | fetched bytes | written bytes | traffic | algorithmic bytes | traffic / algorithmic |",
         "|---|---|---|---|---|---|---|",
@@ -973,6 +1052,7 @@ def pmc_workload(args):
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
+    calibration_probes()
     print("pmc workload done", flush=True)
 
 
@@ -989,6 +1069,9 @@ def main():
         return
     if args.summarize_pmc_codec:
         summarize_pmc_codec(*args.summarize_pmc_codec)
+        return
+    if args.summarize_gemv_pmc:
+        summarize_gemv_pmc(*args.summarize_gemv_pmc)
         return
     if args.summarize_gemv_trace:
         summarize_gemv_trace(args.summarize_gemv_trace)
