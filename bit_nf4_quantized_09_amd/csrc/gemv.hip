@@ -363,21 +363,21 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(GvArgs a, int64_t slices) {
 #pragma unroll
     for (int q8 = 0; q8 < 16; ++q8)
         bv[q8] = (row_ok && q8 < a.r / 8) ? reinterpret_cast<const uint4*>(a.Bl + n * a.r)[q8] : make_uint4(0, 0, 0, 0);
-    // partial-sum offsets of the outputs and T entries; an entry that does not exist
-    // reads offset 0 and adds zero
-    int64_t off[NE];
-    bool ok[NE];
+    // partial-sum byte offsets of the outputs and T entries in slice 0 (all slices span
+    // slices x M x (N + r) x 4 < 2^28 bytes); an entry that does not exist, or a slice past
+    // the last, requests an offset past the range, which reads zero and touches no memory
+    constexpr uint32_t OOR = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t rs_part = make_rsrc(a.part, slices * sstride * 4);
+    uint32_t off[NE];
 #pragma unroll
     for (int i = 0; i < NO; ++i) {
         const int m = tg + TG * i;
-        ok[i] = row_ok && m < a.M;
-        off[i] = ok[i] ? (int64_t)m * ld + n : 0;
+        off[i] = (row_ok && m < a.M) ? (uint32_t)(((int64_t)m * ld + n) * 4) : OOR;
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int e = tid + 256 * t;
-        ok[NO + t] = e < a.M * a.r;
-        off[NO + t] = ok[NO + t] ? (int64_t)(e / a.r) * ld + a.N + e % a.r : 0;
+        off[NO + t] = e < a.M * a.r ? (uint32_t)(((int64_t)(e / a.r) * ld + a.N + e % a.r) * 4) : OOR;
     }
     float sum[NE];
 #pragma unroll
@@ -386,20 +386,19 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(GvArgs a, int64_t slices) {
         float v[8][NE];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const float* ps = a.part + (s0 + u < slices ? (s0 + u) * sstride : 0);
-#pragma unroll
-            for (int i = 0; i < NE; ++i) v[u][i] = ps[off[i]];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
             const bool su = s0 + u < slices;
+            const uint32_t so = (uint32_t)((s0 + u) * sstride * 4);
 #pragma unroll
-            for (int i = 0; i < NE; ++i) sum[i] += (su && ok[i]) ? v[u][i] : 0.0f;
+            for (int i = 0; i < NE; ++i) v[u][i] = buf_loadf(rs_part, su && off[i] != OOR ? off[i] + so : OOR, 0);
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int i = 0; i < NE; ++i) sum[i] += v[u][i];
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        if (ok[NO + t]) {
+        if (off[NO + t] != OOR) {
             const int e = tid + 256 * t, m = e / a.r, q = e % a.r;
             s_ts[m][q] = bf16_to_f32(f32_to_bf16(a.s * sum[NO + t]));
             if (blockIdx.x == 0) a.T[(int64_t)m * a.r + q] = f32_to_bf16(sum[NO + t]);
@@ -408,7 +407,7 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(GvArgs a, int64_t slices) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < NO; ++i) {
-        if (!ok[i]) continue;
+        if (off[i] == OOR) continue;
         const int m = tg + TG * i;
         float l = 0.0f;
 #pragma unroll
@@ -462,7 +461,12 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
                                           : launch_gemv_part<16, false>(g1, ga, tab, st));
             if (e != hipSuccess) return e;
         }
-        if (small) hipLaunchKernelGGL((k_gemv_reduce<32, 1, 2>), g2, dim3(256), 0, st, ga, slices);
+        // T entries per thread: just enough for the M x r of them (every reduce workgroup
+        // forms all of T, so unused slots would only add requests)
+        const int64_t mr = M * r;
+        if (small && mr <= 256) hipLaunchKernelGGL((k_gemv_reduce<32, 1, 1>), g2, dim3(256), 0, st, ga, slices);
+        else if (small) hipLaunchKernelGGL((k_gemv_reduce<32, 1, 2>), g2, dim3(256), 0, st, ga, slices);
+        else if (mr <= 1024) hipLaunchKernelGGL((k_gemv_reduce<64, 4, 4>), g2, dim3(256), 0, st, ga, slices);
         else hipLaunchKernelGGL((k_gemv_reduce<64, 4, 8>), g2, dim3(256), 0, st, ga, slices);
         return hipGetLastError();
     });
