@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "NF4Error", "NF4Weight", "lib_path", "load_library", "nf4_quantize", "nf4_double_quantize",
-    "nf4_double_dequantize", "nf4_dequantize", "quantize_weight", "qlora_linear_fwd",
+    "nf4_double_dequantize", "nf4_double_quantize_batch", "nf4_dequantize", "quantize_weight", "qlora_linear_fwd",
     "qlora_linear_bwd", "nf4_storage_bytes", "nf4_codebook", "nf4_workspace_bytes",
     "nf4_profile_next_fused", "adamw_step", "adamw_step_paged", "PagedAdamW",
     "nf4_quantize_codebook", "nf4_codebook_stats", "qlora_linear_fwd_noalloc", "codebook_int4_symmetric", "codebook_uniform16",
@@ -75,6 +75,10 @@ def load_library():
     L.nf4_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i32, _vp, _vp, _vp]
     L.nf4_double_quantize.restype = ctypes.c_int
     L.nf4_double_quantize.argtypes = [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.nf4_double_quantize_batch.restype = ctypes.c_int
+    L.nf4_double_quantize_batch.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.nf4_double_quantize_batch_workspace_bytes.restype = _sz
+    L.nf4_double_quantize_batch_workspace_bytes.argtypes = [_i32, _vp]
     L.nf4_double_dequantize.restype = ctypes.c_int
     L.nf4_double_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i32, _vp, _vp]
     L.nf4_dequantize.restype = ctypes.c_int
@@ -266,6 +270,37 @@ def nf4_double_quantize(absmax: torch.Tensor, blocksize2: int = 256):
     _check(L.nf4_double_quantize(_ptr(absmax), n1, blocksize2, _ptr(q), _ptr(c2), _ptr(mean),
                                  _ptr(ws), wsb, _stream(absmax.device)))
     return q, c2, mean
+
+
+def nf4_double_quantize_batch(absmax_list):
+    """Double quantization of many first-level constant vectors at once (same device):
+    a list of (q, c2, mean), each exactly what nf4_double_quantize gives for that vector,
+    from two kernel launches per 32 vectors."""
+    L = load_library()
+    absmax_list = list(absmax_list)
+    count = len(absmax_list)
+    if count == 0:
+        return []
+    for i, a in enumerate(absmax_list):
+        _dev(a, "absmax[%d]" % i, torch.float32)
+    _same_device(*(("absmax[%d]" % i, a) for i, a in enumerate(absmax_list)))
+    dev = absmax_list[0].device
+    outs = []
+    for a in absmax_list:
+        n1 = a.numel()
+        outs.append((torch.empty(n1, dtype=torch.uint8, device=dev),
+                     torch.empty((n1 + 255) // 256, dtype=torch.float32, device=dev),
+                     torch.empty(1, dtype=torch.float32, device=dev)))
+    arr = lambda vals, ct: (ct * count)(*vals)
+    n1s = arr([a.numel() for a in absmax_list], ctypes.c_int64)
+    c1p = arr([_ptr(a) for a in absmax_list], ctypes.c_void_p)
+    qp = arr([_ptr(o[0]) for o in outs], ctypes.c_void_p)
+    c2p = arr([_ptr(o[1]) for o in outs], ctypes.c_void_p)
+    mp = arr([_ptr(o[2]) for o in outs], ctypes.c_void_p)
+    wsb = L.nf4_double_quantize_batch_workspace_bytes(count, n1s)
+    ws = _workspace(wsb, dev)
+    _check(L.nf4_double_quantize_batch(count, c1p, n1s, qp, c2p, mp, _ptr(ws), wsb, _stream(dev)))
+    return outs
 
 
 def nf4_double_dequantize(q: torch.Tensor, c2: torch.Tensor, mean: torch.Tensor,

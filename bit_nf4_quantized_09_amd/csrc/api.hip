@@ -361,6 +361,38 @@ nf4_status nf4_double_quantize(const float* absmax, int64_t n1, int32_t blocksiz
                       "nf4_double_quantize");
 }
 
+size_t nf4_double_quantize_batch_workspace_bytes(int32_t count, const int64_t* n1) {
+    if (count <= 0 || !n1) return 0;
+    for (int32_t t = 0; t < count; ++t)
+        if (n1[t] < 0) return 0;
+    return nf4::double_quantize_batch_ws_bytes(count, n1);
+}
+
+nf4_status nf4_double_quantize_batch(int32_t count, const float* const* absmax, const int64_t* n1,
+                                     uint8_t* const* q, float* const* c2, float* const* mean, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    if (count < 0) return fail(NF4_ERR_ARG, "count must be >= 0");
+    if (count == 0) return NF4_OK;
+    if (!absmax || !n1 || !q || !c2 || !mean) return fail(NF4_ERR_ARG, "NULL array");
+    for (int32_t t = 0; t < count; ++t) {
+        if (n1[t] < 0) return fail(NF4_ERR_ARG, "n1 must be >= 0");
+        if (n1[t] > nf4::DQB_MAX_N1)
+            return fail(NF4_ERR_UNSUPPORTED, "a batched tensor holds at most 2048 x 2048 constants");
+        if (!mean[t]) return fail(NF4_ERR_ARG, "mean is NULL");
+        if (n1[t] > 0 && (!absmax[t] || !q[t] || !c2[t])) return fail(NF4_ERR_ARG, "NULL absmax/q/c2");
+        if (!aligned(absmax[t], 16)) return fail(NF4_ERR_ARG, "absmax must be 16-byte aligned");
+        if (!aligned(q[t], 4) || !aligned(c2[t], 4) || !aligned(mean[t], 4))
+            return fail(NF4_ERR_ARG, "misaligned q/c2/mean");
+    }
+    const size_t need = nf4::double_quantize_batch_ws_bytes(count, n1);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(NF4_ERR_WORKSPACE, "workspace smaller than nf4_double_quantize_batch_workspace_bytes()");
+    if (need > 0 && !aligned(workspace, 8)) return fail(NF4_ERR_ARG, "workspace must be 8-byte aligned");
+    return hip_status(nf4::launch_double_quantize_batch(count, absmax, n1, q, c2, mean, (double*)workspace,
+                                                        (hipStream_t)stream),
+                      "nf4_double_quantize_batch");
+}
+
 nf4_status nf4_double_dequantize(const uint8_t* q, const float* c2, const float* mean, int64_t n1,
                                  int32_t blocksize2, float* c1_out, void* stream) {
     if (blocksize2 != 256) return fail(NF4_ERR_UNSUPPORTED, "blocksize2 must be 256");

@@ -351,7 +351,9 @@ template <int ROWS, int NO, int NT>
 __global__ __launch_bounds__(256) void k_gemv_reduce(GvArgs a, int64_t slices) {
     constexpr int TG = 256 / ROWS;
     constexpr int NE = NO + NT;
-    __shared__ float s_ts[16][129];       // s T (rounded to bf16), tokens x rank
+    // s T (rounded to bf16), tokens x rank; the lanes of a wave share a token, so each read
+    // is a broadcast, four ranks at a time
+    __shared__ __attribute__((aligned(16))) float s_ts[16][128];
     const int tid = threadIdx.x;
     const int64_t ld = a.N + a.r;
     const int64_t sstride = (int64_t)a.M * ld;        // one slice of partial sums
@@ -414,10 +416,13 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(GvArgs a, int64_t slices) {
         for (int q8 = 0; q8 < 16; ++q8) {
             if (q8 < a.r / 8) {
                 const uint32_t bw[4] = {bv[q8].x, bv[q8].y, bv[q8].z, bv[q8].w};
+                const float4 t0 = *reinterpret_cast<const float4*>(&s_ts[m][8 * q8]);
+                const float4 t1 = *reinterpret_cast<const float4*>(&s_ts[m][8 * q8 + 4]);
+                const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    l = __fmaf_rn(s_ts[m][8 * q8 + 2 * e], bf16_lo(bw[e]), l);
-                    l = __fmaf_rn(s_ts[m][8 * q8 + 2 * e + 1], bf16_hi(bw[e]), l);
+                    l = __fmaf_rn(tv[2 * e], bf16_lo(bw[e]), l);
+                    l = __fmaf_rn(tv[2 * e + 1], bf16_hi(bw[e]), l);
                 }
             }
         }

@@ -25,6 +25,25 @@ struct WeightView {
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, uint8_t* codes, float* absmax,
                            const Nf4Table& tab, hipStream_t s);
 size_t double_quantize_ws_bytes(int64_t n1);
+// A batch of tensors for double quantization (up to DQB_MAX per launch pair), each of at
+// most 2048 x 2048 constants: device pointers, sizes and the prefix counts of their
+// 2048-constant chunks and encode groups.
+constexpr int DQB_MAX = 32;
+struct DqBatch {
+    int count;
+    const float* c1[DQB_MAX];
+    uint8_t* q[DQB_MAX];
+    float* c2[DQB_MAX];
+    float* mean[DQB_MAX];
+    int64_t n1[DQB_MAX];
+    int64_t chunk0[DQB_MAX + 1];
+    int64_t group0[DQB_MAX + 1];
+    double* ws;                // chunk sums, chunk0[count] of them
+};
+constexpr int64_t DQB_MAX_N1 = (int64_t)2048 * 2048;
+size_t double_quantize_batch_ws_bytes(int count, const int64_t* n1);
+hipError_t launch_double_quantize_batch(int count, const float* const* c1, const int64_t* n1, uint8_t* const* q,
+                                        float* const* c2, float* const* mean, double* ws, hipStream_t s);
 hipError_t launch_double_quantize(const float* c1, int64_t n1, uint8_t* q, float* c2, float* mean,
                                   double* ws, hipStream_t s);
 hipError_t launch_double_dequantize(const uint8_t* q, const float* c2, const float* mean, int64_t n1,

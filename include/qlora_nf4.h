@@ -155,6 +155,22 @@ nf4_status nf4_double_quantize(const float* absmax, int64_t n1, int32_t blocksiz
                                float* c2, float* mean, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* [DQ] for many tensors at once (a model's weights quantized in bulk): the
+ * result for tensor t is exactly nf4_double_quantize(absmax[t], n1[t], 256, q[t],
+ * c2[t], mean[t]); the whole batch takes two kernel launches per 32 tensors
+ * instead of two per tensor.
+ *   count   number of tensors (0: nothing to do)
+ *   absmax, n1, q, c2, mean   HOST arrays of `count` entries: device pointers
+ *           (as for nf4_double_quantize) and sizes, 0 <= n1[t] <= 2048 * 2048
+ *           (NF4_ERR_UNSUPPORTED above: use nf4_double_quantize for such a tensor)
+ *   workspace   nf4_double_quantize_batch_workspace_bytes(count, n1) bytes,
+ *               8-byte aligned (chunk sums).
+ * The host arrays are read during the call only. */
+size_t nf4_double_quantize_batch_workspace_bytes(int32_t count, const int64_t* n1);
+nf4_status nf4_double_quantize_batch(int32_t count, const float* const* absmax, const int64_t* n1,
+                                     uint8_t* const* q, float* const* c2, float* const* mean, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* [DQ]: two-level constant decode (stub double_dequantize(q, c2, mean)):
  * c1'[i] = fma(E4M3(q[i]), fp32(c2[i/256] / 448), mean), one rounding.
  *   c1_out  out: n1 fp32 */

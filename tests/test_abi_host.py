@@ -36,7 +36,8 @@ def test_library_exports_every_declared_symbol():
                             "nf4_workspace_bytes", "nf4_storage_bytes", "nf4_codebook",
                             "nf4_last_error", "nf4_profile_next_fused", "nf4_adamw_step",
                             "nf4_adamw_step_paged", "nf4_quantize_codebook", "nf4_codebook_stats",
-                            "qlora_linear_fwd_noalloc", "nf4_lowrank_svd", "nf4_loftq_init"])
+                            "qlora_linear_fwd_noalloc", "nf4_lowrank_svd", "nf4_loftq_init",
+                            "nf4_double_quantize_batch", "nf4_double_quantize_batch_workspace_bytes"])
     for name in names:
         assert hasattr(L, name), name
     # and the C symbols are unmangled (extern "C")
@@ -302,3 +303,25 @@ def test_lowrank_and_loftq_reject_bad_arguments():
     assert lq(p, 256, 192, 8, 16.0, 3, 24, 2, p, p, p, p, p, None, p, p, ws, big, None) == nf4.NF4_ERR_ARG
     assert L.nf4_workspace_bytes(nf4.NF4_OP_LOFTQ, 24, 256, 192, 8) > 256 * 192 * 4
     assert L.nf4_workspace_bytes(nf4.NF4_OP_LOWRANK_SVD, 97, 256, 192, 8) == 0
+
+
+def test_double_quantize_batch_host_checks():
+    # sizes and argument checks of the batched double quantization, before any HIP call
+    import ctypes
+    L = nf4.load_library()
+    n1 = (ctypes.c_int64 * 4)(1, 2048, 2049, 2048 * 2048)
+    # one float64 chunk sum per 2048 constants of every tensor
+    assert L.nf4_double_quantize_batch_workspace_bytes(4, n1) == 8 * (1 + 1 + 2 + 2048)
+    assert L.nf4_double_quantize_batch_workspace_bytes(0, n1) == 0
+    null = (ctypes.c_void_p * 1)(None)
+    one = (ctypes.c_int64 * 1)(64)
+    assert L.nf4_double_quantize_batch(0, None, None, None, None, None, None, 0, None) == 0
+    assert L.nf4_double_quantize_batch(-1, null, one, null, null, null, None, 0, None) == nf4.NF4_ERR_ARG
+    big = (ctypes.c_int64 * 1)(2048 * 2048 + 1)
+    assert L.nf4_double_quantize_batch(1, null, big, null, null, null, None, 0, None) == nf4.NF4_ERR_UNSUPPORTED
+    # NULL mean
+    assert L.nf4_double_quantize_batch(1, null, one, null, null, null, None, 0, None) == nf4.NF4_ERR_ARG
+    # a non-null but too small workspace is refused before anything runs
+    fake = (ctypes.c_void_p * 1)(0x1000)
+    assert L.nf4_double_quantize_batch(1, fake, one, fake, fake, fake, ctypes.c_void_p(0x1000), 4,
+                                       None) == nf4.NF4_ERR_WORKSPACE

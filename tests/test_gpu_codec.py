@@ -153,6 +153,27 @@ def test_double_quant_constant_and_mean_tree():
     assert np.array_equal(c2.cpu().numpy().view(np.uint32), rc2.view(np.uint32))
 
 
+def test_double_quantize_batch():
+    # the batched double quantization equals the oracle, tensor by tensor, bit for bit: sizes
+    # that are empty, one constant, one ragged block, whole and ragged chunks, the largest a
+    # batch takes (2048 chunks), and more tensors than one launch pair holds (32)
+    rng = np.random.Generator(np.random.PCG64(21))
+    sizes = [0, 1, 255, 256, 2047, 2048, 2049, 70001, 2048 * 2048] + [int(x) for x in rng.integers(1, 9000, 40)]
+    host = [np.abs(rng.standard_normal(n)).astype(np.float32) * np.float32(rng.uniform(1e-3, 10.0))
+            for n in sizes]
+    host[3][:] = np.float32(0.0625)                        # a constant vector: c2 = 0, q = 0
+    dev = [torch.from_numpy(h).to(DEV) for h in host]
+    outs = nf4.nf4_double_quantize_batch(dev)
+    torch.cuda.synchronize()
+    assert len(outs) == len(sizes)
+    for n, h, (q, c2, mean) in zip(sizes, host, outs):
+        rq, rc2, rmean = oracle.double_quantize(h)
+        where = "n1=%d" % n
+        assert mean.cpu().numpy().view(np.uint32)[0] == np.asarray(rmean, np.float32).view(np.uint32).reshape(-1)[0], where
+        assert np.array_equal(q.cpu().numpy(), rq), where
+        assert np.array_equal(c2.cpu().numpy().view(np.uint32), np.asarray(rc2, np.float32).view(np.uint32)), where
+
+
 @pytest.mark.parametrize("name,N,K", [("q7b", 4096, 4096), ("gate7b", 11008, 4096),
                                       ("down65b", 8192, 22016)])
 def test_codec_full_llama_shapes(name, N, K):
