@@ -898,6 +898,34 @@ def hbm_ceiling(reps=10):
     gbs = 2 * nbytes / (t0.elapsed_time(t1) / 1e3 / reps) / 1e9
     rows.append("| copy (torch copy_) | - | - | %.0f | %.1f%% |" % (gbs, 100.0 * gbs / PEAK_HBM_GBS))
     rows += ["", "best: " + ", ".join("%s %.0f GB/s" % kv for kv in best.items())]
+    del src, dst
+    rows += ["", "One launch over a buffer of the few-token forward's size (the packed 8192 x 8192 and",
+             "22016 x 8192 weights): GPU time per launch over launches queued behind a sleeping",
+             "kernel, rotating through copies of more than 1 GB, so each reads from HBM.", "",
+             "| MB read | nontemporal | workgroups | us per launch | GB/s | % of 8 TB/s |", "|---|---|---|---|---|---|"]
+    for mb in (34.6, 92.9):
+        size = int(mb * 1e6) // 16 * 16
+        copies = max(2, (1 << 30) // size + 1)
+        bufs = [torch.empty(size // 4, dtype=torch.int32, device="cuda:0").fill_(i) for i in range(copies)]
+        for nt in (0, 1):
+            for grid in (1024, 2048, 4096, 8192):
+                for b in bufs:
+                    L.nf4probe_stream(0, b.data_ptr(), sink.data_ptr(), size, grid, nt, stream)
+                torch.cuda.synchronize()
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(int(5e7))
+                t0.record()
+                for b in bufs:
+                    L.nf4probe_stream(0, b.data_ptr(), sink.data_ptr(), size, grid, nt, stream)
+                t1.record()
+                torch.cuda.synchronize()
+                us = t0.elapsed_time(t1) * 1e3 / copies
+                gbs = size / (us * 1e-6) / 1e9
+                rows.append("| %.1f | %s | %d | %.2f | %.0f | %.1f%% |" % (size / 1e6, "yes" if nt else "no", grid, us,
+                                                                           gbs, 100.0 * gbs / PEAK_HBM_GBS))
+        del bufs
+        print("hbm ceiling: %.1f MB reads done" % mb, file=sys.stderr, flush=True)
     print("\n".join(rows), flush=True)
 
 
@@ -982,8 +1010,8 @@ def summarize_pmc_codec(fetch_csv, write_csv):
     fams = [
         ("quantize, fp32 in", lambda k: "k_quantize<unsigned int>" in k, 7, n * (4 + 0.5 + 4 / 64)),
         ("quantize, bf16 in", lambda k: "k_quantize<unsigned short>" in k, 7, n * (2 + 0.5 + 4 / 64)),
-        ("double quantization: chunk sums", lambda k: "k_pairwise_chunks" in k, 7, n1 * 4),
-        ("double quantization: mean + 8-bit encode", lambda k: "k_dq_encode_mean" in k, 7,
+        ("double quantization: chunk sums", lambda k: "k_dqb_chunks" in k, 7, n1 * 4),
+        ("double quantization: mean + 8-bit encode", lambda k: "k_dqb_encode" in k or "k_dq_encode" in k, 7,
          n1 * (4 + 1) + n1 / 256 * 4),
         ("dequantize, fp32 out", lambda k: "k_dequantize<false, false>" in k, 7, n * (NF4_BYTES_PER_PARAM + 4)),
         ("dequantize, bf16 out", lambda k: "k_dequantize<true, false>" in k, 7, n * (NF4_BYTES_PER_PARAM + 2)),

@@ -111,6 +111,25 @@ def test_gemv_second_level_groups(M):
         worst, err[worst], row_norm[worst])
 
 
+def test_backward_rows_stay_apart():
+    # dX contracts over N = 72: the last 64-value step holds 8 real columns. An infinite
+    # value at the start of dY's row 1 sits right after row 0's last column in memory; row 0
+    # of dX (and every other row but 1) must not see it: the packed dY holds zeros past N.
+    N, K, M, r = 72, 128, 40, 8
+    W, X, A, B, dY = (t.to(DEV) for t in linear_inputs(N, K, M, r, seed=seed_of(16)))
+    dY[1, 0] = float("inf")
+    ref = oracle_weight(W.cpu())
+    Wq = nf4.quantize_weight(W)
+    dX, dA, dB = nf4.qlora_linear_bwd(Wq, X, dY, A, B, 16.0)
+    torch.cuda.synchronize()
+    dXr, _, _ = oracle.qlora_linear_bwd(ref["Wd"], host_f32(X), host_f32(dY), host_f32(A), host_f32(B), 16.0,
+                                        want_da=False, want_db=False)
+    keep = [m for m in range(M) if m != 1]
+    got = to_np(dX)[keep]
+    assert np.all(np.isfinite(got)), "a row other than 1 saw the infinite value"
+    assert_close("dX", got, dXr[keep])
+
+
 def test_gemv_and_gemm_paths_agree():
     # 16 tokens run through the dequant-GEMV; the same 16 plus one more run through the GEMM
     N, K, r = 520, 1024, 64
