@@ -39,7 +39,7 @@ namespace nf4 {
 // the adapter rows A (bf16, no scale): partial sums of T = X A^T from the same pass.
 // Partial sums go to part[slice][token][row] (rows N.. hold T).
 //
-// k_gemv_reduce: per 32 or 64 weight rows, sums the slices in slice order, forms T
+// k_gemv_reduce: per 32 weight rows, sums the slices in slice order, forms T
 // (the sum of its slices) and s T (bf16), and Y = sum + (s T) B^T (bf16), with every
 // load of a thread requested before the first is used.
 // ---------------------------------------------------------------------------
@@ -453,9 +453,10 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
     const bool small = M <= 4;
     const int64_t wrows = small ? gv_rows(4) : gv_rows(16);
     dim3 g1((unsigned)(slices * ((r + GV_AROWS - 1) / GV_AROWS + (W.rows + wrows - 1) / wrows)));
-    // reduce: 32 rows x 8 token groups (one output per thread) for up to 4 tokens,
-    // 64 rows x 4 token groups (four outputs) above
-    const int64_t rrows = small ? 32 : 64;
+    // reduce: 32 rows x 8 token groups, one output per thread for up to 4 tokens, two
+    // above (64-row workgroups with four outputs each left half the chip idle on the
+    // 8192-row weights and measured 1% slower at 16 tokens)
+    const int64_t rrows = 32;
     dim3 g2((unsigned)((W.rows + rrows - 1) / rrows > 0 ? (W.rows + rrows - 1) / rrows : 1));
     return with_events(st, [&] {
         if (g1.x > 0) {
@@ -471,8 +472,8 @@ hipError_t launch_fused_gemv(const WeightView& W, const uint16_t* X, int64_t M, 
         const int64_t mr = M * r;
         if (small && mr <= 256) hipLaunchKernelGGL((k_gemv_reduce<32, 1, 1>), g2, dim3(256), 0, st, ga, slices);
         else if (small) hipLaunchKernelGGL((k_gemv_reduce<32, 1, 2>), g2, dim3(256), 0, st, ga, slices);
-        else if (mr <= 1024) hipLaunchKernelGGL((k_gemv_reduce<64, 4, 4>), g2, dim3(256), 0, st, ga, slices);
-        else hipLaunchKernelGGL((k_gemv_reduce<64, 4, 8>), g2, dim3(256), 0, st, ga, slices);
+        else if (mr <= 1024) hipLaunchKernelGGL((k_gemv_reduce<32, 2, 4>), g2, dim3(256), 0, st, ga, slices);
+        else hipLaunchKernelGGL((k_gemv_reduce<32, 2, 8>), g2, dim3(256), 0, st, ga, slices);
         return hipGetLastError();
     });
 }
