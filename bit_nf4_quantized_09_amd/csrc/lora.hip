@@ -454,6 +454,8 @@ hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, 
     if ((!a_trans || !b_trans) && P >= ((int64_t)1 << 22)) return hipErrorInvalidValue;
     if ((a_trans && Mc >= ((int64_t)1 << 23)) || (b_trans && Nc >= ((int64_t)1 << 23)))
         return hipErrorInvalidValue;
+    // a strided operand is read in 16-byte pieces along its rows: 8 | its row length
+    if ((a_trans && (Mc & 7)) || (b_trans && (Nc & 7))) return hipErrorInvalidValue;
     int S;
     int64_t cps;
     skinny_plan(Mc, Nc, P, &S, &cps);
