@@ -18,7 +18,7 @@ constexpr int FUSED_TN = 128;           //              x features
 constexpr int TILE_FLOATS = 65536;      // TM x TN of every tile shape
 constexpr int XCDS = 8;                 // accelerator complex dies, each with its own L2
 constexpr int XCD_CUS = 32;             // compute units per XCD (256 / 8)
-constexpr int GROUP_M = 4;              // token tiles per group of the tile order
+constexpr int GROUP_M = 2;              // token tiles per group of the tile order
 constexpr int MAX_SPLIT = 4;            // pieces per tail tile at most
 // Fragment-order layout of the fused products' A operand (X forward, dY backward), written
 // by k_skinny (lora.hip) and read by k_fused: one 64 KB block per (512-row token tile, 64-value step),
@@ -79,9 +79,10 @@ inline FusedPlan fused_bwd_plan(int64_t M, int64_t N, int64_t K) { return fused_
 //
 // Workgroups are handed to the XCDs in turn: workgroup i runs on XCD i % 8.  The map
 // gives XCD x a contiguous range of the tile order, and walks that order in groups of
-// 4 token tiles, so the ~32 workgroups an XCD holds at once cover a compact 4 x 8 block
+// 2 token tiles, so the ~32 workgroups an XCD holds at once cover a compact 2 x 16 block
 // of output tiles and share their A tiles and W' tiles in that XCD's L2 instead of
-// fetching them again.  With S > 1, the last (tiles mod XCD_CUS) tiles of each XCD's
+// fetching them again (2 x 16 fetched a third less than 4 x 8 at the same speed; 8 x 4
+// fetched twice as much).  With S > 1, the last (tiles mod XCD_CUS) tiles of each XCD's
 // range are run as S pieces each, by workgroups that follow the whole tiles in launch
 // order on the same XCD (so the pieces of a tile share its L2).  Returns false for a
 // workgroup with no unit (XCDs with one tile fewer than the first).
