@@ -35,6 +35,14 @@ namespace nf4 {
 // threshold, +inf if none).  The same fp32 thresholds and strict comparisons as a
 // search through all fifteen, in one LDS read, one compare and one add.
 // ---------------------------------------------------------------------------
+// floor(x) as an int in one v_cvt_flr_i32_f32 (for |x| < 2^31; (int)floorf(x) compiles to a
+// v_floor_f32 and a v_cvt_i32_f32): quantize fp32 +3%, bf16 +3-5%
+__device__ __forceinline__ int floor_to_int(float x) {
+    int r;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 // values per lane: 64 bytes of fp32 or 32 of bf16 in flight per lane (8 values per lane
 // measured 7% slower for fp32 and 20% for bf16; 32 per lane no faster)
 constexpr int Q_EPL = 16;
@@ -136,7 +144,7 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ w, int64
                 // infinite absmax) takes entry 0 and code 0, as the comparisons x > m_j all
                 // fail for it (a zero block gives NaN too; its codes are replaced below)
                 const float xe = x[8 * k + e];
-                const int bi = (int)floorf(fminf(fmaxf(xe * 32.0f, -33.0f), 32.0f)) + 33;
+                const int bi = floor_to_int(fminf(fmaxf(xe * 32.0f, -33.0f), 32.0f)) + 33;
                 const uint2 bk = s_bucket[bi];
                 const uint32_t code = bk.x + (xe > __uint_as_float(bk.y) ? 1u : 0u);
                 pw |= code << (4 * e);
