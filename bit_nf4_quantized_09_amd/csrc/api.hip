@@ -455,15 +455,13 @@ nf4_status qlora_linear_fwd(const nf4_weight* W, const void* X, int64_t M, const
     }
     // T = X A^T (kept for the backward) and s*T for the epilogue of the fused product; the
     // same pass writes X in the fused product's fragment order
+    // The block constants of W are decoded by extra workgroups of T's slice-sum launch (plain
+    // constants are read as they are)
+    const nf4::DqDecode dq{v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1};
     e = nf4::launch_lora_gemm(x, false, (const uint16_t*)A, false, M, r, v.cols, part, 1.0f, Tb,
-                              false, false, Ts, s, hs, xpk, true);
+                              false, false, Ts, s, hs, xpk, true, v.absmax ? nullptr : &dq);
     if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (T)");
-    if (v.absmax) {
-        c1 = (float*)v.absmax;            // plain constants: read as they are
-    } else {
-        e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
-        if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd (constants)");
-    }
+    if (v.absmax) c1 = (float*)v.absmax;
     e = nf4::launch_fused_fwd(v, c1, xpk, M, Ts, (const uint16_t*)B, r, (uint16_t*)Y, part, table(), hs);
     return hip_status(e, "qlora_linear_fwd (gemm)");
 }
@@ -528,8 +526,11 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
     if (M > 0) {
         // Us = s dY B   (B stored N x r: contraction-strided); with dX wanted, the same pass
         // writes dY in the fused product's fragment order
+        // with dX wanted, extra workgroups of the slice-sum launch decode W's block constants
+        const nf4::DqDecode dq{v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1};
         e = nf4::launch_lora_gemm(g, false, bl, true, M, r, v.rows, part, s, Us, false, false,
-                                  nullptr, 0.0f, hs, dX ? gpk : nullptr);
+                                  nullptr, 0.0f, hs, dX ? gpk : nullptr, false,
+                                  (dX && !v.absmax) ? &dq : nullptr);
         if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (U)");
         if (!Tb) {
             uint16_t* Tw = (uint16_t*)((char*)workspace + rb);
@@ -539,12 +540,7 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
             Tb = Tw;
         }
         if (dX) {
-            const float* c1b = v.absmax;   // plain constants: read as they are
-            if (!c1b) {
-                e = nf4::launch_double_dequantize(v.q, v.c2, v.mean, v.rows * (v.cols / 64), c1, hs);
-                if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (constants)");
-                c1b = c1;
-            }
+            const float* c1b = v.absmax ? v.absmax : c1;   // plain constants: read as they are
             e = nf4::launch_fused_bwd_dx(v, c1b, gpk, M, Us, al, r, (uint16_t*)dX, part, table(), hs);
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dX)");
         }

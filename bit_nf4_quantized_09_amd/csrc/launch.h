@@ -63,10 +63,20 @@ hipError_t launch_dequantize(const WeightView& W, void* out, bool out_bf16, cons
 // anyway; with pack_even_odd each 16-byte piece holds its 8 values in the order 0, 2, 4, 6,
 // 1, 3, 5, 7 (the order of the forward product's decoded weights).
 size_t skinny_partial_bytes(int64_t Mc, int64_t Nc, int64_t P);
+// A two-level constant decode (as launch_double_dequantize) that rides on the slice-sum
+// launch of a rank-r product: extra workgroups of that launch write out[0 .. n1).
+struct DqDecode {
+    const uint8_t* q;
+    const float* c2;
+    const float* mean;
+    int64_t n1;
+    float* out;
+};
 hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, bool b_trans,
                             int64_t Mc, int64_t Nc, int64_t P, float* part, float scale, void* C,
                             bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s,
-                            uint16_t* pack = nullptr, bool pack_even_odd = false);
+                            uint16_t* pack = nullptr, bool pack_even_odd = false,
+                            const DqDecode* dq = nullptr);
 
 // ---- profiling hook: events around the next fused launch on this thread ----
 struct FusedEvents {

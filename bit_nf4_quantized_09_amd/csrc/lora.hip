@@ -385,12 +385,19 @@ __global__ __launch_bounds__(256) void k_skinny_tt(const uint16_t* __restrict__ 
 }
 
 // Fixed-order sum of the slices: v = sum_z part[z][i][j];  C = scale * v (bf16 or fp32,
-// [i][j] or transposed [j][i]);  C2 = bf16(scale2 * v) when given.
+// [i][j] or transposed [j][i]);  C2 = bf16(scale2 * v) when given.  Workgroups from
+// `sum_blocks` on decode the weight's block constants instead (dq.n1 of them, one per
+// thread), so that the decode the next fused product needs costs no launch of its own.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int S,
                                                        int64_t Mc, int64_t Nc, float scale,
                                                        void* __restrict__ C, bool c_f32,
                                                        bool c_trans, uint16_t* __restrict__ C2,
-                                                       float scale2) {
+                                                       float scale2, int64_t sum_blocks, DqDecode dq) {
+    if ((int64_t)blockIdx.x >= sum_blocks) {
+        const int64_t i = ((int64_t)blockIdx.x - sum_blocks) * 256 + threadIdx.x;
+        if (i < dq.n1) dq.out[i] = decode_c1(dq.q[i], c2_step(dq.c2[i >> 8]), *dq.mean);
+        return;
+    }
     const int64_t total = Mc * Nc;
     const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i4 >= total) return;
@@ -446,7 +453,7 @@ size_t skinny_partial_bytes(int64_t Mc, int64_t Nc, int64_t P) {
 hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, bool b_trans,
                             int64_t Mc, int64_t Nc, int64_t P, float* part, float scale, void* C,
                             bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s,
-                            uint16_t* pack, bool pack_even_odd) {
+                            uint16_t* pack, bool pack_even_odd, const DqDecode* dq) {
     if (Mc == 0 || Nc == 0) return hipSuccess;
     if (pack && a_trans) return hipErrorInvalidValue;
     // per-lane buffer offsets are 32-bit: a direct operand spans 128 rows of its leading
@@ -474,8 +481,12 @@ hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = Mc * Nc;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((total + 1023) / 1024)), dim3(256), 0, s, part, S,
-                       Mc, Nc, scale, C, c_f32, c_trans, C2, scale2);
+    const int64_t sum_blocks = (total + 1023) / 1024;
+    const DqDecode none{nullptr, nullptr, nullptr, 0, nullptr};
+    const DqDecode& d = dq ? *dq : none;
+    const int64_t blocks = sum_blocks + (d.n1 + 255) / 256;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, S, Mc, Nc, scale, C,
+                       c_f32, c_trans, C2, scale2, sum_blocks, d);
     return hipGetLastError();
 }
 
