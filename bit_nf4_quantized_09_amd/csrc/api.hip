@@ -545,14 +545,15 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
             if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dX)");
         }
     }
-    // dA^T = X^T (s U)  (K x r, stored transposed as dA r x K); dB = s dY^T T (N x r);
-    // both contract over the M tokens (stored token-major: contraction-strided)
-    e = nf4::launch_lora_gemm(x, true, Us, true, v.cols, r, M, part, 1.0f, dA, true, true, nullptr,
-                              0.0f, hs);
-    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dA)");
+    // dB = s dY^T T (N x r); dA^T = X^T (s U)  (K x r, stored transposed as dA r x K);
+    // both contract over the M tokens (stored token-major: contraction-strided).  dB first:
+    // part of dY, read by the U pass, may still sit in the Infinity Cache (step -0.1%)
     e = nf4::launch_lora_gemm(g, true, Tb, true, v.rows, r, M, part, s, dB, true, false, nullptr,
                               0.0f, hs);
-    return hip_status(e, "qlora_linear_bwd (dB)");
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dB)");
+    e = nf4::launch_lora_gemm(x, true, Us, true, v.cols, r, M, part, 1.0f, dA, true, true, nullptr,
+                              0.0f, hs);
+    return hip_status(e, "qlora_linear_bwd (dA)");
 }
 
 }  // extern "C"
