@@ -431,12 +431,30 @@ void skinny_plan(int64_t Mc, int64_t Nc, int64_t P, int* slices, int64_t* chunks
         *chunks_per_slice = 0;
         return;
     }
-    // about one workgroup per CU: more slices would add fp32 partial traffic (S times the
-    // output, written once and read once) faster than they add bandwidth
-    int64_t S = (256 + tiles - 1) / tiles;
+    // About one workgroup per CU: more slices would add fp32 partial traffic (S times the
+    // output, written once and read once) faster than they add bandwidth.  When that leaves
+    // the CUs unevenly loaded (the busiest one runs ceil(tiles S / 256) workgroups of 1/S
+    // of a tile each), another S up to 8 is taken if a cost estimate puts it 5% lower: the
+    // busiest CU's share of the operands at 1/256 of 5 TB/s, 3 us per workgroup it runs,
+    // and the partial sums written and read at 5 TB/s.
     const int64_t smax = nchunks / 4 > 1 ? nchunks / 4 : 1;
+    int64_t S = (256 + tiles - 1) / tiles;
     if (S > smax) S = smax;
     if (S < 1) S = 1;
+    auto cost = [&](int64_t c) {
+        const double rounds = (double)((tiles * c + 255) / 256);
+        return rounds / (double)c * (double)P * (SK_BM + SK_BN) * 2.0 / 19.5e9 + rounds * 3e-6 +
+               (double)c * (double)Mc * (double)Nc * 8.0 / 5e12;
+    };
+    const double base = cost(S);
+    double best = base;
+    for (int64_t c = 1; c <= 8 && c <= smax; ++c) {
+        const double t = cost(c);
+        if (t < 0.95 * base && t < best) {
+            best = t;
+            S = c;
+        }
+    }
     int64_t cps = nchunks > 0 ? (nchunks + S - 1) / S : 0;
     if (cps > 0) S = (nchunks + cps - 1) / cps;
     *slices = (int)S;
