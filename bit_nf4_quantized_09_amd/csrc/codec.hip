@@ -207,8 +207,15 @@ __device__ __forceinline__ double chunk_tree_sum(const T* __restrict__ x, int64_
     __shared__ double sw[4];
     const int64_t i0 = c0 + threadIdx.x * 8;
     double v[8];
+    if (sizeof(T) == 4 && i0 + 8 <= n) {
+        // fp32 constants (16-byte aligned; i0 is a multiple of 8): two 16-byte loads
+        const float4 a = reinterpret_cast<const float4*>(x + i0)[0];
+        const float4 b = reinterpret_cast<const float4*>(x + i0)[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (i0 + e < n) ? (double)x[i0 + e] : 0.0;
+        for (int e = 0; e < 8; ++e) v[e] = (i0 + e < n) ? (double)x[i0 + e] : 0.0;
+    }
     double s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
