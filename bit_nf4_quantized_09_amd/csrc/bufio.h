@@ -26,4 +26,9 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
 
+// 16-bit store: dropped by the hardware when the per-lane offset reaches the range.
+__device__ __forceinline__ void buf_store2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)voff, 0, 0);
+}
+
 }  // namespace nf4

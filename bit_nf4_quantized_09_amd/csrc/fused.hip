@@ -399,17 +399,38 @@ void k_fused(FusedArgs a, Nf4Table tab) {
     }
 
     // ---- store bf16 ----
+    // One buffer range per group of 8 rows (fragment row tile i, register group g): a group
+    // with rows past M gets a shorter range, and a lane whose column is past the last takes
+    // an offset beyond every range, so the hardware drops those stores with no branch.  The
+    // per-lane offsets hold the row in the group and the column; nothing goes through the
+    // wave-uniform offset, which the range check does not see.  Ranges and offsets stay
+    // below 2^27 (8 rows of fewer than 2^22 columns).
     const int64_t ncols = BWD ? a.K : a.N;
+    const uint32_t rstride = (uint32_t)(ncols * 2);       // bytes per output row
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t voff[4][4];                                  // [row of the group][j]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool col_ok = c0 + j * 32 + rl_col < ncols;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            voff[k][j] = col_ok ? (uint32_t)(4 * h + k) * rstride + (uint32_t)(j * 32 + rl_col) * 2 : 0x80000000u;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = c0 + j * 32 + rl_col;
+        for (int g = 0; g < 4; ++g) {
+            const int64_t grow = wv * 128 + i * 32 + 8 * g;     // first row of the group in the tile
+            const int64_t live = arows - grow < 8 ? (arows - grow > 0 ? arows - grow : 0) : 8;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.out + (m0 + grow) * ncols + c0, live * rstride);
 #pragma unroll
-            for (int reg = 0; reg < 16; ++reg) {
-                const int64_t row = m0 + wave * 128 + i * 32 + 8 * (reg >> 2) + 4 * h + (reg & 3);
-                if (row < a.M && col < ncols) a.out[row * ncols + col] = f32_to_bf16(acc[i][j][reg]);
-            }
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int k = 0; k < 4; k += 2) {
+                    const uint32_t pk = pack_bf16x2(acc[i][j][4 * g + k], acc[i][j][4 * g + k + 1]);
+                    buf_store2(rs, voff[k][j], (uint16_t)pk);
+                    buf_store2(rs, voff[k + 1][j], (uint16_t)(pk >> 16));
+                }
         }
 }
 
