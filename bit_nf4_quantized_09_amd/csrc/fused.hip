@@ -299,55 +299,43 @@ void k_fused(FusedArgs a, Nf4Table tab) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- prologue: stage 0 <- W' of step 0; A fragments of steps 0 and 1; codes of step 1 ----
+    // ---- prologue ----
+    // The rank-r adapter term goes first, in rank chunks of 64 (piece 0 only, for a split
+    // tile), through stage 1 of the W' buffer, which the main loop first writes after the
+    // prologue's barrier:
+    //   forward : acc += (s T) B^T   (A operand s*T [M x r], stage: rows of B [N x r])
+    //   backward: acc += (s U) A     (A operand s*U [M x r], stage: A [r x K], read transposed)
+    // Its operands are requested before the main loop's first A fragments (those of step 0;
+    // the step-1 fragments follow the term), so that its MFMAs run while those are in flight.  The A operand comes straight from global memory (it is
+    // small: M x r); rank values past r are zero on both sides.
+    // Then stage 0 <- W' of step 0, with the A fragments of steps 0 and 1 and the codes of
+    // step 1 requested.
     AFrags fa0, fa1;
-    {
-        const BlockCodes b0 = load_codes(0);
-        wcur = load_codes(steps > 1 ? 1 : 0);
-        load_all(fa0, 0);
-        load_all(fa1, steps > 1 ? 1 : 0);
-        const ScaledTable t0 = make_pair_table(lvh, b0.c1);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) decode_chunk(lds, t0, b0, c);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[0][j] = read_b(0, j, 0);
-
-    {
-        int it = 0;
-        for (; it + 1 < steps; it += 2) {
-            step_body(std::integral_constant<int, 0>{}, it, fa0);
-            step_body(std::integral_constant<int, 1>{}, it + 1, fa1);
-        }
-        if (it < steps) step_body(std::integral_constant<int, 0>{}, it, fa0);
-    }
-
-    // ---- rank-r adapter term, in rank chunks of 64 (piece 0 only, for a split tile) ----
-    //   forward : acc += (s T) B^T   (A operand s*T [M x r], W' stage: rows of B [N x r])
-    //   backward: acc += (s U) A     (A operand s*U [M x r], W' stage: A [r x K], read transposed)
-    // The A operand comes straight from global memory (it is small: M x r), rank values past r
-    // zeroed on both sides.
+    const BlockCodes b0 = load_codes(0);
+    wcur = load_codes(steps > 1 ? 1 : 0);
     const int rr = u.split <= 0 ? a.r : 0;
     const int64_t arows = a.M - m0 < TM ? a.M - m0 : TM;
     for (int rc = 0; rc < rr; rc += 64) {
-        __syncthreads();                    // every wave is done with the stages
+        if (rc > 0) __syncthreads();        // every wave is done with the previous chunk
+        // stage operand, through buffer loads that read zero out of range (no branch, so
+        // that nothing waits for them before the other loads are issued)
+        uint4 rv[TN * 8 / 256];
+        {
+            const __amdgpu_buffer_rsrc_t rs =
+                BWD ? make_rsrc(a.Lr + (int64_t)rc * a.K, (int64_t)(a.r - rc) * a.K * 2)
+                    : make_rsrc(a.Lr + c0 * a.r, (a.N - c0 < TN ? a.N - c0 : TN) * a.r * 2);
 #pragma unroll
-        for (int i = 0; i < TN * 8 / 256; ++i) {
-            const int qi = tid + 256 * i;
-            if constexpr (BWD) {
-                const int j = qi / (TN / 8), c = qi % (TN / 8);   // rank row j, 8 features per chunk
-                const int64_t gk = c0 + 8 * c;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (rc + j < a.r && gk < a.K) v = even_odd8(*reinterpret_cast<const uint4*>(a.Lr + (int64_t)(rc + j) * a.K + gk));
-                *reinterpret_cast<uint4*>(lds + wt_off<TN>(j, 8 * c)) = v;
-            } else {
-                const int row = qi >> 3, c = qi & 7;
-                const int col = rc + 8 * c;
-                const int64_t gn = c0 + row;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (col < a.r && gn < a.N) v = *reinterpret_cast<const uint4*>(a.Lr + gn * a.r + col);
-                *reinterpret_cast<uint4*>(lds + tile_off(row, c)) = v;
+            for (int i = 0; i < TN * 8 / 256; ++i) {
+                const int qi = tid + 256 * i;
+                uint32_t off;
+                if constexpr (BWD) {
+                    const int j = qi / (TN / 8), c = qi % (TN / 8);   // rank row rc + j, 8 features per chunk
+                    off = c0 + 8 * c < a.K ? (uint32_t)(((int64_t)j * a.K + 8 * c) * 2) + (uint32_t)(c0 * 2) : 0x80000000u;
+                } else {
+                    const int row = qi >> 3, c = qi & 7;             // feature c0 + row, rank rc + 8 c
+                    off = rc + 8 * c < a.r ? (uint32_t)((row * a.r + rc + 8 * c) * 2) : 0x80000000u;
+                }
+                rv[i] = buf_load16(rs, off, 0);
             }
         }
         AFrags R;
@@ -363,17 +351,47 @@ void k_fused(FusedArgs a, Nf4Table tab) {
                 }
             }
         }
+        if (rc == 0) load_all(fa0, 0);
+#pragma unroll
+        for (int i = 0; i < TN * 8 / 256; ++i) {
+            const int qi = tid + 256 * i;
+            if constexpr (BWD) {
+                const int j = qi / (TN / 8), c = qi % (TN / 8);
+                *reinterpret_cast<uint4*>(lds + W_STAGE_BYTES + wt_off<TN>(j, 8 * c)) = even_odd8(rv[i]);
+            } else {
+                *reinterpret_cast<uint4*>(lds + W_STAGE_BYTES + tile_off(qi >> 3, qi & 7)) = rv[i];
+            }
+        }
         __syncthreads();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             bf16x8 b[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = read_b(0, j, s);
+            for (int j = 0; j < 4; ++j) b[j] = read_b(1, j, s);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) mfma(i, j, R.f[i][s], b[j]);
         }
+    }
+    if (rr <= 0) load_all(fa0, 0);
+    load_all(fa1, steps > 1 ? 1 : 0);
+    {
+        const ScaledTable t0 = make_pair_table(lvh, b0.c1);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) decode_chunk(lds, t0, b0, c);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[0][j] = read_b(0, j, 0);
+
+    {
+        int it = 0;
+        for (; it + 1 < steps; it += 2) {
+            step_body(std::integral_constant<int, 0>{}, it, fa0);
+            step_body(std::integral_constant<int, 1>{}, it + 1, fa1);
+        }
+        if (it < steps) step_body(std::integral_constant<int, 0>{}, it, fa0);
     }
 
     // The output column of accumulator column rl: forward, the feature itself; backward, the
