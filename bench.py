@@ -603,6 +603,15 @@ def codec_paths(layer, dev, reps=3):
     bdq = n_total * (4 / 64 + 1 / 64 + 4 / (64 * 256))
     res["double_quantize"] = dict(GBps=bdq / tdq / 1e9, ms=tdq * 1e3, bytes=bdq)
 
+    # the layer's seven constant vectors in one batched call (two launches), as a layer
+    # is quantized: the per-tensor figure above is bound by the host's seven calls
+    def dq_batch():
+        nf4.nf4_double_quantize_batch([absmax[p["name"]] for p in layer])
+
+    dq_batch()
+    tdqb = timed(dq_batch)
+    res["double_quantize_layer_batched"] = dict(GBps=bdq / tdqb / 1e9, ms=tdqb * 1e3, bytes=bdq)
+
     def deq():
         for p in layer:
             nf4.nf4_dequantize(p["Wq"], torch.float32)
