@@ -203,8 +203,9 @@ size_t fwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
 size_t bwd_partial_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
     size_t b = align256(nf4::fused_bwd_plan(M, N, K).bytes);
     b = nf4::skinny_partial_bytes(M, r, N) > b ? nf4::skinny_partial_bytes(M, r, N) : b;
-    const size_t c[3] = {nf4::skinny_partial_bytes(M, r, K), nf4::skinny_partial_bytes(K, r, M),
-                         nf4::skinny_partial_bytes(N, r, M)};
+    // dB and dA run in one launch, each with its own slices
+    const size_t c[2] = {nf4::skinny_partial_bytes(M, r, K),
+                         nf4::skinny_partial_bytes(N, r, M) + nf4::skinny_partial_bytes(K, r, M)};
     for (size_t x : c) b = x > b ? x : b;
     return b;
 }
@@ -546,14 +547,13 @@ nf4_status qlora_linear_bwd(const nf4_weight* W, const void* X, const void* dY, 
         }
     }
     // dB = s dY^T T (N x r); dA^T = X^T (s U)  (K x r, stored transposed as dA r x K);
-    // both contract over the M tokens (stored token-major: contraction-strided).  dB first:
-    // part of dY, read by the U pass, may still sit in the Infinity Cache (step -0.1%)
-    e = nf4::launch_lora_gemm(g, true, Tb, true, v.rows, r, M, part, s, dB, true, false, nullptr,
-                              0.0f, hs);
-    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd (dB)");
-    e = nf4::launch_lora_gemm(x, true, Us, true, v.cols, r, M, part, 1.0f, dA, true, true, nullptr,
-                              0.0f, hs);
-    return hip_status(e, "qlora_linear_bwd (dA)");
+    // both contract over the M tokens (stored token-major: contraction-strided).  One launch
+    // runs the two side by side, dB's workgroups first, each into its own partial slices.
+    const nf4::TtProduct pb_dB{g, Tb, v.rows, r, M, part, s, dB, false};
+    float* part_dA = (float*)((char*)part + nf4::skinny_partial_bytes(v.rows, r, M));
+    const nf4::TtProduct pb_dA{x, Us, v.cols, r, M, part_dA, 1.0f, dA, true};
+    e = nf4::launch_lora_tt_pair(pb_dB, pb_dA, hs);
+    return hip_status(e, "qlora_linear_bwd (dA, dB)");
 }
 
 }  // extern "C"

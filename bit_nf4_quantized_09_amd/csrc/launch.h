@@ -72,6 +72,29 @@ struct DqDecode {
     int64_t n1;
     float* out;
 };
+// A both-strided product C = scale * A^T B (fp32 out, C transposed when c_trans): A is
+// P x Mc and B is P x Nc, both row-major with the contraction P as rows (Mc, Nc multiples
+// of 8, below 2^23); part holds skinny_partial_bytes(Mc, Nc, P).
+struct TtProduct {
+    const uint16_t* A;
+    const uint16_t* B;
+    int64_t Mc, Nc, P;
+    float* part;
+    float scale;
+    float* C;
+    bool c_trans;
+};
+// Kernel argument of one both-strided product: its operands, slice length and grid.
+struct TtProblem {
+    const uint16_t* A;
+    const uint16_t* B;
+    int64_t Mc, Nc, P, cps;
+    float* part;
+    int64_t gx, gy;           // column tiles, row tiles (slices are the third dimension)
+};
+// Two both-strided products in one launch (two workgroups per CU), then the slice sum of
+// each; their partial regions must not overlap.
+hipError_t launch_lora_tt_pair(const TtProduct& d0, const TtProduct& d1, hipStream_t s);
 hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, bool b_trans,
                             int64_t Mc, int64_t Nc, int64_t P, float* part, float scale, void* C,
                             bool c_f32, bool c_trans, uint16_t* C2, float scale2, hipStream_t s,

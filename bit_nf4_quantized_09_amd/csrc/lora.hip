@@ -269,19 +269,19 @@ __device__ __forceinline__ uint2 tt_read_tr16(const uint8_t* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-__global__ __launch_bounds__(256) void k_skinny_tt(const uint16_t* __restrict__ A,
-                                                   const uint16_t* __restrict__ B, int64_t Mc,
-                                                   int64_t Nc, int64_t P, int64_t chunks_per_slice,
-                                                   float* __restrict__ part) {
+// Workgroup (bx, by, bz) of one both-strided product: output tile (by, bx), slice bz.
+__device__ __forceinline__ void skinny_tt_unit(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                               int64_t Mc, int64_t Nc, int64_t P, int64_t chunks_per_slice,
+                                               float* __restrict__ part, int64_t bx, int64_t by, int64_t bz) {
     constexpr int NA = SK_BM * SK_PC * 2 / 16 / 256;   // A pieces per thread: 4
     constexpr int NB = SK_BN * SK_PC * 2 / 16 / 256;   // B pieces per thread: 2
     static_assert(SK_BM == 128 && SK_BN == 64 && SK_PC == 64, "tile");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SK_STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t i0 = (int64_t)blockIdx.y * SK_BM, j0 = (int64_t)blockIdx.x * SK_BN;
+    const int64_t i0 = by * SK_BM, j0 = bx * SK_BN;
     const int64_t nchunks = (P + SK_PC - 1) / SK_PC;
-    const int64_t c0 = (int64_t)blockIdx.z * chunks_per_slice;
+    const int64_t c0 = bz * chunks_per_slice;
     const int64_t c1 = (c0 + chunks_per_slice < nchunks) ? c0 + chunks_per_slice : nchunks;
     // element (i, p) of the A operand at A[p * Mc + i], (j, p) of the B operand at B[p * Nc + j]
     uint32_t offa[NA], offb[NB];
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256) void k_skinny_tt(const uint16_t* __restrict__ 
         if (k < n) step(k, s0, s1);
         if (k + 1 < n) step(k + 1, s1, s2);
     }
-    float* out = part + (int64_t)blockIdx.z * Mc * Nc;
+    float* out = part + bz * Mc * Nc;
 #pragma unroll
     for (int reg = 0; reg < 16; ++reg) {
         const int64_t row = i0 + wave * 32 + 8 * (reg >> 2) + 4 * (lane >> 5) + (reg & 3);
@@ -382,6 +382,19 @@ __global__ __launch_bounds__(256) void k_skinny_tt(const uint16_t* __restrict__ 
             if (col1 < Nc) out[row * Nc + col1] = acc1[reg];
         }
     }
+}
+
+// One launch runs two both-strided products side by side (dA and dB of the backward, each
+// of which fills the chip with about one workgroup per CU; together they hold two per CU,
+// so twice the loads are in flight): workgroups below blocks0 belong to p0, the rest to p1.
+// A single product passes itself twice with blocks0 = its workgroup count.
+__global__ __launch_bounds__(256) void k_skinny_tt(TtProblem p0, TtProblem p1, int64_t blocks0) {
+    const bool second = (int64_t)blockIdx.x >= blocks0;
+    const int64_t b = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
+    const int64_t gx = second ? p1.gx : p0.gx, gy = second ? p1.gy : p0.gy;
+    skinny_tt_unit(second ? p1.A : p0.A, second ? p1.B : p0.B, second ? p1.Mc : p0.Mc, second ? p1.Nc : p0.Nc,
+                   second ? p1.P : p0.P, second ? p1.cps : p0.cps, second ? p1.part : p0.part, b % gx,
+                   (b / gx) % gy, b / (gx * gy));
 }
 
 // Fixed-order sum of the slices: v = sum_z part[z][i][j];  C = scale * v (bf16 or fp32,
@@ -492,8 +505,11 @@ hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, 
         hipLaunchKernelGGL((k_skinny<false, false>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part, pack, pack_even_odd);
     else if (!a_trans && b_trans)
         hipLaunchKernelGGL((k_skinny<false, true>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part, pack, pack_even_odd);
-    else if (a_trans && b_trans)
-        hipLaunchKernelGGL(k_skinny_tt, grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part);
+    else if (a_trans && b_trans) {
+        const TtProblem p{A, B, Mc, Nc, P, cps, part, (int64_t)grid.x, (int64_t)grid.y};
+        const int64_t blocks = (int64_t)grid.x * grid.y * grid.z;
+        hipLaunchKernelGGL(k_skinny_tt, dim3((unsigned)blocks), dim3(256), 0, s, p, p, blocks);
+    }
     else
         hipLaunchKernelGGL((k_skinny<true, false>), grid, dim3(256), 0, s, A, B, Mc, Nc, P, cps, part, nullptr, false);
     hipError_t e = hipGetLastError();
@@ -506,6 +522,37 @@ hipError_t launch_lora_gemm(const uint16_t* A, bool a_trans, const uint16_t* B, 
     hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, S, Mc, Nc, scale, C,
                        c_f32, c_trans, C2, scale2, sum_blocks, d);
     return hipGetLastError();
+}
+
+hipError_t launch_lora_tt_pair(const TtProduct& d0, const TtProduct& d1, hipStream_t s) {
+    const TtProduct* d[2] = {&d0, &d1};
+    TtProblem p[2];
+    int S[2];
+    int64_t blocks[2];
+    for (int i = 0; i < 2; ++i) {
+        const TtProduct& q = *d[i];
+        if (q.Mc >= ((int64_t)1 << 23) || q.Nc >= ((int64_t)1 << 23) || (q.Mc & 7) || (q.Nc & 7))
+            return hipErrorInvalidValue;
+        int64_t cps;
+        skinny_plan(q.Mc, q.Nc, q.P, &S[i], &cps);
+        p[i] = TtProblem{q.A, q.B, q.Mc, q.Nc, q.P, cps, q.part, (q.Nc + SK_BN - 1) / SK_BN,
+                         (q.Mc + SK_BM - 1) / SK_BM};
+        blocks[i] = q.Mc == 0 || q.Nc == 0 ? 0 : p[i].gx * p[i].gy * S[i];
+    }
+    if (blocks[0] + blocks[1] > 0)
+        hipLaunchKernelGGL(k_skinny_tt, dim3((unsigned)(blocks[0] + blocks[1])), dim3(256), 0, s, p[0], p[1],
+                           blocks[0]);
+    hipError_t e = hipGetLastError();
+    const DqDecode none{nullptr, nullptr, nullptr, 0, nullptr};
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+        const TtProduct& q = *d[i];
+        if (blocks[i] == 0) continue;
+        const int64_t sum_blocks = (q.Mc * q.Nc + 1023) / 1024;
+        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)sum_blocks), dim3(256), 0, s, q.part, S[i], q.Mc, q.Nc,
+                           q.scale, q.C, true, q.c_trans, (uint16_t*)nullptr, 0.0f, sum_blocks, none);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 }  // namespace nf4
