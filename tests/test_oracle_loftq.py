@@ -80,7 +80,9 @@ def test_loftq_second_alternation_quantizes_the_residual():
          ).astype(np.float32)
     one = oracle.loftq(W, r, gamma, 1)
     two = oracle.loftq(W, r, gamma, 2)
-    np.testing.assert_allclose(two["err"][0], one["err"][0], rtol=0, atol=0)
+    # the same first alternation in both calls (threaded float64 LAPACK may round its last
+    # bit differently from call to call)
+    np.testing.assert_allclose(two["err"][0], one["err"][0], rtol=1e-12, atol=0)
     R = (W.astype(np.float64) - gamma * one["B"] @ one["A"]).astype(np.float32)
     codes, absmax = oracle.nf4_quantize(R.reshape(-1))
     # a last-bit difference of the residual can move a code across a threshold: nearly all agree
